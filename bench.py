@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of the Hyper-Connection Gated Residual op on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-sweep] [--no-cpu] [--warm]
+
+A step is one hcgr_forward call (all three kernels) over one batch of M
+tokens. The headline line is the decode batch M=32 (HC=4, HS=2560, r=320,
+bf16, separate Wd/Wi). Timing:
+  * the K timed steps are queued behind a GPU spin kernel, so the host has
+    enqueued all of them before the GPU starts; HIP events bracket the K
+    steps on the stream the library launches on (device back-to-back time,
+    like a graph replay; host launch overhead is reported separately);
+  * "cold": every step reads its own copy of the weights and activations,
+    rotating over enough sets to exceed the 256 MB Infinity Cache, so the
+    weights come from HBM as they would when other layers run in between;
+    "warm" re-reads one set.
+  * per-kernel durations come from HIP events recorded by hcgr_forward_timed
+    between the kernels, on the same stream.
+Inputs are seeded synthetic data (synth/) with the study's distributions.
+Prints ONE JSON line on stdout; --json-out also writes it (and the sweep) to a file.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/call & tokens/s of HC gated-residual op, M=1..65536; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+CACHE_BYTES = 256 << 20      # Infinity Cache; rotating sets exceed it
+HC, HS, R_LOW = 4, 2560, 320
+K = HC * HS
+
+
+def op_bytes(M, merged=False):
+    """Algorithmic bytes of one call: weights once (Wd, Wi or the 324 used rows
+    of Wm, Wu, Wnorm) + per token R, y, inj in and R2, rrms, inj_next, x out."""
+    w = (R_LOW + HC) * K * 2 + K * R_LOW * 2 + (0 if merged else HS * 2)
+    if merged:
+        w += HS * 2  # the up kernel still reads Wnorm
+    return w + M * (K * 2 + HS * 2 + HC * 2 + K * 2 + HC * 4 + HC * 2 + HS * 2)
+
+
+def op_flops(M):
+    return M * 2 * (R_LOW + HC) * K + M * 2 * R_LOW * K
+
+
+def kernel_bytes(name, M, merged=False):
+    """Algorithmic bytes per launch of each kernel (what it must move at least)."""
+    if name == "hcgr_k1_down":
+        w = (R_LOW + HC) * K * 2 + (0 if merged else HS * 2)
+        return w + M * (K * 2 + HS * 2 + HC * 2 + K * 2)
+    if name == "hcgr_k1_reduce":
+        return M * (HC * 4 + HC * 2)
+    if name == "hcgr_k2_up_mix":
+        return K * R_LOW * 2 + HS * 2 + M * (K * 2 + HC * 4 + HS * 2)
+    raise KeyError(name)
+
+
+def kernel_flops(name, M):
+    return {"hcgr_k1_down": M * 2 * (R_LOW + HC) * K, "hcgr_k1_reduce": 0,
+            "hcgr_k2_up_mix": M * 2 * R_LOW * K}[name]
+
+
+KERNELS = ("hcgr_k1_down", "hcgr_k1_reduce", "hcgr_k2_up_mix")
+
+
+class Sets:
+    """NB independent buffer sets (inputs, weights, outputs, workspace) for M tokens."""
+
+    def __init__(self, H, op, M, nb, merged=False, scale_stream0=1.0, seed0=0):
+        import torch
+        import synth
+        self.M, self.nb, self.merged = M, nb, merged
+        sh = synth.Shape(HC, HS, R_LOW)
+        self.sets = []
+        for i in range(nb):
+            inp = synth.make_inputs(M, sh, seed=seed0 + i, device="cuda", scale_stream0=scale_stream0)
+            if merged:
+                inp["wd"] = synth.fold_merged_weight(inp["wd"], inp["wi"], inp["wnorm"], 336, HS)
+                inp["wi"] = None
+            out = op.alloc_outputs(M)
+            ws = torch.empty(max(H.hcgr_workspace_size(op.handle, M), 256), dtype=torch.uint8, device="cuda")
+            self.sets.append((inp, out, ws))
+
+    def call(self, H, op, i, stream, events=None):
+        inp, out, ws = self.sets[i % self.nb]
+        args = (op.handle, inp["R"], inp["y"], inp["inj"], inp["inj"].stride(0), inp["wnorm"], inp["wd"], inp["wi"],
+                inp["wu"], self.M, out["R2"], out["rrms"], out["inj_next"], out["ld_inj_next"], out["x"], ws,
+                ws.numel(), stream)
+        if events is None:
+            H.hcgr_forward(*args)
+        else:
+            H.hcgr_forward_timed(*args, events)
+
+
+def set_count(M, merged=False, cold=True):
+    if not cold:
+        return 1
+    per = op_bytes(M, merged) + M * (K * 2 + HS * 2)  # + outputs written
+    return max(1, min(64, math.ceil(1.25 * CACHE_BYTES / per)))
+
+
+def _spin(torch, us):
+    # torch's bounded spin kernel (clock cycles at ~2.4 GHz); holds the queue
+    torch.cuda._sleep(int(us * 2400))
+
+
+def time_calls(H, op, sets, steps, warmup, stream):
+    """Device time per call (µs) for `steps` back-to-back calls, plus the host
+    enqueue time per call."""
+    import torch
+    for i in range(warmup):
+        sets.call(H, op, i, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(min(steps, 20)):
+        sets.call(H, op, i, stream)
+    host_us = (time.perf_counter() - t0) / min(steps, 20) * 1e6
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    _spin(torch, host_us * steps * 1.5 + 2000)
+    start.record()
+    for i in range(steps):
+        sets.call(H, op, i, stream)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / steps, host_us
+
+
+def time_kernels(H, op, sets, steps, stream, host_us):
+    """Average duration (µs) of each of the three kernels over `steps` calls,
+    from HIP events that hcgr_forward_timed records on the launch stream."""
+    import torch
+    evs = []
+    for _ in range(steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in row:
+            e.record()  # materialise the hipEvent_t
+        evs.append(row)
+    torch.cuda.synchronize()
+    _spin(torch, (host_us + 20) * steps * 1.5 + 2000)
+    for i in range(steps):
+        sets.call(H, op, i, stream, [e.cuda_event for e in evs[i]])
+    torch.cuda.synchronize()
+    sums = [0.0, 0.0, 0.0]
+    for row in evs:
+        for j in range(3):
+            sums[j] += row[j].elapsed_time(row[j + 1]) * 1e3
+    return {KERNELS[j]: sums[j] / steps for j in range(3)}
+
+
+def time_graph(H, op, sets, replays, stream):
+    """µs per call when `sets.nb` calls are captured into one HIP graph and replayed."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(sets.nb):
+            sets.call(H, op, i, s.cuda_stream)
+        with torch.cuda.graph(g, stream=s):
+            for i in range(sets.nb):
+                sets.call(H, op, i, s.cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    _spin(torch, 40 * replays + 2000)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / (replays * sets.nb)
+    del g
+    return us
+
+
+def roofline_entry(name, M, us, merged):
+    b = kernel_bytes(name, M, merged)
+    gbs = b / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": name, "avg_us": round(us, 3),
+            "alg_bytes_per_launch": b, "flops_per_launch": kernel_flops(name, M)}
+
+
+def run_workload(H, op_sep, op_merged, name, M, merged, scale0, steps, warmup, cold, stream):
+    op = op_merged if merged else op_sep
+    nb = set_count(M, merged, cold)
+    sets = Sets(H, op, M, nb, merged=merged, scale_stream0=scale0)
+    us, host_us = time_calls(H, op, sets, steps, warmup, stream)
+    kern = time_kernels(H, op, sets, max(8, min(steps, 200)), stream, host_us)
+    graph_us = time_graph(H, op, sets, max(1, min(200, (steps + nb - 1) // nb)), stream)
+    B, F = op_bytes(M, merged), op_flops(M)
+    res = {"workload": name, "M": M, "merged": merged, "buffer_sets": nb,
+           "cache": "cold (rotating sets > Infinity Cache)" if nb > 1 else ("warm" if not cold else "single set"),
+           "us_per_call": round(us, 3), "us_per_call_graph": round(graph_us, 3),
+           "host_enqueue_us_per_call": round(host_us, 2), "tokens_per_s": round(M / (us * 1e-6), 1),
+           "op_alg_bytes": B, "op_flops": F,
+           "op_hbm_frac": round(B / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+           "op_mfma_frac": round(F / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+           "op_roofline_us": round(max(B / (HBM_PEAK_GBS * 1e9), F / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6, 3),
+           "kernels_us": {k: round(v, 3) for k, v in kern.items()},
+           "plan": H.hcgr_describe_plan(op.cfg, M)}
+    res["op_roofline_frac"] = round(res["op_roofline_us"] / us, 4)
+    del sets
+    return res
+
+
+def cpu_baseline(M, budget_s=12.0):
+    """The fp64 oracle (as it stands) on this host's cores, on the same
+    workload shape: repeated full M-token batches until ~budget_s of CPU time."""
+    import torch
+    import oracle
+    import synth
+    d = synth.make_inputs(M, synth.Shape(HC, HS, R_LOW), seed=0, device="cpu")
+    cfg = oracle.OracleConfig()
+    oracle.forward(cfg, d["R"][:1], d["y"][:1], d["inj"][:1], d["wnorm"], d["wd"], d["wi"], d["wu"])
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.forward(cfg, d["R"], d["y"], d["inj"], d["wnorm"], d["wd"], d["wi"], d["wu"])
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    del torch
+    return {"value": round(n * M / dt, 2), "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{n} full batches of the M={M} workload ({n * M} tokens), fp64, OpenMP over tokens",
+            "us_per_call": round(dt / n * 1e6, 1)}
+
+
+WORKLOADS = {
+    "decode_m1": (1, False, 1.0),
+    "decode_m32": (32, False, 1.0),
+    "merged_m1024": (1024, True, 1.0),
+    "prefill_m8192_s0x8": (8192, False, 8.0),
+    "prefill_m65536": (65536, False, 1.0),
+}
+SWEEP_M = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_m32", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="headline on one re-read buffer set")
+    ap.add_argument("--json-out", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the op is token-parallel and this build has no multi-GPU "
+              "path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import skinny_gemm_hcgr_amd as H
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    H.load_library()
+    op = H.HCGR(H.Config(), 0)
+    opm = H.HCGR(H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336), 0)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    M, merged, scale0 = WORKLOADS[args.workload]
+    torch.cuda.synchronize()
+    head = run_workload(H, op, opm, args.workload, M, merged, scale0, args.steps, args.warmup, not args.warm, stream)
+    warm = None
+    if not args.warm:
+        warm = run_workload(H, op, opm, args.workload, M, merged, scale0, args.steps, args.warmup, False, stream)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: {head['us_per_call']} us/call ({head['cache']}), kernels {head['kernels_us']}",
+          file=sys.stderr, flush=True)
+
+    sweep = []
+    if not args.no_sweep:
+        named = [(n, *v) for n, v in WORKLOADS.items() if n != args.workload]
+        extra = [(f"sweep_m{m}", m, False, 1.0) for m in SWEEP_M if m not in (1, 32, 65536)]
+        for name, m, mg, sc in named + extra:
+            steps = max(10, min(args.steps, int(2e5 / max(1, m)) + 10))
+            r = run_workload(H, op, opm, name, m, mg, sc, steps, 5, True, stream)
+            print(f"[bench] {name}: {r['us_per_call']} us/call graph {r['us_per_call_graph']} "
+                  f"roofline {r['op_roofline_frac']}", file=sys.stderr, flush=True)
+            sweep.append(r)
+            torch.cuda.empty_cache()
+
+    dom = max(head["kernels_us"], key=lambda k: head["kernels_us"][k])
+    roof = roofline_entry(dom, M, head["kernels_us"][dom], merged)
+    line = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["us_per_call"] / 1e3, 6),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded SplitMix64/Box-Muller, the study's distributions)",
+            "config": {"workload": args.workload, "M": M, "hc": HC, "hs": HS, "r": R_LOW, "eps": 1e-6,
+                       "weights": "merged_folded_n336" if merged else "separate",
+                       "buffers": head["cache"], "buffer_sets": head["buffer_sets"]},
+            "us_per_call": head["us_per_call"], "us_per_call_graph": head["us_per_call_graph"],
+            "us_per_call_warm": warm["us_per_call"] if warm else None,
+            "op_roofline_frac": head["op_roofline_frac"], "op_hbm_frac": head["op_hbm_frac"],
+            "kernels_us": head["kernels_us"], "roofline": roof,
+            "context": {"pages_two_stage_graph_us": {"1": 21.0, "32": 28.8, "1024": 76.3, "8192": 339.2,
+                                                     "65536": 2636.4},
+                        "note": "page numbers: MI355X, merged/folded weights, graph replay; context only"}}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(M if M <= 1024 else 64)
+    else:
+        line["cpu_baseline"] = None
+    if sweep:
+        line["sweep"] = [{k: r[k] for k in ("workload", "M", "us_per_call", "us_per_call_graph", "tokens_per_s",
+                                            "op_roofline_frac", "op_hbm_frac", "op_mfma_frac", "kernels_us")}
+                         for r in sweep]
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            json.dump({"line": line, "headline": head, "warm": warm, "sweep": sweep}, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

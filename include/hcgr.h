@@ -1,0 +1,181 @@
+/*
+ * hcgr.h -- C ABI of the MI355X (gfx950) Hyper-Connection Gated Residual op.
+ *
+ * The op (ROCm/aiter pull request #5913, "Two-stage Hyper-Connection Gated
+ * Residual kernel", section "Technical Details") takes, per token, the HC
+ * incoming residual streams R (flattened to K = HC*HS values, stream-major:
+ * element (s, c) at k = s*HS + c), the block output y [HS] and the incoming
+ * injection logits inj [HC], and computes
+ *   (COMBINE) iw[s] = 2*sigmoid(inj[s]/HC);  R2[s,c] = R[s,c] + y[c]*iw[s]
+ *   (N)       rrms[s] = 1/sqrt(mean_c R2[s,c]^2 + eps);
+ *             xn[s,c] = R2[s,c]*rrms[s]*(1 + Wnorm)
+ *   (G1)      h = SiLU((xn . Wd^T) / HC)                  Wd: [r, K]
+ *   (INJ)     inj_next = xn . Wi^T                          Wi: [HC, K]
+ *   (G2)      G = sigmoid(h . Wu^T)                         Wu: [K, r]
+ *   (MIX)     x[c] = (1/HC) * sum_s G[s,c]*xn[s,c]
+ * and returns R2 (the next residual), rrms, inj_next and x (the next block's
+ * input). xn, h and the gate never leave the chip except h, which crosses
+ * between kernels through the caller's workspace.
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major, dense rows
+ *     unless a leading dimension (ld_*) is given.
+ *   - All tensor pointers are device pointers on the handle's device,
+ *     allocated and owned by the caller. The library never allocates device
+ *     memory, never synchronises the host, and enqueues its kernels on the
+ *     caller's stream in order, so a call can be captured into a HIP graph.
+ *   - Every check runs on the host before the first launch; on any error
+ *     nothing is launched and nothing is written. No C++ exception crosses
+ *     this boundary.
+ *   - hcgr_last_error() gives a human-readable reason for the last non-OK
+ *     status returned on the calling thread.
+ */
+#ifndef HCGR_H
+#define HCGR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hcgr_status {
+    HCGR_OK = 0,
+    HCGR_ERR_INVALID_ARGUMENT = 1,     /* null/misaligned pointer, bad size, bad stride, bad config */
+    HCGR_ERR_UNSUPPORTED = 2,          /* device is not gfx950, or a shape the kernels cannot tile */
+    HCGR_ERR_ALIASING = 3,             /* an output overlaps another output or an input            */
+    HCGR_ERR_WORKSPACE_TOO_SMALL = 4,  /* workspace_bytes < hcgr_workspace_size(M)                 */
+    HCGR_ERR_HIP = 5                   /* a HIP runtime call or a kernel launch failed             */
+} hcgr_status;
+
+typedef enum hcgr_weight_layout {
+    /* Wd [r, K] and Wi [HC, K] passed separately; (1 + Wnorm) applied in-kernel. */
+    HCGR_WEIGHTS_SEPARATE = 0,
+    /* One merged matrix Wm [n_pad, K]: rows 0..r-1 are Wd, rows r..r+HC-1 are
+     * Wi, rows r+HC..n_pad-1 are padding that is never read; the caller has
+     * folded (1 + Wnorm) into its columns (Wm[j,k] = W[j,k]*(1 + Wnorm[k mod HS])
+     * rounded to bf16). Described in the "Performance" section of the same
+     * pull request (336 rows = 320 + 4 + 12 padding, "(1+w) folded in"). */
+    HCGR_WEIGHTS_MERGED_FOLDED = 1
+} hcgr_weight_layout;
+
+typedef struct hcgr_config {
+    int32_t hc;            /* residual streams HC. Supported: 4.                              */
+    int32_t hs;            /* stream width HS. Supported: multiple of 128, 128..65536.        */
+    int32_t r;             /* low-rank width r. Supported: multiple of 32, 32..512.           */
+    float eps;             /* RMSNorm epsilon (>= 0, finite), added to the mean square.       */
+    int32_t wnorm_len;     /* hs (Wnorm shared by all streams, indexed by c) or hc*hs (by k). */
+    int32_t weight_layout; /* hcgr_weight_layout                                              */
+    int32_t n_pad;         /* rows of Wm for MERGED_FOLDED (>= r + hc); ignored otherwise.    */
+} hcgr_config;
+
+typedef struct hcgr_op* hcgr_handle;
+
+/* Validates cfg and binds a handle to `device` (a HIP device ordinal).
+ * Returns HCGR_ERR_UNSUPPORTED when the device is not gfx950 or the shape is
+ * outside the supported set above, HCGR_ERR_INVALID_ARGUMENT for a malformed
+ * config or a NULL `out`, HCGR_ERR_HIP when the device cannot be queried.
+ * On success *out owns only host memory; free it with hcgr_destroy. */
+hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out);
+
+/* Frees a handle (NULL is allowed). Outstanding work on streams is unaffected. */
+void hcgr_destroy(hcgr_handle h);
+
+/* Bytes of device workspace hcgr_forward needs for M tokens (0 for M == 0).
+ * The workspace holds the per-chunk partial sums of the down/inject
+ * contraction, the per-chunk sums of squares and the SiLU output h handed to
+ * the up kernel. Its contents on entry are ignored (no zero-fill needed);
+ * calls that may run concurrently (different streams) need separate
+ * workspaces. */
+hcgr_status hcgr_workspace_size(hcgr_handle h, int64_t M, size_t* bytes);
+
+/* The full op for M tokens, enqueued on `stream` (a hipStream_t; NULL = the
+ * device's default stream), which must belong to the handle's device.
+ *
+ * Inputs (bf16 unless noted):
+ *   R        [M, K]            incoming residual streams, k = s*HS + c
+ *   y        [M, HS]           block output to inject
+ *   inj      [M, ld_inj]       injection logits; columns 0..HC-1 are read,
+ *                              ld_inj >= HC (a strided view such as a previous
+ *                              call's inj_next is allowed)
+ *   wnorm    [wnorm_len]       RMSNorm weight (the op uses 1 + wnorm)
+ *   wd       [r, K]            down weight, or Wm [n_pad, K] when MERGED_FOLDED
+ *   wi       [HC, K]           inject weight; must be NULL when MERGED_FOLDED
+ *   wu       [K, r]            up weight (row k = s*HS + c)
+ * Outputs:
+ *   R2       [M, K]   bf16     next residual (round-to-nearest-even of the
+ *                              fp32 value)
+ *   rrms     [M, HC]  float    per-stream reciprocal RMS
+ *   inj_next [M, ld_inj_next]  next layer's injection logits, bf16, columns
+ *                              0..HC-1 written, others untouched
+ *   x        [M, HS]  bf16     gated mean of the normalised streams
+ * Pointer alignment: R, y, wnorm, wd, wi, wu, R2, x and workspace 16 bytes;
+ * rrms 4; inj, inj_next 2. Any M >= 1 is accepted (tails are handled in the
+ * kernels); M == 0 returns HCGR_OK and touches nothing (pointers may be NULL).
+ * Errors: HCGR_ERR_INVALID_ARGUMENT (M < 0, NULL, misalignment, ld < HC,
+ * stream of another device, wi given with MERGED_FOLDED), HCGR_ERR_ALIASING
+ * (the byte range of any output overlaps another output, an input or the
+ * workspace), HCGR_ERR_WORKSPACE_TOO_SMALL, HCGR_ERR_HIP (launch failure). */
+hcgr_status hcgr_forward(hcgr_handle h,
+                         const uint16_t* R, const uint16_t* y,
+                         const uint16_t* inj, int64_t ld_inj,
+                         const uint16_t* wnorm, const uint16_t* wd,
+                         const uint16_t* wi, const uint16_t* wu,
+                         int64_t M,
+                         uint16_t* R2, float* rrms,
+                         uint16_t* inj_next, int64_t ld_inj_next,
+                         uint16_t* x,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* hcgr_forward with per-kernel timing marks, for measurement: `events` points
+ * to 4 hipEvent_t handles owned by the caller (created with timing enabled);
+ * events[0] is recorded on `stream` before the first kernel and events[1],
+ * events[2], events[3] right after the down/inject kernel, the reduction
+ * kernel and the up/mix kernel. Same arguments, checks and results as
+ * hcgr_forward otherwise; NULL events -> HCGR_ERR_INVALID_ARGUMENT. */
+hcgr_status hcgr_forward_timed(hcgr_handle h,
+                               const uint16_t* R, const uint16_t* y,
+                               const uint16_t* inj, int64_t ld_inj,
+                               const uint16_t* wnorm, const uint16_t* wd,
+                               const uint16_t* wi, const uint16_t* wu,
+                               int64_t M,
+                               uint16_t* R2, float* rrms,
+                               uint16_t* inj_next, int64_t ld_inj_next,
+                               uint16_t* x,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream, void* const* events);
+
+/* The host-side checks of hcgr_forward for a configuration, without a handle,
+ * a device or a launch: returns what hcgr_forward would return before
+ * launching (device and stream checks excluded). Pure host code. */
+hcgr_status hcgr_validate(const hcgr_config* cfg,
+                          const uint16_t* R, const uint16_t* y,
+                          const uint16_t* inj, int64_t ld_inj,
+                          const uint16_t* wnorm, const uint16_t* wd,
+                          const uint16_t* wi, const uint16_t* wu,
+                          int64_t M,
+                          const uint16_t* R2, const float* rrms,
+                          const uint16_t* inj_next, int64_t ld_inj_next,
+                          const uint16_t* x,
+                          const void* workspace, size_t workspace_bytes);
+
+/* Workspace bytes for a configuration without a handle (pure host code). */
+hcgr_status hcgr_workspace_size_for(const hcgr_config* cfg, int64_t M, size_t* bytes);
+
+/* Writes a one-line description of the kernel plan used for M tokens (tile
+ * sizes, split counts, grids) into buf (always NUL-terminated when len > 0). */
+hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, size_t len);
+
+/* Static name of a status code. */
+const char* hcgr_status_string(hcgr_status s);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char* hcgr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCGR_H */

@@ -1,0 +1,247 @@
+"""Python binding of the MI355X Hyper-Connection Gated Residual library.
+
+The functions below carry the C ABI names of ``include/hcgr.h`` and only
+marshal arguments (tensor pointers, sizes, the current HIP stream) to
+``libhcgr.so``; every step of the op runs in the library's HIP kernels.
+PyTorch provides device memory and streams. There is no fallback: if the
+library is missing or cannot be loaded, every call raises.
+
+``HCGR`` is a small convenience object over the same calls that allocates
+outputs and the workspace with torch on the tensors' device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhcgr.so")
+
+HCGR_OK = 0
+HCGR_ERR_INVALID_ARGUMENT = 1
+HCGR_ERR_UNSUPPORTED = 2
+HCGR_ERR_ALIASING = 3
+HCGR_ERR_WORKSPACE_TOO_SMALL = 4
+HCGR_ERR_HIP = 5
+HCGR_WEIGHTS_SEPARATE = 0
+HCGR_WEIGHTS_MERGED_FOLDED = 1
+
+
+class HcgrError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}: {detail}")
+
+
+class hcgr_config(ctypes.Structure):
+    _fields_ = [("hc", ctypes.c_int32), ("hs", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("wnorm_len", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32), ("n_pad", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Config:
+    hc: int = 4
+    hs: int = 2560
+    r: int = 320
+    eps: float = 1e-6
+    wnorm_len: int = 0          # 0 means hs
+    weight_layout: int = HCGR_WEIGHTS_SEPARATE
+    n_pad: int = 0
+
+    def c(self) -> hcgr_config:
+        return hcgr_config(self.hc, self.hs, self.r, self.eps, self.wnorm_len or self.hs,
+                           self.weight_layout, self.n_pad)
+
+    @property
+    def k(self) -> int:
+        return self.hc * self.hs
+
+    @property
+    def merged(self) -> bool:
+        return self.weight_layout == HCGR_WEIGHTS_MERGED_FOLDED
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libhcgr.so (built by ``skinny_gemm_hcgr_amd.build``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m skinny_gemm_hcgr_amd.build` "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    CFG = ctypes.POINTER(hcgr_config)
+    lib.hcgr_create.argtypes = [CFG, ctypes.c_int, ctypes.POINTER(P)]
+    lib.hcgr_destroy.argtypes = [P]
+    lib.hcgr_destroy.restype = None
+    lib.hcgr_workspace_size.argtypes = [P, I64, ctypes.POINTER(SZ)]
+    lib.hcgr_workspace_size_for.argtypes = [CFG, I64, ctypes.POINTER(SZ)]
+    lib.hcgr_forward.argtypes = [P, P, P, P, I64, P, P, P, P, I64, P, P, P, I64, P, P, SZ, P]
+    lib.hcgr_forward_timed.argtypes = [P, P, P, P, I64, P, P, P, P, I64, P, P, P, I64, P, P, SZ, P,
+                                       ctypes.POINTER(P)]
+    lib.hcgr_validate.argtypes = [CFG, P, P, P, I64, P, P, P, P, I64, P, P, P, I64, P, P, SZ]
+    lib.hcgr_describe_plan.argtypes = [CFG, I64, ctypes.c_char_p, SZ]
+    lib.hcgr_status_string.argtypes = [ctypes.c_int]
+    lib.hcgr_status_string.restype = ctypes.c_char_p
+    lib.hcgr_last_error.argtypes = []
+    lib.hcgr_last_error.restype = ctypes.c_char_p
+    for name in ("hcgr_create", "hcgr_workspace_size", "hcgr_workspace_size_for", "hcgr_forward",
+                 "hcgr_forward_timed",
+                 "hcgr_validate", "hcgr_describe_plan"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().hcgr_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return load_library().hcgr_last_error().decode()
+
+
+def _check(status: int, where: str) -> int:
+    if status != HCGR_OK:
+        raise HcgrError(status, where, last_error())
+    return status
+
+
+def _p(t) -> int:
+    """Device (or host) address of a tensor, an int address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+# ------------------------------------------------------- C ABI, same names --
+def hcgr_create(cfg: Config, device: int = 0) -> int:
+    h = ctypes.c_void_p()
+    c = cfg.c()
+    _check(load_library().hcgr_create(ctypes.byref(c), int(device), ctypes.byref(h)), "hcgr_create")
+    return h.value
+
+
+def hcgr_destroy(handle: int) -> None:
+    load_library().hcgr_destroy(handle)
+
+
+def hcgr_workspace_size(handle: int, M: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().hcgr_workspace_size(handle, int(M), ctypes.byref(n)), "hcgr_workspace_size")
+    return n.value
+
+
+def hcgr_workspace_size_for(cfg: Config, M: int) -> int:
+    n = ctypes.c_size_t()
+    c = cfg.c()
+    _check(load_library().hcgr_workspace_size_for(ctypes.byref(c), int(M), ctypes.byref(n)),
+           "hcgr_workspace_size_for")
+    return n.value
+
+
+def hcgr_describe_plan(cfg: Config, M: int) -> str:
+    buf = ctypes.create_string_buffer(1024)
+    c = cfg.c()
+    _check(load_library().hcgr_describe_plan(ctypes.byref(c), int(M), buf, len(buf)), "hcgr_describe_plan")
+    return buf.value.decode()
+
+
+def hcgr_forward(handle, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x,
+                 workspace, workspace_bytes, stream=None, *, check: bool = True) -> int:
+    """Tensors (or raw addresses) in, status out; ``stream`` is a raw hipStream_t
+    (an int), a torch stream, or None for torch's current stream on ``R``'s device."""
+    if stream is None:
+        import torch
+        dev = R.device if hasattr(R, "device") else None
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = load_library().hcgr_forward(handle, _p(R), _p(y), _p(inj), int(ld_inj), _p(wnorm), _p(wd), _p(wi),
+                                     _p(wu), int(M), _p(R2), _p(rrms), _p(inj_next), int(ld_inj_next), _p(x),
+                                     _p(workspace), int(workspace_bytes), stream)
+    if check:
+        _check(st, "hcgr_forward")
+    return st
+
+
+def hcgr_forward_timed(handle, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x,
+                       workspace, workspace_bytes, stream, events) -> int:
+    """``hcgr_forward`` plus 4 caller-owned hipEvent_t marks (raw handles, ints)
+    recorded before the first kernel and after each of the three kernels."""
+    if not isinstance(stream, int):
+        stream = stream.cuda_stream
+    ev = (ctypes.c_void_p * 4)(*events)
+    st = load_library().hcgr_forward_timed(handle, _p(R), _p(y), _p(inj), int(ld_inj), _p(wnorm), _p(wd), _p(wi),
+                                           _p(wu), int(M), _p(R2), _p(rrms), _p(inj_next), int(ld_inj_next), _p(x),
+                                           _p(workspace), int(workspace_bytes), stream, ev)
+    return _check(st, "hcgr_forward_timed")
+
+
+def hcgr_validate(cfg: Config, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x,
+                  workspace, workspace_bytes) -> int:
+    """Host-only argument checks; returns the status code (does not raise)."""
+    c = cfg.c()
+    return load_library().hcgr_validate(ctypes.byref(c), _p(R), _p(y), _p(inj), int(ld_inj), _p(wnorm), _p(wd),
+                                        _p(wi), _p(wu), int(M), _p(R2), _p(rrms), _p(inj_next),
+                                        int(ld_inj_next), _p(x), _p(workspace), int(workspace_bytes))
+
+
+# ------------------------------------------------------------ convenience --
+class HCGR:
+    """Handle + torch-allocated outputs/workspace around ``hcgr_forward``."""
+
+    def __init__(self, cfg: Config = Config(), device: int = 0):
+        self.cfg = cfg
+        self.device = device
+        self.handle = hcgr_create(cfg, device)
+        self._ws = None
+
+    def close(self):
+        if self.handle:
+            hcgr_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace(self, M: int):
+        import torch
+        n = hcgr_workspace_size(self.handle, M)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=f"cuda:{self.device}")
+        return self._ws
+
+    def alloc_outputs(self, M: int, ld_inj_next: int | None = None):
+        import torch
+        c = self.cfg
+        dev = f"cuda:{self.device}"
+        ld = c.hc if ld_inj_next is None else ld_inj_next
+        packed = torch.zeros((M, ld), dtype=torch.bfloat16, device=dev)
+        return {"R2": torch.empty((M, c.k), dtype=torch.bfloat16, device=dev),
+                "rrms": torch.empty((M, c.hc), dtype=torch.float32, device=dev),
+                "inj_next_buf": packed, "inj_next": packed[:, :c.hc], "ld_inj_next": ld,
+                "x": torch.empty((M, c.hs), dtype=torch.bfloat16, device=dev)}
+
+    def forward(self, R, y, inj, wnorm, wd, wi, wu, *, ld_inj: int | None = None, out: dict | None = None,
+                workspace=None, stream=None) -> dict:
+        M = R.shape[0]
+        if out is None:
+            out = self.alloc_outputs(M)
+        ws = self.workspace(M) if workspace is None else workspace
+        ld = inj.stride(0) if ld_inj is None else ld_inj
+        hcgr_forward(self.handle, R, y, inj, ld, wnorm, wd, wi, wu, M, out["R2"], out["rrms"],
+                     out["inj_next"], out["ld_inj_next"], out["x"], ws, ws.numel(), stream)
+        return out

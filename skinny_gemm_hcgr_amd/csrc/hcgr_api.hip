@@ -1,0 +1,316 @@
+// hcgr_api.hip -- C ABI of the HCGR op (declarations and contract in
+// include/hcgr.h). Host code only: argument checks, planning, launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "../../include/hcgr.h"
+#include "hcgr_internal.h"
+
+struct hcgr_op {
+  hcgr::Shape shape;
+  hcgr_config cfg;
+  int device;
+  int cu_count;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hcgr_status fail(hcgr_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+hcgr_status fail(hcgr_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+hcgr_status ok() {
+  g_err[0] = '\0';
+  return HCGR_OK;
+}
+
+// Config checks shared by create, validate and the size queries.
+hcgr_status check_config(const hcgr_config* c, hcgr::Shape* out) {
+  if (!c) return fail(HCGR_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (c->hc < 1 || c->hs < 1 || c->r < 1)
+    return fail(HCGR_ERR_INVALID_ARGUMENT, "hc, hs and r must be positive (hc=%d hs=%d r=%d)", c->hc, c->hs, c->r);
+  if (!std::isfinite(c->eps) || c->eps < 0.0f)
+    return fail(HCGR_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (c->weight_layout != HCGR_WEIGHTS_SEPARATE && c->weight_layout != HCGR_WEIGHTS_MERGED_FOLDED)
+    return fail(HCGR_ERR_INVALID_ARGUMENT, "unknown weight_layout %d", c->weight_layout);
+  const int64_t k = (int64_t)c->hc * c->hs;
+  if (c->wnorm_len != c->hs && (int64_t)c->wnorm_len != k)
+    return fail(HCGR_ERR_INVALID_ARGUMENT, "wnorm_len must be hs (%d) or hc*hs (%lld), got %d", c->hs,
+                (long long)k, c->wnorm_len);
+  if (c->weight_layout == HCGR_WEIGHTS_MERGED_FOLDED && c->n_pad < c->r + c->hc)
+    return fail(HCGR_ERR_INVALID_ARGUMENT, "n_pad (%d) must be >= r + hc (%d)", c->n_pad, c->r + c->hc);
+  if (c->hc != 4) return fail(HCGR_ERR_UNSUPPORTED, "hc=%d: the kernels support hc=4", c->hc);
+  if (c->hs % 128 != 0 || c->hs > 65536)
+    return fail(HCGR_ERR_UNSUPPORTED, "hs=%d: the kernels support multiples of 128 up to 65536", c->hs);
+  if (c->r % 32 != 0 || c->r > 512)
+    return fail(HCGR_ERR_UNSUPPORTED, "r=%d: the kernels support multiples of 32 up to 512", c->r);
+  if (out) {
+    out->hc = c->hc;
+    out->hs = c->hs;
+    out->r = c->r;
+    out->eps = c->eps;
+    out->wn_full = (int64_t)c->wnorm_len == k && c->wnorm_len != c->hs;
+    out->merged = c->weight_layout == HCGR_WEIGHTS_MERGED_FOLDED;
+    out->n_pad = c->n_pad;
+  }
+  return HCGR_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+hcgr_status check_forward(const hcgr_config* cfg, const hcgr::Shape& s, const uint16_t* R, const uint16_t* y,
+                          const uint16_t* inj, int64_t ld_inj, const uint16_t* wnorm, const uint16_t* wd,
+                          const uint16_t* wi, const uint16_t* wu, int64_t M, const void* R2, const float* rrms,
+                          const void* inj_next, int64_t ld_inj_next, const void* x, const void* ws,
+                          size_t ws_bytes, hcgr::Plan* plan_out) {
+  if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
+  if (M > (int64_t)1 << 31) return fail(HCGR_ERR_UNSUPPORTED, "M=%lld exceeds 2^31", (long long)M);
+  if (M == 0) return ok();
+  const bool merged = s.merged;
+  struct P {
+    const void* p;
+    const char* name;
+    size_t align;
+  } ptrs[] = {{R, "R", 16},        {y, "y", 16},   {inj, "inj", 2},       {wnorm, "wnorm", 16},
+              {wd, "wd", 16},      {wu, "wu", 16}, {R2, "R2", 16},        {rrms, "rrms", 4},
+              {inj_next, "inj_next", 2}, {x, "x", 16}};
+  for (const P& p : ptrs) {
+    if (!p.p) return fail(HCGR_ERR_INVALID_ARGUMENT, "%s is NULL", p.name);
+    if ((uintptr_t)p.p % p.align) return fail(HCGR_ERR_INVALID_ARGUMENT, "%s is not %zu-byte aligned", p.name, p.align);
+  }
+  if (merged && wi) return fail(HCGR_ERR_INVALID_ARGUMENT, "wi must be NULL with the merged/folded layout");
+  if (!merged) {
+    if (!wi) return fail(HCGR_ERR_INVALID_ARGUMENT, "wi is NULL");
+    if ((uintptr_t)wi % 16) return fail(HCGR_ERR_INVALID_ARGUMENT, "wi is not 16-byte aligned");
+  }
+  if (ld_inj < s.hc) return fail(HCGR_ERR_INVALID_ARGUMENT, "ld_inj=%lld < hc=%d", (long long)ld_inj, s.hc);
+  if (ld_inj_next < s.hc)
+    return fail(HCGR_ERR_INVALID_ARGUMENT, "ld_inj_next=%lld < hc=%d", (long long)ld_inj_next, s.hc);
+  hcgr::Plan plan = hcgr::make_plan(s, M);
+  if (ws_bytes < plan.ws_bytes)
+    return fail(HCGR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed for M=%lld", ws_bytes,
+                plan.ws_bytes, (long long)M);
+  if (!ws) return fail(HCGR_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if ((uintptr_t)ws % 16) return fail(HCGR_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+
+  const uint64_t K = (uint64_t)s.k(), HS = (uint64_t)s.hs, HC = (uint64_t)s.hc, r = (uint64_t)s.r;
+  const uint64_t m = (uint64_t)M;
+  auto rng = [](const void* p, uint64_t bytes, const char* n) {
+    return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes, n};
+  };
+  const uint64_t wrows = merged ? (uint64_t)s.n_pad : r;
+  const Range ins[] = {
+      rng(R, m * K * 2, "R"),
+      rng(y, m * HS * 2, "y"),
+      rng(inj, ((m - 1) * (uint64_t)ld_inj + HC) * 2, "inj"),
+      rng(wnorm, (uint64_t)cfg->wnorm_len * 2, "wnorm"),
+      rng(wd, wrows * K * 2, "wd"),
+      rng(merged ? nullptr : wi, merged ? 0 : HC * K * 2, "wi"),
+      rng(wu, K * r * 2, "wu"),
+  };
+  const Range outs[] = {
+      rng(R2, m * K * 2, "R2"),
+      rng(rrms, m * HC * 4, "rrms"),
+      rng(inj_next, ((m - 1) * (uint64_t)ld_inj_next + HC) * 2, "inj_next"),
+      rng(x, m * HS * 2, "x"),
+      rng(ws, plan.ws_bytes, "workspace"),
+  };
+  const int nin = sizeof ins / sizeof ins[0], nout = sizeof outs / sizeof outs[0];
+  for (int i = 0; i < nout; ++i) {
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(HCGR_ERR_ALIASING, "output %s overlaps output %s", outs[i].name, outs[j].name);
+    for (int j = 0; j < nin; ++j)
+      if (ins[j].hi > ins[j].lo && overlap(outs[i], ins[j]))
+        return fail(HCGR_ERR_ALIASING, "output %s overlaps input %s", outs[i].name, ins[j].name);
+  }
+  if (plan_out) *plan_out = plan;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hcgr_status_string(hcgr_status s) {
+  switch (s) {
+    case HCGR_OK: return "HCGR_OK";
+    case HCGR_ERR_INVALID_ARGUMENT: return "HCGR_ERR_INVALID_ARGUMENT";
+    case HCGR_ERR_UNSUPPORTED: return "HCGR_ERR_UNSUPPORTED";
+    case HCGR_ERR_ALIASING: return "HCGR_ERR_ALIASING";
+    case HCGR_ERR_WORKSPACE_TOO_SMALL: return "HCGR_ERR_WORKSPACE_TOO_SMALL";
+    case HCGR_ERR_HIP: return "HCGR_ERR_HIP";
+  }
+  return "HCGR_ERR_UNKNOWN";
+}
+
+const char* hcgr_last_error(void) { return g_err; }
+
+hcgr_status hcgr_workspace_size_for(const hcgr_config* cfg, int64_t M, size_t* bytes) {
+  hcgr::Shape s;
+  hcgr_status st = check_config(cfg, &s);
+  if (st != HCGR_OK) return st;
+  if (!bytes) return fail(HCGR_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
+  *bytes = hcgr::make_plan(s, M).ws_bytes;
+  return ok();
+}
+
+hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, size_t len) {
+  hcgr::Shape s;
+  hcgr_status st = check_config(cfg, &s);
+  if (st != HCGR_OK) return st;
+  if (!buf && len) return fail(HCGR_ERR_INVALID_ARGUMENT, "buf is NULL");
+  if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
+  hcgr::Plan p = hcgr::make_plan(s, M);
+  if (len) {
+    if (M == 0) {
+      snprintf(buf, len, "M=0: no launch");
+    } else {
+      hcgr::K1Shape a = hcgr::k1_shape(p.k1);
+      hcgr::K2Shape b = hcgr::k2_shape(p.k2);
+      snprintf(buf, len,
+               "M=%lld mpad=%lld | k1 tm=%d waves=%d blocks/wave=%d stage_k=%d k_chunk=%d chunks=%d n_tiles=%d "
+               "grid=%dx%lld | reduce grid=%lldx%d | k2 tm=%d waves=%d rowblocks/wave=%d channels=%d grid=%dx%lld | "
+               "workspace=%zu",
+               (long long)M, (long long)p.mpad, a.tm, a.nw, a.nbw, a.ks, p.kc, p.nkc, p.ntiles_n,
+               p.ntiles_n * p.nkc, (long long)(p.mpad / p.tm), (long long)((p.mpad + 63) / 64),
+               (s.n_rows() + 31) / 32, b.tm, b.nw, b.rbw, p.cb, s.hs / p.cb, (long long)(p.mpad / p.tm),
+               p.ws_bytes);
+    }
+  }
+  return ok();
+}
+
+hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out) {
+  if (!out) return fail(HCGR_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  hcgr::Shape s;
+  hcgr_status st = check_config(cfg, &s);
+  if (st != HCGR_OK) return st;
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return fail(HCGR_ERR_HIP, "hipGetDeviceCount: %s", hipGetErrorString(e));
+  if (device < 0 || device >= ndev)
+    return fail(HCGR_ERR_INVALID_ARGUMENT, "device %d out of range (%d devices)", device, ndev);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return fail(HCGR_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(HCGR_ERR_UNSUPPORTED, "device %d is %s; the kernels are built for gfx950 (MI355X)", device,
+                prop.gcnArchName);
+  int cur = -1;
+  e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(HCGR_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (cur != device && (e = hipSetDevice(device)) != hipSuccess)
+    return fail(HCGR_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(e));
+  int ke = hcgr::configure_kernels();
+  if (cur != device) (void)hipSetDevice(cur);
+  if (ke != (int)hipSuccess)
+    return fail(HCGR_ERR_HIP, "kernel attribute set-up failed: %s", hipGetErrorString((hipError_t)ke));
+  hcgr_op* op = new (std::nothrow) hcgr_op;
+  if (!op) return fail(HCGR_ERR_INVALID_ARGUMENT, "out of host memory");
+  op->shape = s;
+  op->cfg = *cfg;
+  op->device = device;
+  op->cu_count = prop.multiProcessorCount;
+  *out = op;
+  return ok();
+}
+
+void hcgr_destroy(hcgr_handle h) { delete h; }
+
+hcgr_status hcgr_workspace_size(hcgr_handle h, int64_t M, size_t* bytes) {
+  if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
+  return hcgr_workspace_size_for(&h->cfg, M, bytes);
+}
+
+hcgr_status hcgr_validate(const hcgr_config* cfg, const uint16_t* R, const uint16_t* y, const uint16_t* inj,
+                          int64_t ld_inj, const uint16_t* wnorm, const uint16_t* wd, const uint16_t* wi,
+                          const uint16_t* wu, int64_t M, const uint16_t* R2, const float* rrms,
+                          const uint16_t* inj_next, int64_t ld_inj_next, const uint16_t* x, const void* workspace,
+                          size_t workspace_bytes) {
+  hcgr::Shape s;
+  hcgr_status st = check_config(cfg, &s);
+  if (st != HCGR_OK) return st;
+  return check_forward(cfg, s, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x,
+                       workspace, workspace_bytes, nullptr);
+}
+
+static hcgr_status forward_impl(hcgr_handle h, const uint16_t* R, const uint16_t* y, const uint16_t* inj,
+                                int64_t ld_inj, const uint16_t* wnorm, const uint16_t* wd, const uint16_t* wi,
+                                const uint16_t* wu, int64_t M, uint16_t* R2, float* rrms, uint16_t* inj_next,
+                                int64_t ld_inj_next, uint16_t* x, void* workspace, size_t workspace_bytes,
+                                void* stream, void* const* events) {
+  if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
+  hcgr::Plan plan;
+  hcgr_status st = check_forward(&h->cfg, h->shape, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next,
+                                 ld_inj_next, x, workspace, workspace_bytes, &plan);
+  if (st != HCGR_OK || M == 0) return st;
+  int dev = -1;
+  hipError_t e;
+  if (stream) {
+    e = hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dev);
+    if (e != hipSuccess) return fail(HCGR_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  } else {
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(HCGR_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev != h->device)
+    return fail(HCGR_ERR_INVALID_ARGUMENT, "stream belongs to device %d, handle to device %d", dev, h->device);
+  int cur = -1;
+  e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(HCGR_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (cur != h->device) {
+    e = hipSetDevice(h->device);
+    if (e != hipSuccess) return fail(HCGR_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(e));
+  }
+  hcgr::ForwardArgs a;
+  a.R = R; a.y = y; a.inj = inj; a.wnorm = wnorm; a.wd = wd; a.wi = wi; a.wu = wu;
+  a.ld_inj = ld_inj; a.ld_inj_next = ld_inj_next; a.M = M;
+  a.R2 = R2; a.inj_next = inj_next; a.x = x; a.rrms = rrms; a.ws = workspace;
+  int le = hcgr::launch_forward(h->shape, plan, a, stream, events);
+  if (cur != h->device) (void)hipSetDevice(cur);
+  if (le != (int)hipSuccess)
+    return fail(HCGR_ERR_HIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)le));
+  return ok();
+}
+
+hcgr_status hcgr_forward(hcgr_handle h, const uint16_t* R, const uint16_t* y, const uint16_t* inj, int64_t ld_inj,
+                         const uint16_t* wnorm, const uint16_t* wd, const uint16_t* wi, const uint16_t* wu, int64_t M,
+                         uint16_t* R2, float* rrms, uint16_t* inj_next, int64_t ld_inj_next, uint16_t* x,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(h, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+hcgr_status hcgr_forward_timed(hcgr_handle h, const uint16_t* R, const uint16_t* y, const uint16_t* inj,
+                               int64_t ld_inj, const uint16_t* wnorm, const uint16_t* wd, const uint16_t* wi,
+                               const uint16_t* wu, int64_t M, uint16_t* R2, float* rrms, uint16_t* inj_next,
+                               int64_t ld_inj_next, uint16_t* x, void* workspace, size_t workspace_bytes,
+                               void* stream, void* const* events) {
+  if (!events) return fail(HCGR_ERR_INVALID_ARGUMENT, "events is NULL");
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return fail(HCGR_ERR_INVALID_ARGUMENT, "events[%d] is NULL", i);
+  return forward_impl(h, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x, workspace,
+                      workspace_bytes, stream, events);
+}
+
+}  // extern "C"

@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path (called through the C ABI binding) against the
+fp64 oracle on the same seeded inputs. Small and mid M are compared on every
+row; the M=8192 and M=65536 workloads, in the configuration the benchmark
+times, on sampled rows (every step is per token, so a row of a large call is
+checked by running the oracle on that row alone)."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import check_all, check_r2, check_rrms, check_tol, to64
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = synth.Shape()
+
+
+@pytest.fixture(scope="module")
+def H():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import skinny_gemm_hcgr_amd as H
+    H.load_library()
+    return H
+
+
+@pytest.fixture(scope="module")
+def op(H):
+    o = H.HCGR(H.Config(), 0)
+    yield o
+    o.close()
+
+
+@pytest.fixture(scope="module")
+def weights():
+    return synth.make_weights(SHAPE, seed=0, device="cuda")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_oracle(inp, rows=None, merged=False, n_pad=0, wnorm_full=False, wd_key="wd"):
+    cfg = oracle.OracleConfig(wnorm_full=wnorm_full, merged=merged, n_pad=n_pad)
+    R, y, inj = inp["R"], inp["y"], inp["inj"]
+    if rows is not None:
+        idx = torch.as_tensor(rows, device=R.device)
+        R, y, inj = R[idx], y[idx], inj[idx]
+    return oracle.forward(cfg, R.cpu(), y.cpu(), inj.cpu().contiguous(), inp["wnorm"].cpu(), inp[wd_key].cpu(),
+                          None if merged else inp["wi"].cpu(), inp["wu"].cpu(),
+                          ld_inj=inj.shape[1])
+
+
+def gpu_forward(op, inp, *, wd=None, wi="default", ld_next=None):
+    M = inp["R"].shape[0]
+    out = op.alloc_outputs(M, ld_next)
+    op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"] if wd is None else wd,
+               inp["wi"] if wi == "default" else wi, inp["wu"], out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+def sample_rows(M, n=96, seed=1):
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, M // 2, M - 2, M - 1} | set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < M))
+
+
+SWEEP = [1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 224, 257, 512, 1000,
+         1024, 1025]
+
+
+@pytest.mark.parametrize("M", SWEEP)
+def test_token_sweep_every_row(op, weights, M):
+    _say(f"[parity] sweep M={M} plan: {__import__('skinny_gemm_hcgr_amd').hcgr_describe_plan(op.cfg, M)}")
+    inp = synth.make_inputs(M, SHAPE, seed=0, device="cuda", weights=weights)
+    out = gpu_forward(op, inp)
+    ref = run_oracle(inp)
+    check_all(out, ref)
+
+
+@pytest.mark.parametrize("M", [2048, 4095, 4096, 8192, 16384, 65536])
+def test_token_sweep_sampled_rows(op, weights, M):
+    _say(f"[parity] sampled M={M}")
+    inp = synth.make_inputs(M, SHAPE, seed=0, device="cuda", weights=weights)
+    out = gpu_forward(op, inp)
+    rows = sample_rows(M)
+    check_all(out, run_oracle(inp, rows), rows)
+
+
+def test_decode_m1(op, weights):
+    inp = synth.make_inputs(1, SHAPE, seed=0, device="cuda", weights=weights)
+    check_all(gpu_forward(op, inp), run_oracle(inp))
+
+
+def test_decode_m32(op, weights):
+    inp = synth.make_inputs(32, SHAPE, seed=0, device="cuda", weights=weights)
+    check_all(gpu_forward(op, inp), run_oracle(inp))
+
+
+@pytest.mark.parametrize("M", [1, 7, 32, 100, 1024, 3000, 8192])
+def test_merged_folded_n336(H, weights, M):
+    """Merged 336-row down/inject weight with (1+Wnorm) folded in (the M=1024
+    workload; also decode and large M, where the folded path has no other
+    coverage)."""
+    _say(f"[parity] merged M={M}")
+    o = H.HCGR(H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336), 0)
+    inp = synth.make_inputs(M, SHAPE, seed=0, device="cuda", weights=weights)
+    inp["wm"] = synth.fold_merged_weight(inp["wd"], inp["wi"], inp["wnorm"], 336, SHAPE.hs)
+    out = gpu_forward(o, inp, wd=inp["wm"], wi=None)
+    rows = None if M <= 1024 else sample_rows(M)
+    check_all(out, run_oracle(inp, rows, merged=True, n_pad=336, wd_key="wm"), rows)
+    o.close()
+
+
+def test_prefill_m8192_stream0_x8(op, weights):
+    """M=8192 with stream 0 of R scaled by 8 (per-stream RMS range)."""
+    inp = synth.make_inputs(8192, SHAPE, seed=0, device="cuda", weights=weights, scale_stream0=8.0)
+    out = gpu_forward(op, inp)
+    rows = sample_rows(8192, 128)
+    ref = run_oracle(inp, rows)
+    check_all(out, ref, rows)
+    r = to64(out["rrms"][torch.as_tensor(rows, device="cuda")])
+    assert np.all(r[:, 0] < r[:, 1:].min(axis=1))
+
+
+def test_strided_injection_and_layer_chaining(op, weights):
+    """inj_next written into a packed [M, 336] buffer (row stride 336) is fed
+    back as the next call's inj, like consecutive layers; padding columns of
+    the packed buffer must stay untouched."""
+    M = 37
+    inp = synth.make_inputs(M, SHAPE, seed=4, device="cuda", weights=weights, ld_inj=336)
+    assert inp["inj"].stride(0) == 336
+    out1 = gpu_forward(op, inp, ld_next=336)
+    check_all(out1, run_oracle(inp))
+    assert torch.all(out1["inj_next_buf"][:, 4:] == 0)
+    y2 = synth.normal_bf16(9, 2, M, SHAPE.hs, device="cuda")
+    inp2 = dict(inp, R=out1["R2"], y=y2, inj=out1["inj_next"])
+    out2 = gpu_forward(op, inp2)
+    check_all(out2, run_oracle(inp2))
+
+
+def test_full_width_wnorm(H):
+    o = H.HCGR(H.Config(wnorm_len=SHAPE.k), 0)
+    inp = synth.make_inputs(40, SHAPE, seed=5, device="cuda", wnorm_full=True)
+    check_all(gpu_forward(o, inp), run_oracle(inp, wnorm_full=True))
+    o.close()
+
+
+@pytest.mark.parametrize("M", [3, 40, 300])
+def test_wide_gates(op, M):
+    """Unit-test variant with wider projections (Wd ~ N(0, 64/K), Wu ~ N(0, 4/r)) so
+    that the gate spans (0, 1) and the up/sigmoid/mix path carries real weight."""
+    inp = synth.make_inputs(M, SHAPE, seed=6, device="cuda", wd_std=8 / SHAPE.k ** 0.5, wu_std=2 / SHAPE.r ** 0.5)
+    ref = oracle.forward(oracle.OracleConfig(), inp["R"].cpu(), inp["y"].cpu(), inp["inj"].cpu(), inp["wnorm"].cpu(),
+                         inp["wd"].cpu(), inp["wi"].cpu(), inp["wu"].cpu(), debug=True)
+    assert np.ptp(ref["G"]) > 0.9
+    check_all(gpu_forward(op, inp), ref)
+
+
+def test_zero_rows(op, weights):
+    """All-zero rows: rrms = 1/sqrt(eps), x = 0, inj_next = 0."""
+    inp = synth.make_inputs(20, SHAPE, seed=7, device="cuda", weights=weights)
+    inp["R"][3:6] = 0
+    inp["y"][3:6] = 0
+    out = gpu_forward(op, inp)
+    check_all(out, run_oracle(inp))
+    assert torch.all(out["x"][3:6] == 0) and torch.all(out["inj_next"][3:6] == 0)
+
+
+def test_deterministic(op, weights):
+    for M in (5, 33, 2048):
+        inp = synth.make_inputs(M, SHAPE, seed=8, device="cuda", weights=weights)
+        a = gpu_forward(op, inp)
+        b = gpu_forward(op, inp)
+        for k in ("R2", "rrms", "inj_next", "x"):
+            assert torch.equal(a[k], b[k]), (M, k)
+
+
+def test_row_independence(op, weights):
+    """A row of a large call equals the same row run alone: R2 bit for bit
+    (same elementwise formula in every plan), the rest within tolerance."""
+    inp = synth.make_inputs(1024, SHAPE, seed=9, device="cuda", weights=weights)
+    big = gpu_forward(op, inp)
+    for m in (0, 511, 1023):
+        one = gpu_forward(op, dict(inp, R=inp["R"][m:m + 1], y=inp["y"][m:m + 1], inj=inp["inj"][m:m + 1]))
+        assert torch.equal(one["R2"][0], big["R2"][m])
+        check_rrms(one["rrms"][0], to64(big["rrms"][m]))
+        check_tol(one["x"][0], to64(big["x"][m]), "x")
+        check_tol(one["inj_next"][0], to64(big["inj_next"][m]), "inj_next")
+
+
+def test_workspace_reuse_across_sizes(H, op, weights):
+    """One workspace shared by calls of different M (different plans) in a row:
+    a call's result does not depend on what an earlier call left behind."""
+    ws = torch.empty(H.hcgr_workspace_size(op.handle, 2048) + 4096, dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)  # NaN patterns everywhere
+    res = {}
+    for M in (2048, 7, 300, 7, 33):
+        inp = synth.make_inputs(M, SHAPE, seed=10, device="cuda", weights=weights)
+        out = op.alloc_outputs(M)
+        op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"], out=out,
+                   workspace=ws)
+        torch.cuda.synchronize()
+        if M in res:
+            for k in ("R2", "rrms", "inj_next", "x"):
+                assert torch.equal(res[M][k], out[k]), (M, k)
+        res[M] = out
+    inp = synth.make_inputs(7, SHAPE, seed=10, device="cuda", weights=weights)
+    check_all(res[7], run_oracle(inp))
+
+
+def test_graph_capture_replays(op, weights):
+    """hcgr_forward captured into a HIP graph: several replays with new input
+    values written between them, each checked against an eager call."""
+    M = 48
+    inp = synth.make_inputs(M, SHAPE, seed=11, device="cuda", weights=weights)
+    out = op.alloc_outputs(M)
+    ws = op.workspace(M)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"], out=out,
+                   workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"], out=out,
+                   workspace=ws)
+    for rep in range(4):
+        fresh = synth.make_inputs(M, SHAPE, seed=100 + rep, device="cuda", weights=weights)
+        inp["R"].copy_(fresh["R"])
+        inp["y"].copy_(fresh["y"])
+        inp["inj"].copy_(fresh["inj"])
+        g.replay()
+        torch.cuda.synchronize()
+        eager = gpu_forward(op, fresh)
+        for k in ("R2", "rrms", "inj_next", "x"):
+            assert torch.equal(out[k], eager[k]), (rep, k)
+        if rep == 0:
+            check_all(out, run_oracle(fresh))
+
+
+def test_m0_and_errors_on_device(H, op, weights):
+    z = torch.empty(0, SHAPE.k, dtype=torch.bfloat16, device="cuda")
+    assert H.hcgr_forward(op.handle, z, None, None, 4, None, None, None, None, 0, None, None, None, 4, None,
+                          None, 0) == H.HCGR_OK
+    inp = synth.make_inputs(4, SHAPE, seed=0, device="cuda", weights=weights)
+    out = op.alloc_outputs(4)
+    ws = op.workspace(4)
+    with pytest.raises(H.HcgrError) as e:  # R2 aliasing R
+        H.hcgr_forward(op.handle, inp["R"], inp["y"], inp["inj"], 4, inp["wnorm"], inp["wd"], inp["wi"], inp["wu"],
+                       4, inp["R"], out["rrms"], out["inj_next"], 4, out["x"], ws, ws.numel())
+    assert e.value.status == H.HCGR_ERR_ALIASING
+    before = out["x"].clone()
+    with pytest.raises(H.HcgrError) as e:  # workspace too small: nothing written
+        H.hcgr_forward(op.handle, inp["R"], inp["y"], inp["inj"], 4, inp["wnorm"], inp["wd"], inp["wi"], inp["wu"],
+                       4, out["R2"], out["rrms"], out["inj_next"], 4, out["x"], ws, 16)
+    assert e.value.status == H.HCGR_ERR_WORKSPACE_TOO_SMALL
+    torch.cuda.synchronize()
+    assert torch.equal(before, out["x"])
