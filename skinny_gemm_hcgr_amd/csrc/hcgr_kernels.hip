@@ -80,7 +80,7 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_down(DownArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t act[2][TM * LDA];
   __shared__ float ssp[NCH];
-  __shared__ float iws[TM];
+  __shared__ float iwh[TM], iwl[TM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,12 +94,17 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_down(DownArgs a) {
   const int nstage = a.KC / KS;
   const int koff = 8 * (lane >> 4);
 
-  // (COMBINE) iw = 2 * sigmoid(inj[s] / HC) for this stream, per token row
+  // (COMBINE) iw = 2 * sigmoid(inj[s] / HC) for this stream, per token row.
+  // Formed in fp64 and kept as an fp32 pair iw = hi + lo (~48 bits): when R
+  // and y*iw nearly cancel, R2 is far smaller than y and a single fp32 iw
+  // would put an error of |y| * 2^-24 on it, several bf16 ulps of R2.
   if (tid < TM) {
     const int64_t m = m0 + tid;
-    float v = 0.0f;
-    if (m < a.M) v = 2.0f * sigmoid_f(bf1(a.inj[m * a.ld_inj + s]) * a.inv_hc);
-    iws[tid] = v;
+    double v = 0.0;
+    if (m < a.M) v = 2.0 / (1.0 + exp(-(double)bf1(a.inj[m * a.ld_inj + s]) / (double)a.HC));
+    const float hi = (float)v;
+    iwh[tid] = hi;
+    iwl[tid] = (float)(v - (double)hi);
   }
 
   // weight rows of this wave (A operand rows = down/inject output rows n)
@@ -157,7 +162,8 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_down(DownArgs a) {
       if (q < NCH) {
         const int t = q / CPR;
         const int col = (q % CPR) * 8;
-        const float iw = iws[t];
+        const float ih = iwh[t];
+        const float il = iwl[t];
         const uint32_t rw[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
         const uint32_t yw[4] = {yv[j].x, yv[j].y, yv[j].z, yv[j].w};
         const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
@@ -165,8 +171,9 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_down(DownArgs a) {
         float acc = ss[j];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float r0 = fmaf(bf_lo(yw[e]), iw, bf_lo(rw[e]));
-          const float r1 = fmaf(bf_hi(yw[e]), iw, bf_hi(rw[e]));
+          // R2 = (R + y*hi) + y*lo: each fma rounds once, relative to R2 itself
+          const float r0 = fmaf(bf_lo(yw[e]), il, fmaf(bf_lo(yw[e]), ih, bf_lo(rw[e])));
+          const float r1 = fmaf(bf_hi(yw[e]), il, fmaf(bf_hi(yw[e]), ih, bf_hi(rw[e])));
           acc = fmaf(r0, r0, acc);
           acc = fmaf(r1, r1, acc);
           o2[e] = pack_bf2(r0, r1);
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_down(DownArgs a) {
 
   load_w(kbeg);
   load_a(kbeg);
-  __syncthreads();  // iws visible
+  __syncthreads();  // iwh/iwl visible
   store_a(kbeg, 0);
   __syncthreads();
 

@@ -163,6 +163,24 @@ def test_wide_gates(op, M):
     check_all(gpu_forward(op, inp), ref)
 
 
+def test_r2_under_cancellation(op, weights):
+    """R chosen as -bf16(y*iw) so that R2 = R + y*iw nearly cancels everywhere
+    (|R2| down to ~1e-8 |y|): R2 must still be within one bf16 ulp of the
+    exact value, which needs iw to better than fp32 precision."""
+    M = 24
+    inp = synth.make_inputs(M, SHAPE, seed=12, device="cuda", weights=weights)
+    inj = inp["inj"].double().cpu()
+    iw = 2.0 / (1.0 + torch.exp(-inj / SHAPE.hc))  # [M, HC]
+    y = inp["y"].double().cpu()
+    R = -(y[:, None, :] * iw[:, :, None]).reshape(M, SHAPE.k)
+    inp["R"] = R.to(torch.bfloat16).cuda()
+    out = gpu_forward(op, inp)
+    ref = run_oracle(inp)
+    tiny = np.abs(ref["R2"]) < 1e-3 * np.abs(to64(inp["R"]))
+    assert tiny.mean() > 0.5
+    check_all(out, ref)
+
+
 def test_zero_rows(op, weights):
     """All-zero rows: rrms = 1/sqrt(eps), x = 0, inj_next = 0."""
     inp = synth.make_inputs(20, SHAPE, seed=7, device="cuda", weights=weights)
