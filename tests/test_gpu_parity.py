@@ -275,6 +275,7 @@ def test_m0_and_errors_on_device(H, op, weights):
         H.hcgr_forward(op.handle, inp["R"], inp["y"], inp["inj"], 4, inp["wnorm"], inp["wd"], inp["wi"], inp["wu"],
                        4, inp["R"], out["rrms"], out["inj_next"], 4, out["x"], ws, ws.numel())
     assert e.value.status == H.HCGR_ERR_ALIASING
+    out["x"].fill_(7.0)
     before = out["x"].clone()
     with pytest.raises(H.HcgrError) as e:  # workspace too small: nothing written
         H.hcgr_forward(op.handle, inp["R"], inp["y"], inp["inj"], 4, inp["wnorm"], inp["wd"], inp["wi"], inp["wu"],
