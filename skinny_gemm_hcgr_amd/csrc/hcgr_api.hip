@@ -188,11 +188,10 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
       hcgr::K2Shape b = hcgr::k2_shape(p.k2);
       snprintf(buf, len,
                "M=%lld mpad=%lld | k1 tm=%d waves=%d blocks/wave=%d stage_k=%d k_chunk=%d chunks=%d n_tiles=%d "
-               "grid=%dx%lld | reduce grid=%lldx%d | k2 tm=%d waves=%d rowblocks/wave=%d channels=%d grid=%dx%lld | "
+               "grid=%dx%lld | reduce waves=%lld | k2 tm=%d waves=%d rowblocks/wave=%d channels=%d grid=%dx%lld | "
                "workspace=%zu",
                (long long)M, (long long)p.mpad, a.tm, a.nw, a.nbw, a.ks, p.kc, p.nkc, p.ntiles_n,
-               p.ntiles_n * p.nkc, (long long)(p.mpad / p.tm), (long long)((p.mpad + 63) / 64),
-               (s.n_rows() + 31) / 32, b.tm, b.nw, b.rbw, p.cb, s.hs / p.cb, (long long)(p.mpad / p.tm),
+               p.ntiles_n * p.nkc, (long long)(p.mpad / p.tm), (long long)(s.n_rows() * (p.mpad / 16)), b.tm, b.nw, b.rbw, p.cb, s.hs / p.cb, (long long)(p.mpad / p.tm),
                p.ws_bytes);
     }
   }

@@ -41,6 +41,9 @@ inline K2Shape k2_shape(int v) {
   static const K2Shape t[K2_NVAR] = {{16, 4, 1}, {32, 4, 1}, {64, 4, 1}, {64, 4, 4}};
   return t[v];
 }
+// Chunks per stream handled by one lane group of the reduction kernel: the
+// split plans keep chunks-per-stream <= 4 * kRedPerLane.
+constexpr int kRedPerLane = 8;
 
 struct Shape {
   int hc, hs, r;
@@ -59,7 +62,7 @@ struct Plan {
   int tm = 0;
   int k1 = 0, k2 = 0;
   int kc = 0, nkc = 0, kcps = 0;   // k per chunk, chunk count, chunks per stream
-  int ntiles_n = 0;                // K1 n tiles
+  int ntiles_n = 0;                // K1 n tiles (split plan)
   int cb = 0;                      // K2 channels per workgroup
   size_t off_p = 0, off_ss = 0, off_h = 0, ws_bytes = 0;
 };
@@ -72,7 +75,7 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   p.M = M;
   if (M <= 0) return p;
   const int hs = s.hs;
-  // K1 variant and K chunk
+  // split plan: partial sums per K chunk, separate reduction kernel (K1 + K1r + K2)
   int kc;
   if (M <= 16) { p.k1 = K1_T16; p.k2 = K2_T16; kc = 128; }
   else if (M <= 32) { p.k1 = K1_T32; p.k2 = K2_T32; kc = 128; }
@@ -86,9 +89,16 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   }
   const K1Shape a = k1_shape(p.k1);
   const K2Shape b = k2_shape(p.k2);
-  // the chunk must divide the stream width and hold whole LDS stages
-  while (kc > a.ks && (hs % kc != 0 || kc % a.ks != 0)) kc -= a.ks;
-  if (kc < a.ks || hs % kc != 0) kc = a.ks;
+  // the chunk must divide the stream width and hold whole LDS stages, and a
+  // stream may have at most 4 * kRedPerLane chunks (hs itself always fits)
+  auto valid = [&](int c) { return c >= a.ks && c % a.ks == 0 && hs % c == 0; };
+  while (kc > a.ks && !valid(kc)) kc -= a.ks;
+  if (!valid(kc)) kc = a.ks;
+  while (hs / kc > 4 * kRedPerLane) {
+    int c = kc + a.ks;
+    while (!valid(c)) c += a.ks;
+    kc = c;
+  }
   p.tm = a.tm;  // K1 and K2 share the token tile of a plan
   p.kc = kc;
   p.kcps = hs / kc;

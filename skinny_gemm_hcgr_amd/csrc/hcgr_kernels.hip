@@ -258,10 +258,12 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_down(DownArgs a) {
 
 // ---------------------------------------------------------------------------
 // K1r: per token, rrms[s] = 1/sqrt(sum of the stream's chunk sums of squares
-// / HS + eps); row n of the contraction = sum_s rrms[s] * sum over the
-// stream's chunks; down rows -> h = SiLU(v/HC) (bf16, workspace), inject
-// rows -> inj_next (bf16). 64 tokens x 32 rows per workgroup, transposed
-// through LDS so that the partial reads and the h writes are both coalesced.
+// / HS + eps); row n of the contraction = sum_s rrms[s] * (sum of the
+// stream's chunk partials); down rows -> h = SiLU(v/HC) (bf16, workspace),
+// inject rows -> inj_next (bf16). One wave per (row n, 16 tokens): lane
+// l handles token l % 16 and every 4th chunk starting at l / 16; all of a
+// lane's loads are issued before the first add (one memory round trip), and
+// the four lane groups are then summed with cross-lane adds. HC = 4.
 // ---------------------------------------------------------------------------
 struct ReduceArgs {
   const float* P;
@@ -275,57 +277,61 @@ struct ReduceArgs {
   int64_t ld_inj_next;
 };
 
+__device__ __forceinline__ float sum_lane_groups(float v) {
+  // lanes l, l^16, l^32, l^48 hold the four chunk groups of one token
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
-  __shared__ float tile[32][65];
-  const int tid = threadIdx.x;
-  const int tm = tid & 63;
-  const int ng = tid >> 6;
-  const int64_t mb = (int64_t)blockIdx.x * 64;
-  const int64_t m = mb + tm;
-  const int n0 = blockIdx.y * 32;
-  float rr[8];
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t mblocks = a.Mpad / 16;
+  const int n = (int)(wid / mblocks);
+  if (n >= a.n_rows) return;  // whole wave leaves together
+  const int64_t m = (wid % mblocks) * 16 + (lane & 15);
+  const int g = lane >> 4;
+  const int kcps = a.kcps;  // <= 4 * kRedPerLane
+  float sv[4][kRedPerLane], pv[4][kRedPerLane];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) rr[s] = 0.0f;
-  if (m < a.Mpad) {
-    for (int s = 0; s < a.HC; ++s) {
-      float t = 0.0f;
-      for (int c = 0; c < a.kcps; ++c) t += a.SS[(int64_t)(s * a.kcps + c) * a.Mpad + m];
-      rr[s] = 1.0f / sqrtf(t * a.inv_hs + a.eps);
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < kRedPerLane; ++i) {
+      const int c = g + 4 * i;
+      const int64_t kc = (int64_t)s * kcps + c;
+      sv[s][i] = c < kcps ? a.SS[kc * a.Mpad + m] : 0.0f;
+      pv[s][i] = c < kcps ? a.P[(kc * a.NP + n) * a.Mpad + m] : 0.0f;
     }
-    if (blockIdx.y == 0 && ng == 0 && m < a.M)
-      for (int s = 0; s < a.HC; ++s) a.rrms[m * a.HC + s] = rr[s];
+  float ss[4], ps[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float t = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRedPerLane; ++i) {
+      t += sv[s][i];
+      u += pv[s][i];
+    }
+    ss[s] = t;
+    ps[s] = u;
   }
+  float v = 0.0f;
+  float rr[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int nn = ng + 4 * i;
-    const int n = n0 + nn;
-    float v = 0.0f;
-    if (n < a.n_rows && m < a.Mpad) {
-      for (int s = 0; s < a.HC; ++s) {
-        float ps = 0.0f;
-        for (int c = 0; c < a.kcps; ++c) ps += a.P[((int64_t)(s * a.kcps + c) * a.NP + n) * a.Mpad + m];
-        v = fmaf(rr[s], ps, v);
-      }
-    }
-    tile[nn][tm] = v;
+  for (int s = 0; s < 4; ++s) {
+    rr[s] = 1.0f / sqrtf(sum_lane_groups(ss[s]) * a.inv_hs + a.eps);
+    v = fmaf(rr[s], sum_lane_groups(ps[s]), v);
   }
-  __syncthreads();
-  const int nn = tid & 31;
-  const int tg = tid >> 5;
-  const int n = n0 + nn;
+  if (g != 0) return;
+  if (n == 0 && m < a.M) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int tt = tg + 8 * i;
-    const int64_t mm = mb + tt;
-    if (mm >= a.Mpad) continue;
-    const float v = tile[nn][tt];
-    if (n < a.r) {
-      const float z = v * a.inv_hc;
-      const float hv = z * sigmoid_f(z);  // (G1) SiLU(lora / HC)
-      a.h[mm * a.r + n] = (mm < a.M) ? to_bf(hv) : (uint16_t)0;
-    } else if (n < a.n_rows && mm < a.M) {
-      a.inj_next[mm * a.ld_inj_next + (n - a.r)] = to_bf(v);  // (INJ), not scaled
-    }
+    for (int s = 0; s < 4; ++s) a.rrms[m * 4 + s] = rr[s];
+  }
+  if (n < a.r) {
+    const float z = v * a.inv_hc;
+    a.h[m * a.r + n] = (m < a.M) ? to_bf(z * sigmoid_f(z)) : (uint16_t)0;  // (G1) SiLU(lora / HC)
+  } else if (m < a.M) {
+    a.inj_next[m * a.ld_inj_next + (n - a.r)] = to_bf(v);  // (INJ), not scaled
   }
 }
 
@@ -371,12 +377,26 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k2_up_mix(UpArgs a) {
     wrow[rb] = a.wu + ((int64_t)s * a.HS + c) * a.r;
   }
 
-  // decode-sized tiles: issue every weight load of the wave before waiting
+  // decode-sized tiles: issue every global load of the wave (weights and the
+  // epilogue's R2, rrms and Wnorm) before the first wait
   uint4 wall[RBW == 1 ? JMAX : 1];
+  float pr2[RBW == 1 ? NTB : 1][4], prr[RBW == 1 ? NTB : 1][4], pone[4];
   if constexpr (RBW == 1) {
 #pragma unroll
     for (int j = 0; j < JMAX; ++j)
       if (j < nj) wall[j] = ld16(wrow[0] + j * 32 + koff);
+    const int c = cbase + wave * 4 + (lane >> 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pone[q] = 1.0f + bf1(a.wn[a.wn_full ? q * a.HS + c : c]);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const int64_t m = m0 + tb * 16 + (lane & 15);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        pr2[tb][q] = m < a.M ? bf1(a.R2[m * a.K + q * a.HS + c]) : 0.0f;
+        prr[tb][q] = m < a.M ? a.rrms[m * 4 + q] : 0.0f;
+      }
+    }
   }
 
   const int cpr = a.r / 8;
@@ -426,6 +446,20 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k2_up_mix(UpArgs a) {
   }
 
   // epilogue: lane holds streams q = 0..3 of channel c for token m
+  if constexpr (RBW == 1) {
+    const int c = cbase + wave * 4 + (lane >> 4);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const int64_t m = m0 + tb * 16 + (lane & 15);
+      if (m < a.M) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum = fmaf(sigmoid_f(acc[0][tb][q]), pr2[tb][q] * prr[tb][q] * pone[q], sum);
+        a.x[m * a.HS + c] = to_bf(sum * 0.25f);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     const int c = cbase + (wave * RBW + rb) * 4 + (lane >> 4);
@@ -504,8 +538,8 @@ int launch_forward(const Shape& s, const Plan& p, const ForwardArgs& f, void* st
   r.NP = s.np(); r.kcps = p.kcps; r.HS = s.hs; r.HC = s.hc; r.r = s.r; r.n_rows = s.n_rows();
   r.eps = s.eps; r.inv_hc = 1.0f / (float)s.hc; r.inv_hs = 1.0f / (float)s.hs;
   r.rrms = f.rrms; r.h = H; r.inj_next = f.inj_next; r.ld_inj_next = f.ld_inj_next;
-  dim3 gr((unsigned)((p.mpad + 63) / 64), (unsigned)((s.n_rows() + 31) / 32));
-  hipLaunchKernelGGL(hcgr_k1_reduce, gr, dim3(256), 0, st, r);
+  const int64_t waves = (int64_t)s.n_rows() * (p.mpad / 16);
+  hipLaunchKernelGGL(hcgr_k1_reduce, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, r);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return (int)e;
 
   UpArgs u;

@@ -219,7 +219,7 @@ def test_workspace_reuse_across_sizes(H, op, weights):
     ws = torch.empty(H.hcgr_workspace_size(op.handle, 2048) + 4096, dtype=torch.uint8, device="cuda")
     ws.fill_(0xFF)  # NaN patterns everywhere
     res = {}
-    for M in (2048, 7, 300, 7, 33):
+    for M in (2048, 7, 300, 7, 33, 64, 16, 33):
         inp = synth.make_inputs(M, SHAPE, seed=10, device="cuda", weights=weights)
         out = op.alloc_outputs(M)
         op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"], out=out,
