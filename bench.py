@@ -53,26 +53,41 @@ def op_flops(M):
     return M * 2 * (R_LOW + HC) * K + M * 2 * R_LOW * K
 
 
-def kernel_bytes(name, M, merged=False):
-    """Algorithmic bytes per launch of each kernel (what it must move at least)."""
+def kernel_bytes(name, M, merged=False, plan=""):
+    """Algorithmic bytes per launch of each kernel: what it must read and write
+    at least, given what it receives and hands on (weights once per launch)."""
+    wdown = (R_LOW + HC) * K * 2 + (0 if merged else HS * 2)
+    act_in = K * 2 + HS * 2 + HC * 2          # R, y, inj
     if name == "hcgr_k1_down":
-        w = (R_LOW + HC) * K * 2 + (0 if merged else HS * 2)
-        return w + M * (K * 2 + HS * 2 + HC * 2 + K * 2)
+        return wdown + M * (act_in + K * 2)     # + R2 out
     if name == "hcgr_k1_reduce":
-        return M * (HC * 4 + HC * 2)
-    if name == "hcgr_k2_up_mix":
-        return K * R_LOW * 2 + HS * 2 + M * (K * 2 + HC * 4 + HS * 2)
+        return M * (HC * 4 + HC * 2)            # rrms, inj_next out
+    if name == "hcgr_k1_full":
+        out = K * 2 + HC * 4 + (HC * 2 if "plan=full" in plan else 0)
+        return wdown + M * (act_in + out)
+    if name == "hcgr_k1_sum":
+        return M * HC * 2                       # inj_next out
+    if name in ("hcgr_k2_up_mix", "hcgr_k2_tile"):
+        return K * R_LOW * 2 + HS * 2 + M * (K * 2 + HC * 4 + HS * 2)  # Wu, Wnorm; R2, rrms in; x out
     raise KeyError(name)
 
 
 def kernel_flops(name, M):
-    return {"hcgr_k1_down": M * 2 * (R_LOW + HC) * K, "hcgr_k1_reduce": 0,
-            "hcgr_k2_up_mix": M * 2 * R_LOW * K}[name]
+    if name in ("hcgr_k1_down", "hcgr_k1_full"):
+        return M * 2 * (R_LOW + HC) * K
+    if name in ("hcgr_k2_up_mix", "hcgr_k2_tile"):
+        return M * 2 * R_LOW * K
+    return 0
 
 
 def stage_names(plan: str):
-    """Kernels between the four timing marks of hcgr_forward_timed."""
-    return ("hcgr_k1_down", "hcgr_k1_reduce", "hcgr_k2_up_mix")
+    """Kernels between the four timing marks of hcgr_forward_timed (None where
+    a plan has no kernel between two marks)."""
+    if "plan=split" in plan:
+        return ("hcgr_k1_down", "hcgr_k1_reduce", "hcgr_k2_up_mix")
+    if "plan=stream" in plan:
+        return ("hcgr_k1_full", "hcgr_k1_sum", "hcgr_k2_tile")
+    return ("hcgr_k1_full", None, "hcgr_k2_tile")
 
 
 class Sets:
@@ -192,8 +207,8 @@ def time_graph(H, op, sets, replays, stream):
     return us
 
 
-def roofline_entry(name, M, us, merged):
-    b = kernel_bytes(name, M, merged)
+def roofline_entry(name, M, us, merged, plan):
+    b = kernel_bytes(name, M, merged, plan)
     gbs = b / (us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": name, "avg_us": round(us, 3),
@@ -304,7 +319,7 @@ def main():
             torch.cuda.empty_cache()
 
     dom = max(head["kernels_us"], key=lambda k: head["kernels_us"][k])
-    roof = roofline_entry(dom, M, head["kernels_us"][dom], merged)
+    roof = roofline_entry(dom, M, head["kernels_us"][dom], merged, head["plan"])
     line = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["us_per_call"] / 1e3, 6),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

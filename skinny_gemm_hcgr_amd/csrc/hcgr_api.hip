@@ -183,16 +183,25 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
   if (len) {
     if (M == 0) {
       snprintf(buf, len, "M=0: no launch");
-    } else {
+    } else if (p.kind == hcgr::PLAN_SPLIT) {
       hcgr::K1Shape a = hcgr::k1_shape(p.k1);
       hcgr::K2Shape b = hcgr::k2_shape(p.k2);
       snprintf(buf, len,
-               "M=%lld mpad=%lld | k1 tm=%d waves=%d blocks/wave=%d stage_k=%d k_chunk=%d chunks=%d n_tiles=%d "
-               "grid=%dx%lld | reduce waves=%lld | k2 tm=%d waves=%d rowblocks/wave=%d channels=%d grid=%dx%lld | "
+               "M=%lld plan=split mpad=%lld | k1_down tm=%d waves=%d stage_k=%d k_chunk=%d chunks=%d n_tiles=%d "
+               "grid=%dx%lld | k1_reduce waves=%lld | k2_up_mix tm=%d waves=%d channels=%d grid=%dx%lld | "
                "workspace=%zu",
-               (long long)M, (long long)p.mpad, a.tm, a.nw, a.nbw, a.ks, p.kc, p.nkc, p.ntiles_n,
-               p.ntiles_n * p.nkc, (long long)(p.mpad / p.tm), (long long)(s.n_rows() * (p.mpad / 16)), b.tm, b.nw, b.rbw, p.cb, s.hs / p.cb, (long long)(p.mpad / p.tm),
-               p.ws_bytes);
+               (long long)M, (long long)p.mpad, a.tm, a.nw, a.ks, p.kc, p.nkc, p.ntiles_n, p.ntiles_n * p.nkc,
+               (long long)(p.mpad / p.tm), (long long)(s.n_rows() * (p.mpad / 16)), b.tm, b.nw, p.cb,
+               s.hs / p.cb, (long long)(p.mpad / p.tm), p.ws_bytes);
+    } else {
+      hcgr::KFShape f = hcgr::kf_shape(p.kf);
+      hcgr::KTShape t = hcgr::kt_shape(p.kt);
+      snprintf(buf, len,
+               "M=%lld plan=%s | k1_full tm=%d waves=%d stage_k=%d streams/wg=%d row_splits=%d grid=%lldx%d%s | "
+               "k2_tile tm=%d channels=%d grid=%dx%lld | workspace=%zu",
+               (long long)M, p.kind == hcgr::PLAN_FULL ? "full" : "stream", f.tm, f.nw, f.ks, p.spw, p.nsplit,
+               (long long)hcgr::cdiv(M, f.tm), p.nsplit * (4 / p.spw), p.kind == hcgr::PLAN_STREAM ? " | k1_sum" : "",
+               t.tm, t.cb, s.hs / t.cb, (long long)hcgr::cdiv(M, t.tm), p.ws_bytes);
     }
   }
   return ok();

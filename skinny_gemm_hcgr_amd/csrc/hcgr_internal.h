@@ -1,24 +1,33 @@
 // hcgr_internal.h -- plan and kernel-launch interface shared by the C ABI
 // (hcgr_api.hip) and the kernels (hcgr_kernels.hip). Not installed.
 //
-// The op is split into three launches, all on the caller's stream:
-//   K1  hcgr_k1_down    COMBINE + the per-stream sums of squares of (N) + the
-//                       down/inject contraction (G1, INJ) on bf16 MFMA tiles.
-//                       Because rrms is a per-stream scalar and k is
-//                       stream-major, xn . W^T = sum_s rrms[s] * P_s with
-//                       P_s = sum_{c in stream s} R2*(1+Wnorm)*W: each
-//                       workgroup contracts one K chunk that lies inside one
-//                       stream and stores the unscaled partial P and the
-//                       chunk's sum of squares; no workgroup has to wait for
-//                       the whole row's RMS.
-//   K1r hcgr_k1_reduce  sums the chunk partials of each stream, forms rrms,
-//                       scales and adds the streams, applies SiLU(./HC) for
-//                       the down rows (-> h, bf16, workspace) and writes
-//                       inj_next for the inject rows.
-//   K2  hcgr_k2_up_mix  gate = h . Wu^T on MFMA tiles whose 16 rows are 4
-//                       channels x 4 streams, so the sigmoid and the gated
-//                       mean over streams (MIX) happen in registers; xn is
-//                       rebuilt from the bf16 R2 and rrms; writes x.
+// Identity used by every down/inject kernel: rrms is a per-stream scalar and
+// k is stream-major, so  xn . W^T = sum_s rrms[s] * P_s  with
+// P_s = sum_{c in stream s} R2[s,c]*(1+Wnorm) * W[., s*HS+c]. A workgroup can
+// contract a stretch of one stream before that stream's RMS is known and
+// scale the partial once the stream's sum of squares is complete.
+//
+// Three plans, chosen by the token count M (make_plan):
+//   SPLIT  (decode sizes). Weight streaming over every CU:
+//     K1  hcgr_k1_down    COMBINE + sums of squares + unscaled partials P for a
+//                         (token tile, K chunk inside one stream, row tile)
+//     K1r hcgr_k1_reduce  sums the chunk partials per stream, forms rrms,
+//                         scales, SiLU(./HC) -> h (workspace), inj_next
+//     K2  hcgr_k2_up_mix  up contraction on MFMA tiles whose 16 rows are
+//                         4 channels x 4 streams; sigmoid + MIX in registers
+//   STREAM (mid sizes) and FULL (large sizes). Activation streaming:
+//     K1  hcgr_k1_full    a workgroup owns a token tile and every down/inject
+//                         row (or a row split) and runs over one stream
+//                         (STREAM) or all four (FULL) with two accumulator
+//                         sets: the current stream's partial and the
+//                         rrms-scaled total. FULL writes h and inj_next
+//                         directly; STREAM writes rrms_s * P_s per stream
+//     K1s hcgr_k1_sum     (STREAM only) sums the four scaled partials,
+//                         SiLU(./HC) -> h, inj_next
+//     K2  hcgr_k2_tile    h . Wu^T on MFMA with h and Wu staged through LDS,
+//                         the R2 tile prefetched into LDS by direct
+//                         global->LDS loads during the contraction, and the
+//                         sigmoid + MIX epilogue in registers
 #pragma once
 
 #include <stddef.h>
@@ -26,24 +35,42 @@
 
 namespace hcgr {
 
-// Kernel variants compiled into the library (template instantiations).
-enum K1Variant { K1_T16 = 0, K1_T32 = 1, K1_T64S = 2, K1_T64L = 3, K1_NVAR };
-enum K2Variant { K2_T16 = 0, K2_T32 = 1, K2_T64S = 2, K2_T64L = 3, K2_NVAR };
+enum PlanKind { PLAN_SPLIT = 0, PLAN_STREAM = 1, PLAN_FULL = 2 };
+
+// SPLIT-plan kernel variants (template instantiations).
+enum K1Variant { K1_T16 = 0, K1_T32 = 1, K1_T64S = 2, K1_NVAR };
+enum K2Variant { K2_T16 = 0, K2_T32 = 1, K2_T64S = 2, K2_NVAR };
 
 struct K1Shape { int tm, nw, nbw, ks; };
 struct K2Shape { int tm, nw, rbw; };
 
 inline K1Shape k1_shape(int v) {
-  static const K1Shape t[K1_NVAR] = {{16, 7, 1, 128}, {32, 7, 1, 128}, {64, 7, 1, 128}, {64, 4, 6, 32}};
+  static const K1Shape t[K1_NVAR] = {{16, 7, 1, 128}, {32, 7, 1, 128}, {64, 7, 1, 128}};
   return t[v];
 }
 inline K2Shape k2_shape(int v) {
-  static const K2Shape t[K2_NVAR] = {{16, 4, 1}, {32, 4, 1}, {64, 4, 1}, {64, 4, 4}};
+  static const K2Shape t[K2_NVAR] = {{16, 4, 1}, {32, 4, 1}, {64, 4, 1}};
   return t[v];
 }
 // Chunks per stream handled by one lane group of the reduction kernel: the
 // split plans keep chunks-per-stream <= 4 * kRedPerLane.
 constexpr int kRedPerLane = 8;
+
+// STREAM/FULL down kernel variants: token tile, waves, row blocks per wave,
+// k per LDS stage. 8 waves x 3 blocks cover 24 16-row blocks per workgroup.
+enum KFVariant { KF_T32 = 0, KF_T64 = 1, KF_NVAR };
+struct KFShape { int tm, nw, bpw, ks; };
+inline KFShape kf_shape(int v) {
+  static const KFShape t[KF_NVAR] = {{32, 8, 3, 128}, {64, 8, 3, 64}};
+  return t[v];
+}
+// Tiled up kernel variants: token tile, channel tile (x 4 streams).
+enum KTVariant { KT_T64 = 0, KT_NVAR };
+struct KTShape { int tm, cb; };
+inline KTShape kt_shape(int v) {
+  static const KTShape t[KT_NVAR] = {{64, 64}};
+  return t[v];
+}
 
 struct Shape {
   int hc, hs, r;
@@ -59,15 +86,26 @@ struct Shape {
 
 struct Plan {
   int64_t M = 0, mpad = 0;
+  int kind = PLAN_SPLIT;
+  // SPLIT
   int tm = 0;
   int k1 = 0, k2 = 0;
   int kc = 0, nkc = 0, kcps = 0;   // k per chunk, chunk count, chunks per stream
-  int ntiles_n = 0;                // K1 n tiles (split plan)
+  int ntiles_n = 0;                // K1 n tiles
   int cb = 0;                      // K2 channels per workgroup
-  size_t off_p = 0, off_ss = 0, off_h = 0, ws_bytes = 0;
+  // STREAM / FULL
+  int kf = 0, kt = 0;              // variants
+  int spw = 4;                     // streams per down workgroup (4 or 1)
+  int nsplit = 1;                  // row-block splits of the down rows
+  int64_t mq = 0;                  // rows of the per-stream partials (STREAM)
+  size_t off_p = 0, off_ss = 0, off_h = 0, off_q = 0, ws_bytes = 0;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Largest M served by the SPLIT plan.
+constexpr int64_t kSplitMaxM = 64;
 
 // Pure host planning: tile sizes and split counts by token count M.
 inline Plan make_plan(const Shape& s, int64_t M) {
@@ -75,43 +113,69 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   p.M = M;
   if (M <= 0) return p;
   const int hs = s.hs;
-  // split plan: partial sums per K chunk, separate reduction kernel (K1 + K1r + K2)
-  int kc;
-  if (M <= 16) { p.k1 = K1_T16; p.k2 = K2_T16; kc = 128; }
-  else if (M <= 32) { p.k1 = K1_T32; p.k2 = K2_T32; kc = 128; }
-  else if (M <= 64) { p.k1 = K1_T64S; p.k2 = K2_T64S; kc = 128; }
-  else if (M <= 128) { p.k1 = K1_T64S; p.k2 = K2_T64S; kc = 256; }
-  else if (M <= 1024) { p.k1 = K1_T64S; p.k2 = K2_T64L; kc = 640; }
-  else {
-    p.k1 = K1_T64L; p.k2 = K2_T64L;
-    int64_t mt = (M + 63) / 64;
-    kc = mt >= 128 ? hs : (mt >= 64 ? hs / 2 : hs / 4);
+  const size_t np = (size_t)s.np();
+  if (M <= kSplitMaxM) {
+    p.kind = PLAN_SPLIT;
+    int kc;
+    if (M <= 16) { p.k1 = K1_T16; p.k2 = K2_T16; kc = 128; }
+    else if (M <= 32) { p.k1 = K1_T32; p.k2 = K2_T32; kc = 128; }
+    else { p.k1 = K1_T64S; p.k2 = K2_T64S; kc = 128; }
+    const K1Shape a = k1_shape(p.k1);
+    const K2Shape b = k2_shape(p.k2);
+    // the chunk must divide the stream width and hold whole LDS stages, and a
+    // stream may have at most 4 * kRedPerLane chunks (hs itself always fits)
+    auto valid = [&](int c) { return c >= a.ks && c % a.ks == 0 && hs % c == 0; };
+    while (kc > a.ks && !valid(kc)) kc -= a.ks;
+    if (!valid(kc)) kc = a.ks;
+    while (hs / kc > 4 * kRedPerLane) {
+      int c = kc + a.ks;
+      while (!valid(c)) c += a.ks;
+      kc = c;
+    }
+    p.tm = a.tm;  // K1 and K2 share the token tile of a plan
+    p.kc = kc;
+    p.kcps = hs / kc;
+    p.nkc = s.hc * p.kcps;
+    int per_tile = a.nw * a.nbw;
+    p.ntiles_n = (s.nblk() + per_tile - 1) / per_tile;
+    p.cb = b.nw * b.rbw * 4;
+    p.mpad = (M + p.tm - 1) / p.tm * p.tm;
+    p.off_p = 0;
+    p.off_ss = align256(p.off_p + (size_t)p.nkc * np * (size_t)p.mpad * sizeof(float));
+    p.off_h = align256(p.off_ss + (size_t)p.nkc * (size_t)p.mpad * sizeof(float));
+    p.ws_bytes = align256(p.off_h + (size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
+    return p;
   }
-  const K1Shape a = k1_shape(p.k1);
-  const K2Shape b = k2_shape(p.k2);
-  // the chunk must divide the stream width and hold whole LDS stages, and a
-  // stream may have at most 4 * kRedPerLane chunks (hs itself always fits)
-  auto valid = [&](int c) { return c >= a.ks && c % a.ks == 0 && hs % c == 0; };
-  while (kc > a.ks && !valid(kc)) kc -= a.ks;
-  if (!valid(kc)) kc = a.ks;
-  while (hs / kc > 4 * kRedPerLane) {
-    int c = kc + a.ks;
-    while (!valid(c)) c += a.ks;
-    kc = c;
+  // STREAM / FULL: aim for at least one down workgroup per CU (256 CUs)
+  const int64_t target = 256;
+  const KFShape f64 = kf_shape(KF_T64);
+  const int nmin = (int)cdiv(s.nblk(), (int64_t)f64.nw * f64.bpw);  // row splits the blocks need
+  if (cdiv(M, 64) * nmin >= target) {
+    p.kind = PLAN_FULL; p.kf = KF_T64; p.spw = 4; p.nsplit = nmin;
+  } else if (cdiv(M, 32) * nmin >= target) {
+    p.kind = PLAN_FULL; p.kf = KF_T32; p.spw = 4; p.nsplit = nmin;
+  } else if (cdiv(M, 32) * 2 * nmin >= target) {
+    p.kind = PLAN_FULL; p.kf = KF_T32; p.spw = 4; p.nsplit = 2 * nmin;
+  } else if ((hs / kf_shape(KF_T32).ks) % 2 == 0) {
+    // one stream per workgroup (the down kernel runs its stages in pairs,
+    // so a stream must hold an even number of them)
+    p.kind = PLAN_STREAM; p.kf = KF_T32; p.spw = 1;
+    p.nsplit = nmin;
+    while (cdiv(M, 32) * 4 * p.nsplit < target && p.nsplit * 2 <= s.nblk()) p.nsplit *= 2;
+  } else {
+    p.kind = PLAN_FULL; p.kf = KF_T32; p.spw = 4;
+    p.nsplit = nmin;
+    while (cdiv(M, 32) * p.nsplit < target && p.nsplit * 2 <= s.nblk()) p.nsplit *= 2;
   }
-  p.tm = a.tm;  // K1 and K2 share the token tile of a plan
-  p.kc = kc;
-  p.kcps = hs / kc;
-  p.nkc = s.hc * p.kcps;
-  int per_tile = a.nw * a.nbw;
-  p.ntiles_n = (s.nblk() + per_tile - 1) / per_tile;
-  p.cb = b.nw * b.rbw * 4;
-  p.mpad = (M + p.tm - 1) / p.tm * p.tm;
-  size_t np = (size_t)s.np();
-  p.off_p = 0;
-  p.off_ss = align256(p.off_p + (size_t)p.nkc * np * (size_t)p.mpad * sizeof(float));
-  p.off_h = align256(p.off_ss + (size_t)p.nkc * (size_t)p.mpad * sizeof(float));
-  p.ws_bytes = align256(p.off_h + (size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
+  p.kt = KT_T64;
+  const int tm1 = kf_shape(p.kf).tm, tm2 = kt_shape(p.kt).tm;
+  p.tm = tm1;
+  p.mpad = cdiv(M, tm2) * tm2;  // h rows the up kernel may read
+  p.mq = cdiv(M, tm1) * tm1;
+  p.off_h = 0;
+  p.off_q = align256((size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
+  p.ws_bytes = p.off_q;
+  if (p.kind == PLAN_STREAM) p.ws_bytes = align256(p.off_q + (size_t)s.hc * (size_t)p.mq * np * sizeof(float));
   return p;
 }
 
@@ -123,13 +187,13 @@ struct ForwardArgs {
   void* ws;
 };
 
-// Raises the dynamic-LDS limit of the up kernels on the current device (the
-// h tile of a 64-token tile takes up to 66.5 KB at r = 512).
+// Raises the dynamic-LDS limit of the up kernels on the current device.
 int configure_kernels();
 
-// Enqueues K1, K1r and K2 on `stream`; returns the hipError_t of the launches.
-// With `events` (4 hipEvent_t) it records events[0] before K1 and events[i]
-// after the i-th kernel.
+// Enqueues the plan's kernels on `stream`; returns the hipError_t of the
+// launches. With `events` (4 hipEvent_t) it records events[0] before the
+// first kernel and events[i] after the i-th stage (a plan with two kernels
+// records events[2] and events[3] back to back).
 int launch_forward(const Shape& s, const Plan& p, const ForwardArgs& a, void* stream, void* const* events);
 
 }  // namespace hcgr

@@ -11,6 +11,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <functional>
+#include <type_traits>
+
 #include "hcgr_internal.h"
 
 namespace hcgr {
@@ -36,8 +39,35 @@ __device__ __forceinline__ bf16x8_t as_bf8(uint4 v) { return __builtin_bit_cast(
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
 }
-// logistic function through the hardware 2^x: 1/(1 + 2^(-v*log2 e))
-__device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + __expf(-v)); }
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+// Buffer resource over [base, base + bytes): loads past the range return 0
+// and stores past it are dropped. Word 3 (0x00020000) is the 32-bit data
+// format that gfx9-family raw buffer descriptors use.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void bst16(rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, 0);
+}
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 bld8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void bst8(rsrc_t r, uint32_t off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, (int)off, 0, 0);
+}
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations, then s_barrier. Unlike __syncthreads it does not wait for
+// outstanding global->LDS loads, which may stay in flight across it (their
+// target is read only after an explicit full wait).
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// logistic function through the hardware 2^x and reciprocal: 1/(1 + 2^(-v*log2 e))
+__device__ __forceinline__ float sigmoid_f(float v) { return __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // ---------------------------------------------------------------------------
 // K1: COMBINE + sums of squares + down/inject partial contraction.
@@ -484,6 +514,539 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k2_up_mix(UpArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// hcgr_k1_full: COMBINE + N + down/inject contraction for a token tile over
+// whole streams (STREAM and FULL plans).
+// Workgroup = (token tile of TM rows) x (row split: 16-row blocks [b0, b1) of
+// the down/inject rows) x (stream group: streams [s_first, s_first + spw)).
+// The loop runs stream-major over LDS stages of KS columns. Per stage every
+// thread combines one 16-byte chunk of R/y (two stages of raw loads in
+// flight in registers), stores its R2 chunk (row split 0 only) and the bf16
+// activation R2*(1+Wnorm) (or R2 for folded weights) into a double-buffered
+// LDS tile; each wave then runs its row blocks over the tile with
+// v_mfma_f32_16x16x32_bf16 (A = weight rows from global, one stage ahead;
+// B = activation from LDS). At each stream end the stream's sum of squares
+// gives rrms and the stream accumulator is folded into the total with it.
+// Every global access in the loop is an unconditional buffer access through
+// a range-limited descriptor (rows past M read as zero, stores past the
+// range are dropped), so the loop has no branch around a memory operation
+// and the compiler can keep several stages of loads in flight.
+// ---------------------------------------------------------------------------
+struct FullArgs {
+  const uint16_t* R;
+  const uint16_t* y;
+  const uint16_t* inj;
+  int64_t ld_inj;
+  const uint16_t* wn;
+  int wn_len;
+  const uint16_t* w0;  // Wd [r,K] or merged Wm [n_pad,K]
+  const uint16_t* w1;  // Wi [HC,K], or nullptr when the inject rows are rows r.. of w0
+  int folded;
+  int64_t M;
+  int K, HS, HC, r, n_rows, nblk;
+  int nsplit, spw;
+  float eps, inv_hc, inv_hs;
+  uint16_t* R2;
+  float* rrms;
+  uint16_t* h;  // [Mpad, r] (FULL)
+  uint16_t* inj_next;
+  int64_t ld_inj_next;
+  float* Q;  // [HC][Mq][NP] rrms-scaled per-stream partials (STREAM)
+  int64_t Mq;
+  int NP;
+};
+
+template <int B>
+using ic = std::integral_constant<int, B>;
+
+template <int TM, int NW, int BPW, int KS>
+__global__ __launch_bounds__(NW * 64) void hcgr_k1_full(FullArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int CPR = KS / 8;  // 16-byte chunks per token row of a stage
+  constexpr int NCH = TM * CPR;
+  static_assert(NCH % NT == 0, "whole chunks per thread");
+  constexpr int CPT = NCH / NT;
+  static_assert(64 % CPR == 0, "a token's chunks lie inside one wave");
+  constexpr int LDA = KS + 8;  // padded LDS row, bf16 elements
+  constexpr int NTB = TM / 16;
+  constexpr int NKS = KS / 32;
+
+  __shared__ __attribute__((aligned(16))) uint16_t act[2][TM * LDA];
+  __shared__ float iwh[4][TM], iwl[4][TM], rrs[4][TM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
+  const int64_t m0 = (int64_t)blockIdx.x * TM;
+  const int rows = (int)min((int64_t)TM, a.M - m0);  // valid token rows of the tile
+  const int ngroups = 4 / a.spw;
+  const int split = blockIdx.y / ngroups;
+  const int s_first = (int)(blockIdx.y % ngroups) * a.spw;
+  const int b0 = split * a.nblk / a.nsplit;
+  const int b1 = (split + 1) * a.nblk / a.nsplit;
+  const bool lead = split == 0;
+  const int spp = a.HS / KS;  // stages per stream
+  const int nst = a.spw * spp;
+  const int koff = 8 * (lane >> 4);
+  const uint32_t rowb = (uint32_t)a.K * 2u;  // bytes per R/R2 row
+
+  // range-limited descriptors (scalar)
+  const rsrc_t rR = make_rsrc(a.R + m0 * a.K, (uint32_t)rows * rowb);
+  const rsrc_t rY = make_rsrc(a.y + m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
+  const rsrc_t rWn = make_rsrc(a.wn, a.folded ? 0u : (uint32_t)a.wn_len * 2u);  // folded: reads 0 -> factor 1
+  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, lead ? (uint32_t)rows * rowb : 0u);
+  const rsrc_t rW0 = make_rsrc(a.w0, (uint32_t)(a.w1 ? a.r : a.n_rows) * rowb);
+  const rsrc_t rW1 = make_rsrc(a.w1 ? a.w1 : a.w0, a.w1 ? (uint32_t)a.HC * rowb : 0u);
+
+  // (COMBINE) iw = 2*sigmoid(inj/HC), formed in fp64 and kept as fp32 hi + lo
+  // so that R2 = (R + y*hi) + y*lo stays within an ulp of R2 under cancellation
+  for (int i = tid; i < 4 * TM; i += NT) {
+    const int s = i / TM, t = i % TM;
+    const int64_t m = m0 + t;
+    double v = 0.0;
+    if (t < rows) v = 2.0 / (1.0 + exp(-(double)bf1(a.inj[m * a.ld_inj + s]) / (double)a.HC));
+    const float hi = (float)v;
+    iwh[s][t] = hi;
+    iwl[s][t] = (float)(v - (double)hi);
+  }
+
+  // weight rows of this wave: block nb covers rows nb*16.., each either all
+  // down rows (< r) or all inject/pad rows, so the descriptor is wave-uniform
+  rsrc_t wrs[BPW];
+  uint32_t wofs[BPW];
+  bool bval[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int nb = b0 + wave + NW * i;
+    bval[i] = nb < b1;
+    const int n = nb * 16 + (lane & 15);
+    const bool down = nb * 16 < a.r || !a.w1;
+    wrs[i] = down ? rW0 : rW1;
+    wofs[i] = (uint32_t)(down ? n : n - a.r) * rowb;
+  }
+  auto kbase = [&](int st) { return (s_first + st / spp) * a.HS + (st % spp) * KS; };
+
+  uint4 wf[BPW][NKS];
+  auto load_w = [&](int st, int ks) {
+    const uint32_t k2 = (uint32_t)(kbase(st) + ks * 32 + koff) * 2u;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) wf[i][ks] = bld16(wrs[i], wofs[i] + k2);
+  };
+
+  uint4 rv[2][CPT], yv[2][CPT], wv[2][CPT];
+  auto load_raw = [&](auto BUF, int st) {
+    constexpr int b = decltype(BUF)::value;
+    const int s = s_first + st / spp;
+    const int c0 = (st % spp) * KS;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int q = tid + j * NT;
+      const uint32_t t = q / CPR;
+      const uint32_t col = (q % CPR) * 8;
+      rv[b][j] = bld16(rR, t * rowb + (uint32_t)(s * a.HS + c0 + col) * 2u);
+      yv[b][j] = bld16(rY, (t * (uint32_t)a.HS + c0 + col) * 2u);
+      wv[b][j] = bld16(rWn, ((a.wn_len == a.HS ? 0u : (uint32_t)(s * a.HS)) + c0 + col) * 2u);
+    }
+  };
+
+  float ss[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) ss[j] = 0.0f;
+
+  // (COMBINE) R2 = R + y*iw in fp32; sum of squares; R2 -> bf16 output;
+  // activation R2*(1+Wnorm) -> LDS (Wnorm reads as 0 for folded weights)
+  auto combine = [&](auto BUF, int st) {
+    constexpr int b = decltype(BUF)::value;
+    const int s = s_first + st / spp;
+    const int c0 = (st % spp) * KS;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int q = tid + j * NT;
+      const int t = q / CPR;
+      const int col = (q % CPR) * 8;
+      const float ih = iwh[s][t];
+      const float il = iwl[s][t];
+      const uint32_t rw[4] = {rv[b][j].x, rv[b][j].y, rv[b][j].z, rv[b][j].w};
+      const uint32_t yw[4] = {yv[b][j].x, yv[b][j].y, yv[b][j].z, yv[b][j].w};
+      const uint32_t ww[4] = {wv[b][j].x, wv[b][j].y, wv[b][j].z, wv[b][j].w};
+      uint32_t o2[4], ou[4];
+      float acc = ss[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float r0 = fmaf(bf_lo(yw[e]), il, fmaf(bf_lo(yw[e]), ih, bf_lo(rw[e])));
+        const float r1 = fmaf(bf_hi(yw[e]), il, fmaf(bf_hi(yw[e]), ih, bf_hi(rw[e])));
+        acc = fmaf(r0, r0, acc);
+        acc = fmaf(r1, r1, acc);
+        o2[e] = pack_bf2(r0, r1);
+        ou[e] = pack_bf2(r0 * (1.0f + bf_lo(ww[e])), r1 * (1.0f + bf_hi(ww[e])));
+      }
+      ss[j] = acc;
+      bst16(rR2, (uint32_t)t * rowb + (uint32_t)(s * a.HS + c0 + col) * 2u, make_uint4(o2[0], o2[1], o2[2], o2[3]));
+      st16(&act[b][t * LDA + col], make_uint4(ou[0], ou[1], ou[2], ou[3]));
+    }
+  };
+
+  f32x4_t acc_t[BPW][NTB], acc_s[BPW][NTB];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i)
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) acc_t[i][tb] = acc_s[i][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto contract = [&](auto BUF, int st) {
+    constexpr int b = decltype(BUF)::value;
+    const uint16_t* buf = act[b];
+    const int stn = min(st + 1, nst - 1);  // the last stage reloads itself: no branch around a load
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 bfr[NTB];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+        bfr[tb] = *reinterpret_cast<const uint4*>(buf + (tb * 16 + (lane & 15)) * LDA + ks * 32 + koff);
+#pragma unroll
+      for (int i = 0; i < BPW; ++i)
+        if (bval[i]) {
+#pragma unroll
+          for (int tb = 0; tb < NTB; ++tb) acc_s[i][tb] = mfma16(wf[i][ks], bfr[tb], acc_s[i][tb]);
+        }
+      load_w(stn, ks);
+    }
+  };
+
+  // (N) stream end: rrms from the stream's sum of squares; fold the stream
+  // accumulator into the total
+  auto stream_end = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      float v = ss[j];
+#pragma unroll
+      for (int o = 1; o < CPR; o <<= 1) v += __shfl_xor(v, o, 64);
+      ss[j] = 0.0f;
+      const int q = tid + j * NT;
+      if ((tid % CPR) == 0) rrs[s][q / CPR] = 1.0f / sqrtf(v * a.inv_hs + a.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const float rr = rrs[s][tb * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc_t[i][tb][q] = fmaf(rr, acc_s[i][tb][q], acc_t[i][tb][q]);
+        acc_s[i][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+  };
+
+  auto step = [&](auto BUF, int st) {
+    combine(BUF, st);
+    load_raw(BUF, min(st + 2, nst - 1));
+    __syncthreads();
+    contract(BUF, st);
+    if ((st + 1) % spp == 0) stream_end(s_first + st / spp);
+  };
+
+  // nst is even (the plan guarantees it), so the loop runs whole pairs
+  load_raw(ic<0>{}, 0);
+  load_raw(ic<1>{}, 1);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) load_w(0, ks);
+  __syncthreads();  // iwh/iwl
+  for (int st = 0; st < nst; st += 2) {
+    step(ic<0>{}, st);
+    step(ic<1>{}, st + 1);
+  }
+
+  // outputs: rrms of this workgroup's streams; lane holds rows n0..n0+3 of
+  // token m for each of its blocks and token blocks
+  if (lead)
+    for (int i = tid; i < a.spw * TM; i += NT) {
+      const int s = s_first + i / TM, t = i % TM;
+      if (t < rows) a.rrms[(m0 + t) * 4 + s] = rrs[s][t];
+    }
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    if (!bval[i]) continue;
+    const int n0 = (b0 + wave + NW * i) * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const int t = tb * 16 + (lane & 15);
+      if (t >= rows) continue;
+      const int64_t m = m0 + t;
+      const f32x4_t v = acc_t[i][tb];
+      if (a.spw == 1) {
+        if (n0 < a.n_rows)
+          *reinterpret_cast<f32x4_t*>(a.Q + ((int64_t)s_first * a.Mq + m) * a.NP + n0) = v;
+      } else if (n0 < a.r) {
+        float z[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) z[q] = v[q] * a.inv_hc;
+        uint2 o;
+        o.x = pack_bf2(z[0] * sigmoid_f(z[0]), z[1] * sigmoid_f(z[1]));  // (G1) SiLU(lora / HC)
+        o.y = pack_bf2(z[2] * sigmoid_f(z[2]), z[3] * sigmoid_f(z[3]));
+        *reinterpret_cast<uint2*>(a.h + m * a.r + n0) = o;
+      } else if (n0 < a.n_rows) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (n0 + q < a.n_rows) a.inj_next[m * a.ld_inj_next + (n0 - a.r + q)] = to_bf(v[q]);  // (INJ)
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// hcgr_k1_sum (STREAM plan): v = sum_s rrms_s P_s for each token and row;
+// down rows -> h = SiLU(v/HC) (bf16), inject rows -> inj_next. One thread per
+// (token, 8 consecutive rows).
+// ---------------------------------------------------------------------------
+struct SumArgs {
+  const float* Q;
+  int64_t Mq, M;
+  int NP, r, n_rows;
+  float inv_hc;
+  uint16_t* h;
+  uint16_t* inj_next;
+  int64_t ld_inj_next;
+};
+
+__global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
+  const int nch = a.r / 8 + 1;  // r/8 chunks of h, then the chunk holding the inject rows
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t m = idx / nch;
+  const int c = (int)(idx % nch);
+  if (m >= a.M) return;
+  const int n = c * 8;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const float* p = a.Q + ((int64_t)s * a.Mq + m) * a.NP + n;
+    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(p);
+    const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] += lo[e];
+      v[e + 4] += hi[e];
+    }
+  }
+  if (n < a.r) {
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float z0 = v[2 * e] * a.inv_hc, z1 = v[2 * e + 1] * a.inv_hc;
+      o[e] = pack_bf2(z0 * sigmoid_f(z0), z1 * sigmoid_f(z1));  // (G1) SiLU(lora / HC)
+    }
+    st16(a.h + m * a.r + n, make_uint4(o[0], o[1], o[2], o[3]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < a.n_rows) a.inj_next[m * a.ld_inj_next + e] = to_bf(v[e]);  // (INJ)
+  }
+}
+
+// ---------------------------------------------------------------------------
+// hcgr_k2_tile: (G2) + (MIX) for a tile of 64 tokens x 64 channels (x 4
+// streams), 4 waves; wave (wt, wc) owns tokens wt*32.. and channels wc*32..
+// for all 4 streams. MFMA: A = Wu rows (channels), B = h^T (tokens), both
+// staged per 32-wide k step through double-buffered LDS (50 KB per
+// workgroup, so three workgroups share a CU and one's epilogue overlaps
+// another's contraction). Lane l ends with channels 4*(l/16)..+3 of token
+// l%16 of each (token block, channel block, stream), so the MIX sum over
+// streams is lane-local and each lane moves 8 contiguous bytes of R2 and x.
+// R2 and rrms of the lane are loaded into registers two k steps before the
+// end. All global accesses are unconditional buffer accesses whose
+// descriptors end at row M (loads past it read 0, stores past it are
+// dropped).
+// ---------------------------------------------------------------------------
+struct TileArgs {
+  const uint16_t* h;
+  int64_t M;
+  int r, HS, K;
+  const uint16_t* wu;
+  const uint16_t* R2;
+  const float* rrms;
+  const uint16_t* wn;
+  int wn_len;
+  uint16_t* x;
+};
+
+// x = 1/4 sum_s xn_s sigmoid(g_s) with one reciprocal: d_s = 1 + e^(-g_s),
+// sum_s xn_s / d_s = N / D, D = d0 d1 d2 d3, N = (xn0 d1 + xn1 d0) d2 d3 +
+// (xn2 d3 + xn3 d2) d0 d1. g is clamped below at -20 so that D stays finite
+// (d <= 4.9e8, D <= 5.7e34); sigmoid(-20) = 2.1e-9 bounds the change.
+__device__ __forceinline__ float mix4(const float g[4], const float xn[4]) {
+  float d[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) d[s] = 1.0f + __expf(-fmaxf(g[s], -20.0f));
+  const float d01 = d[0] * d[1], d23 = d[2] * d[3];
+  const float n01 = fmaf(xn[0], d[1], xn[1] * d[0]);
+  const float n23 = fmaf(xn[2], d[3], xn[3] * d[2]);
+  return 0.25f * fmaf(n01, d23, n23 * d01) * __builtin_amdgcn_rcpf(d01 * d23);
+}
+
+template <int TM, int CB>
+struct TileLds {
+  static constexpr int LDK = 40;                // padded k row (32 + 8), bf16 elements
+  static constexpr int H_ELEMS = TM * LDK;      // one h stage
+  static constexpr int W_ELEMS = 4 * CB * LDK;  // one Wu stage
+};
+
+template <int TM, int CB>
+__global__ __launch_bounds__(256) void hcgr_k2_tile(TileArgs a) {
+  using L = TileLds<TM, CB>;
+  constexpr int LDK = L::LDK;
+  constexpr int NT = TM / 32;   // token blocks per wave
+  constexpr int NJ = CB / 32;   // channel blocks per wave
+  constexpr int HPT = TM * 4 / 256, WPT = 4 * CB * 4 / 256;
+  static_assert(HPT >= 1 && (TM * 4) % 256 == 0 && (4 * CB * 4) % 256 == 0, "whole chunks per thread");
+
+  __shared__ __attribute__((aligned(16))) uint16_t hs[2][L::H_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][L::W_ELEMS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave & 1, wc = wave >> 1;
+  const int c0 = blockIdx.x * CB;
+  const int64_t m0 = (int64_t)blockIdx.y * TM;
+  const int rows = (int)min((int64_t)TM, a.M - m0);
+  const int koff = 8 * (lane >> 4);
+  const int nk = a.r / 32;
+  const uint32_t rowb = (uint32_t)a.K * 2u;
+  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, (uint32_t)rows * rowb);
+  const rsrc_t rX = make_rsrc(a.x + m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
+  const rsrc_t rRr = make_rsrc(a.rrms + m0 * 4, (uint32_t)rows * 16u);
+
+  // lane coordinates: channel cl..cl+3 of block j, token tl of block tb
+  const int tl = wt * (TM / 2) + (lane & 15);             // + tb*16
+  const int cl = wc * (CB / 2) + 4 * (lane >> 4);         // + j*16
+  // (1 + Wnorm) of the lane's channels
+  float onep[NJ][4][4];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint2 w = *reinterpret_cast<const uint2*>(a.wn + (a.wn_len == a.HS ? 0 : s * a.HS) + c0 + cl + j * 16);
+      onep[j][s][0] = 1.0f + bf_lo(w.x);
+      onep[j][s][1] = 1.0f + bf_hi(w.x);
+      onep[j][s][2] = 1.0f + bf_lo(w.y);
+      onep[j][s][3] = 1.0f + bf_hi(w.y);
+    }
+
+  uint4 hv[HPT], wv[WPT];
+  auto load_stage = [&](int kk) {
+    const int k0 = kk * 32;
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+      const int q = tid + j * 256;
+      hv[j] = ld16(a.h + (m0 + (q >> 2)) * a.r + k0 + (q & 3) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int q = tid + j * 256;
+      const int row = q >> 2;  // s*CB + channel
+      wv[j] = ld16(a.wu + ((int64_t)(row / CB) * a.HS + c0 + row % CB) * a.r + k0 + (q & 3) * 8);
+    }
+  };
+  auto store_stage = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+      const int q = tid + j * 256;
+      st16(&hs[b][(q >> 2) * LDK + (q & 3) * 8], hv[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int q = tid + j * 256;
+      st16(&ws[b][(q >> 2) * LDK + (q & 3) * 8], wv[j]);
+    }
+  };
+
+  f32x4_t acc[NT][NJ][4];
+#pragma unroll
+  for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[tb][j][s] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int b) {
+    uint4 bfr[NT];
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb)
+      bfr[tb] = *reinterpret_cast<const uint4*>(&hs[b][(tl + tb * 16) * LDK + koff]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 af = *reinterpret_cast<const uint4*>(
+            &ws[b][(s * CB + wc * (CB / 2) + j * 16 + (lane & 15)) * LDK + koff]);
+#pragma unroll
+        for (int tb = 0; tb < NT; ++tb) acc[tb][j][s] = mfma16(af, bfr[tb], acc[tb][j][s]);
+      }
+  };
+
+  // epilogue operands, loaded two k steps before the end
+  uint2 r2v[NT][NJ][4];
+  f32x4_t rrv[NT];
+  auto load_epilogue = [&]() {
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb) {
+      const uint32_t t = tl + tb * 16;
+      rrv[tb] = __builtin_bit_cast(f32x4_t, bld16(rRr, t * 16u));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          r2v[tb][j][s] = bld8(rR2, t * rowb + (uint32_t)(s * a.HS + c0 + cl + j * 16) * 2u);
+    }
+  };
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  int kk = 0;
+  for (; kk + 2 < nk; ++kk) {  // every step but the last two: prefetch, contract, stage
+    load_stage(kk + 1);
+    compute(kk & 1);
+    store_stage((kk + 1) & 1);
+    __syncthreads();
+  }
+  if (kk + 1 < nk) {  // second to last step: stage the last k step, then the epilogue loads
+    load_stage(kk + 1);
+    load_epilogue();
+    compute(kk & 1);
+    store_stage((kk + 1) & 1);
+    __syncthreads();
+    ++kk;
+  } else {
+    load_epilogue();
+  }
+  compute(kk & 1);  // last step: no load
+
+  // epilogue: (G2) sigmoid and (MIX) over the lane's four stream accumulators
+#pragma unroll
+  for (int tb = 0; tb < NT; ++tb) {
+    const uint32_t t = tl + tb * 16;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float xo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float g[4], xn[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t w = (q < 2) ? r2v[tb][j][s].x : r2v[tb][j][s].y;
+          const float r2 = (q & 1) ? bf_hi(w) : bf_lo(w);
+          g[s] = acc[tb][j][s][q];
+          xn[s] = r2 * rrv[tb][s] * onep[j][s][q];
+        }
+        xo[q] = mix4(g, xn);
+      }
+      bst8(rX, (t * (uint32_t)a.HS + c0 + cl + j * 16) * 2u, make_uint2(pack_bf2(xo[0], xo[1]), pack_bf2(xo[2], xo[3])));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <int TM, int NW, int NBW, int KS>
 static void launch_k1(const DownArgs& d, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((hcgr_k1_down<TM, NW, NBW, KS>), grid, dim3(NW * 64), 0, st, d);
@@ -492,6 +1055,14 @@ template <int TM, int NW, int RBW>
 static void launch_k2(const UpArgs& u, dim3 grid, size_t lds, hipStream_t st) {
   hipLaunchKernelGGL((hcgr_k2_up_mix<TM, NW, RBW>), grid, dim3(NW * 64), lds, st, u);
 }
+template <int TM, int NW, int BPW, int KS>
+static void launch_kf(const FullArgs& f, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((hcgr_k1_full<TM, NW, BPW, KS>), grid, dim3(NW * 64), 0, st, f);
+}
+template <int TM, int CB>
+static void launch_kt(const TileArgs& t, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((hcgr_k2_tile<TM, CB>), grid, dim3(256), 0, st, t);
+}
 
 int configure_kernels() {
   const int lim = 96 * 1024;
@@ -499,17 +1070,12 @@ int configure_kernels() {
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_up_mix<16, 4, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_up_mix<32, 4, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_up_mix<64, 4, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
-  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_up_mix<64, 4, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
   return (int)hipSuccess;
 }
 
-int launch_forward(const Shape& s, const Plan& p, const ForwardArgs& f, void* stream, void* const* events) {
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  auto mark = [&](int i) -> hipError_t {
-    return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), st) : hipSuccess;
-  };
+static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hipStream_t st,
+                        const std::function<hipError_t(int)>& mark) {
   hipError_t e;
-  if ((e = mark(0)) != hipSuccess) return (int)e;
   char* ws = static_cast<char*>(f.ws);
   float* P = reinterpret_cast<float*>(ws + p.off_p);
   float* SS = reinterpret_cast<float*>(ws + p.off_ss);
@@ -528,8 +1094,7 @@ int launch_forward(const Shape& s, const Plan& p, const ForwardArgs& f, void* st
   switch (p.k1) {
     case K1_T16: launch_k1<16, 7, 1, 128>(d, g1, st); break;
     case K1_T32: launch_k1<32, 7, 1, 128>(d, g1, st); break;
-    case K1_T64S: launch_k1<64, 7, 1, 128>(d, g1, st); break;
-    default: launch_k1<64, 4, 6, 32>(d, g1, st); break;
+    default: launch_k1<64, 7, 1, 128>(d, g1, st); break;
   }
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return (int)e;
 
@@ -551,11 +1116,68 @@ int launch_forward(const Shape& s, const Plan& p, const ForwardArgs& f, void* st
   switch (p.k2) {
     case K2_T16: launch_k2<16, 4, 1>(u, g2, lds, st); break;
     case K2_T32: launch_k2<32, 4, 1>(u, g2, lds, st); break;
-    case K2_T64S: launch_k2<64, 4, 1>(u, g2, lds, st); break;
-    default: launch_k2<64, 4, 4>(u, g2, lds, st); break;
+    default: launch_k2<64, 4, 1>(u, g2, lds, st); break;
   }
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return (int)e;
   return (int)hipSuccess;
+}
+
+static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hipStream_t st,
+                        const std::function<hipError_t(int)>& mark) {
+  hipError_t e;
+  char* ws = static_cast<char*>(f.ws);
+  uint16_t* H = reinterpret_cast<uint16_t*>(ws + p.off_h);
+  float* Q = reinterpret_cast<float*>(ws + p.off_q);
+  const int K = (int)s.k();
+  const KFShape fs = kf_shape(p.kf);
+
+  FullArgs a;
+  a.R = f.R; a.y = f.y; a.inj = f.inj; a.ld_inj = f.ld_inj;
+  a.wn = f.wnorm; a.wn_len = s.wn_full ? K : s.hs;
+  a.w0 = f.wd; a.w1 = s.merged ? nullptr : f.wi; a.folded = s.merged ? 1 : 0;
+  a.M = f.M; a.K = K; a.HS = s.hs; a.HC = s.hc; a.r = s.r; a.n_rows = s.n_rows(); a.nblk = s.nblk();
+  a.nsplit = p.nsplit; a.spw = p.spw;
+  a.eps = s.eps; a.inv_hc = 1.0f / (float)s.hc; a.inv_hs = 1.0f / (float)s.hs;
+  a.R2 = f.R2; a.rrms = f.rrms; a.h = H; a.inj_next = f.inj_next; a.ld_inj_next = f.ld_inj_next;
+  a.Q = Q; a.Mq = p.mq; a.NP = s.np();
+  dim3 g1((unsigned)cdiv(f.M, fs.tm), (unsigned)(p.nsplit * (4 / p.spw)));
+  switch (p.kf) {
+    case KF_T32: launch_kf<32, 8, 3, 128>(a, g1, st); break;
+    default: launch_kf<64, 8, 3, 64>(a, g1, st); break;
+  }
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return (int)e;
+
+  if (p.kind == PLAN_STREAM) {
+    SumArgs sa;
+    sa.Q = Q; sa.Mq = p.mq; sa.M = f.M; sa.NP = s.np(); sa.r = s.r; sa.n_rows = s.n_rows();
+    sa.inv_hc = 1.0f / (float)s.hc; sa.h = H; sa.inj_next = f.inj_next; sa.ld_inj_next = f.ld_inj_next;
+    const int64_t threads = f.M * (s.r / 8 + 1);
+    hipLaunchKernelGGL(hcgr_k1_sum, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st, sa);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
+  if ((e = mark(2)) != hipSuccess) return (int)e;
+
+  TileArgs t;
+  t.h = H; t.M = f.M; t.r = s.r; t.HS = s.hs; t.K = K;
+  t.wu = f.wu; t.R2 = f.R2; t.rrms = f.rrms; t.wn = f.wnorm; t.wn_len = s.wn_full ? K : s.hs; t.x = f.x;
+  const KTShape ts = kt_shape(p.kt);
+  dim3 g2((unsigned)(s.hs / ts.cb), (unsigned)cdiv(f.M, ts.tm));
+  switch (p.kt) {
+    default: launch_kt<64, 64>(t, g2, st); break;
+  }
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return (int)e;
+  return (int)hipSuccess;
+}
+
+int launch_forward(const Shape& s, const Plan& p, const ForwardArgs& f, void* stream, void* const* events) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  std::function<hipError_t(int)> mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), st) : hipSuccess;
+  };
+  hipError_t e;
+  if ((e = mark(0)) != hipSuccess) return (int)e;
+  if (p.kind == PLAN_SPLIT) return launch_split(s, p, f, st, mark);
+  return launch_tiled(s, p, f, st, mark);
 }
 
 }  // namespace hcgr

@@ -169,7 +169,7 @@ def test_plan_description_and_workspace_size(lib):
         n = H.hcgr_workspace_size_for(CFG, M)
         assert n > 0 and n % 256 == 0  # not monotonic: the K split count changes between plans
         d = H.hcgr_describe_plan(CFG, M)
-        assert d.startswith(f"M={M} ")
+        assert d.startswith(f"M={M} plan=")
     assert H.hcgr_describe_plan(CFG, 0) == "M=0: no launch"
 
 
