@@ -58,7 +58,7 @@ def kernel_bytes(name, M, merged=False, plan=""):
     at least, given what it receives and hands on (weights once per launch)."""
     wdown = (R_LOW + HC) * K * 2 + (0 if merged else HS * 2)
     act_in = K * 2 + HS * 2 + HC * 2          # R, y, inj
-    if name == "hcgr_k1_down":
+    if name == "hcgr_k1_dec":
         return wdown + M * (act_in + K * 2)     # + R2 out
     if name == "hcgr_k1_reduce":
         return M * (HC * 4 + HC * 2)            # rrms, inj_next out
@@ -73,7 +73,7 @@ def kernel_bytes(name, M, merged=False, plan=""):
 
 
 def kernel_flops(name, M):
-    if name in ("hcgr_k1_down", "hcgr_k1_full"):
+    if name in ("hcgr_k1_dec", "hcgr_k1_full"):
         return M * 2 * (R_LOW + HC) * K
     if name in ("hcgr_k2_up_mix", "hcgr_k2_tile"):
         return M * 2 * R_LOW * K
@@ -84,7 +84,7 @@ def stage_names(plan: str):
     """Kernels between the four timing marks of hcgr_forward_timed (None where
     a plan has no kernel between two marks)."""
     if "plan=split" in plan:
-        return ("hcgr_k1_down", "hcgr_k1_reduce", "hcgr_k2_up_mix")
+        return ("hcgr_k1_dec", "hcgr_k1_reduce", "hcgr_k2_up_mix")
     if "plan=stream" in plan:
         return ("hcgr_k1_full", "hcgr_k1_sum", "hcgr_k2_tile")
     return ("hcgr_k1_full", None, "hcgr_k2_tile")

@@ -83,11 +83,11 @@ hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out);
 void hcgr_destroy(hcgr_handle h);
 
 /* Bytes of device workspace hcgr_forward needs for M tokens (0 for M == 0).
- * The workspace holds the per-chunk partial sums of the down/inject
- * contraction, the per-chunk sums of squares and the SiLU output h handed to
- * the up kernel. Its contents on entry are ignored (no zero-fill needed);
- * calls that may run concurrently (different streams) need separate
- * workspaces. */
+ * The workspace holds the partial sums of the down/inject contraction (per K
+ * chunk at decode sizes, per stream at mid sizes), the per-chunk sums of
+ * squares and the SiLU output h handed to the up kernel. Its contents on
+ * entry are ignored (no zero-fill needed); calls that may run concurrently
+ * (different streams) need separate workspaces. */
 hcgr_status hcgr_workspace_size(hcgr_handle h, int64_t M, size_t* bytes);
 
 /* The full op for M tokens, enqueued on `stream` (a hipStream_t; NULL = the
@@ -129,12 +129,13 @@ hcgr_status hcgr_forward(hcgr_handle h,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* hcgr_forward with per-kernel timing marks, for measurement: `events` points
- * to 4 hipEvent_t handles owned by the caller (created with timing enabled);
- * events[0] is recorded on `stream` before the first kernel and events[1],
- * events[2], events[3] right after the down/inject kernel, the reduction
- * kernel and the up/mix kernel. Same arguments, checks and results as
- * hcgr_forward otherwise; NULL events -> HCGR_ERR_INVALID_ARGUMENT. */
+/* hcgr_forward with per-stage timing marks, for measurement: `events` points
+ * to 4 hipEvent_t handles owned by the caller (created with timing enabled).
+ * events[0] is recorded on `stream` before the first kernel; events[1] after
+ * the down/inject kernel; events[2] after the reduction kernel when the plan
+ * has one (otherwise right after events[1]); events[3] after the up/mix
+ * kernel. Same arguments, checks and results as hcgr_forward otherwise; NULL
+ * events -> HCGR_ERR_INVALID_ARGUMENT. */
 hcgr_status hcgr_forward_timed(hcgr_handle h,
                                const uint16_t* R, const uint16_t* y,
                                const uint16_t* inj, int64_t ld_inj,

@@ -184,13 +184,13 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
     if (M == 0) {
       snprintf(buf, len, "M=0: no launch");
     } else if (p.kind == hcgr::PLAN_SPLIT) {
-      hcgr::K1Shape a = hcgr::k1_shape(p.k1);
+      hcgr::KDShape a = hcgr::kd_shape(p.k1);
       hcgr::K2Shape b = hcgr::k2_shape(p.k2);
       snprintf(buf, len,
-               "M=%lld plan=split mpad=%lld | k1_down tm=%d waves=%d stage_k=%d k_chunk=%d chunks=%d n_tiles=%d "
+               "M=%lld plan=split mpad=%lld | k1_dec tm=%d row_blocks=%d k_waves=%d k_chunk=%d chunks=%d n_tiles=%d "
                "grid=%dx%lld | k1_reduce waves=%lld | k2_up_mix tm=%d waves=%d channels=%d grid=%dx%lld | "
                "workspace=%zu",
-               (long long)M, (long long)p.mpad, a.tm, a.nw, a.ks, p.kc, p.nkc, p.ntiles_n, p.ntiles_n * p.nkc,
+               (long long)M, (long long)p.mpad, a.tm, a.rb, a.kw, p.kc, p.nkc, p.ntiles_n, p.ntiles_n * p.nkc,
                (long long)(p.mpad / p.tm), (long long)(s.n_rows() * (p.mpad / 16)), b.tm, b.nw, p.cb,
                s.hs / p.cb, (long long)(p.mpad / p.tm), p.ws_bytes);
     } else {

@@ -9,7 +9,7 @@
 //
 // Three plans, chosen by the token count M (make_plan):
 //   SPLIT  (decode sizes). Weight streaming over every CU:
-//     K1  hcgr_k1_down    COMBINE + sums of squares + unscaled partials P for a
+//     K1  hcgr_k1_dec     COMBINE + sums of squares + unscaled partials P for a
 //                         (token tile, K chunk inside one stream, row tile)
 //     K1r hcgr_k1_reduce  sums the chunk partials per stream, forms rrms,
 //                         scales, SiLU(./HC) -> h (workspace), inj_next
@@ -37,24 +37,34 @@ namespace hcgr {
 
 enum PlanKind { PLAN_SPLIT = 0, PLAN_STREAM = 1, PLAN_FULL = 2 };
 
-// SPLIT-plan kernel variants (template instantiations).
-enum K1Variant { K1_T16 = 0, K1_T32 = 1, K1_T64S = 2, K1_NVAR };
-enum K2Variant { K2_T16 = 0, K2_T32 = 1, K2_T64S = 2, K2_NVAR };
-
-struct K1Shape { int tm, nw, nbw, ks; };
-struct K2Shape { int tm, nw, rbw; };
-
-inline K1Shape k1_shape(int v) {
-  static const K1Shape t[K1_NVAR] = {{16, 7, 1, 128}, {32, 7, 1, 128}, {64, 7, 1, 128}};
+// SPLIT-plan down kernel variants: token tile, 16-row blocks per workgroup,
+// waves splitting each block's k range, columns per chunk.
+enum KDVariant {
+  KD_T16_R7_K1_C128 = 0, KD_T16_R1_K4_C512, KD_T16_R3_K1_C256, KD_T16_R3_K2_C512,
+  KD_T32_R7_K1_C128, KD_T32_R1_K4_C512, KD_T32_R3_K1_C256, KD_T32_R3_K2_C512,
+  KD_T64_R7_K1_C128, KD_T64_R3_K1_C256, KD_NVAR
+};
+struct KDShape { int tm, rb, kw, kc; };
+inline KDShape kd_shape(int v) {
+  static const KDShape t[KD_NVAR] = {{16, 7, 1, 128}, {16, 1, 4, 512}, {16, 3, 1, 256}, {16, 3, 2, 512},
+                                     {32, 7, 1, 128}, {32, 1, 4, 512}, {32, 3, 1, 256}, {32, 3, 2, 512},
+                                     {64, 7, 1, 128}, {64, 3, 1, 256}};
   return t[v];
 }
+// SPLIT-plan up kernel variants (token tile; 4 waves of 4 channels x 4 streams).
+enum K2Variant { K2_T16 = 0, K2_T32 = 1, K2_T64S = 2, K2_NVAR };
+struct K2Shape { int tm, nw, rbw; };
 inline K2Shape k2_shape(int v) {
   static const K2Shape t[K2_NVAR] = {{16, 4, 1}, {32, 4, 1}, {64, 4, 1}};
   return t[v];
 }
-// Chunks per stream handled by one lane group of the reduction kernel: the
-// split plans keep chunks-per-stream <= 4 * kRedPerLane.
-constexpr int kRedPerLane = 8;
+// The reduction kernel gives each of a wave's 4 lane groups up to kRedMaxCpl
+// chunks per stream (instantiated: 1, 2, 3, 5, 8).
+constexpr int kRedMaxCpl = 8;
+inline int red_cpl(int kcps) {
+  const int need = (kcps + 3) / 4;
+  return need <= 1 ? 1 : need <= 2 ? 2 : need <= 3 ? 3 : need <= 5 ? 5 : 8;
+}
 
 // STREAM/FULL down kernel variants: token tile, waves, row blocks per wave,
 // k per LDS stage. 8 waves x 3 blocks cover 24 16-row blocks per workgroup.
@@ -107,6 +117,32 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Largest M served by the SPLIT plan.
 constexpr int64_t kSplitMaxM = 64;
 
+// SPLIT plan with down-kernel variant kd; false when the stream width does
+// not split into chunks of the variant (the caller then takes another plan).
+inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
+  const KDShape d = kd_shape(kd);
+  if (s.hs % d.kc != 0 || s.hs / d.kc > 4 * kRedMaxCpl) return false;
+  Plan p;
+  p.M = M;
+  p.kind = PLAN_SPLIT;
+  p.k1 = kd;
+  p.k2 = d.tm == 16 ? K2_T16 : d.tm == 32 ? K2_T32 : K2_T64S;
+  p.tm = d.tm;
+  p.kc = d.kc;
+  p.kcps = s.hs / d.kc;
+  p.nkc = s.hc * p.kcps;
+  p.ntiles_n = (s.nblk() + d.rb - 1) / d.rb;
+  p.cb = k2_shape(p.k2).nw * 4;
+  p.mpad = (M + p.tm - 1) / p.tm * p.tm;
+  const size_t np = (size_t)s.np();
+  p.off_p = 0;
+  p.off_ss = align256(p.off_p + (size_t)p.nkc * np * (size_t)p.mpad * sizeof(float));
+  p.off_h = align256(p.off_ss + (size_t)p.nkc * (size_t)p.mpad * sizeof(float));
+  p.ws_bytes = align256(p.off_h + (size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
+  *out = p;
+  return true;
+}
+
 // Pure host planning: tile sizes and split counts by token count M.
 inline Plan make_plan(const Shape& s, int64_t M) {
   Plan p;
@@ -115,36 +151,9 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   const int hs = s.hs;
   const size_t np = (size_t)s.np();
   if (M <= kSplitMaxM) {
-    p.kind = PLAN_SPLIT;
-    int kc;
-    if (M <= 16) { p.k1 = K1_T16; p.k2 = K2_T16; kc = 128; }
-    else if (M <= 32) { p.k1 = K1_T32; p.k2 = K2_T32; kc = 128; }
-    else { p.k1 = K1_T64S; p.k2 = K2_T64S; kc = 128; }
-    const K1Shape a = k1_shape(p.k1);
-    const K2Shape b = k2_shape(p.k2);
-    // the chunk must divide the stream width and hold whole LDS stages, and a
-    // stream may have at most 4 * kRedPerLane chunks (hs itself always fits)
-    auto valid = [&](int c) { return c >= a.ks && c % a.ks == 0 && hs % c == 0; };
-    while (kc > a.ks && !valid(kc)) kc -= a.ks;
-    if (!valid(kc)) kc = a.ks;
-    while (hs / kc > 4 * kRedPerLane) {
-      int c = kc + a.ks;
-      while (!valid(c)) c += a.ks;
-      kc = c;
-    }
-    p.tm = a.tm;  // K1 and K2 share the token tile of a plan
-    p.kc = kc;
-    p.kcps = hs / kc;
-    p.nkc = s.hc * p.kcps;
-    int per_tile = a.nw * a.nbw;
-    p.ntiles_n = (s.nblk() + per_tile - 1) / per_tile;
-    p.cb = b.nw * b.rbw * 4;
-    p.mpad = (M + p.tm - 1) / p.tm * p.tm;
-    p.off_p = 0;
-    p.off_ss = align256(p.off_p + (size_t)p.nkc * np * (size_t)p.mpad * sizeof(float));
-    p.off_h = align256(p.off_ss + (size_t)p.nkc * (size_t)p.mpad * sizeof(float));
-    p.ws_bytes = align256(p.off_h + (size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
-    return p;
+    const int kd = M <= 16 ? KD_T16_R7_K1_C128 : M <= 32 ? KD_T32_R7_K1_C128 : KD_T64_R7_K1_C128;
+    const int kd_wide = M <= 16 ? KD_T16_R3_K2_C512 : M <= 32 ? KD_T32_R3_K2_C512 : KD_T64_R3_K1_C256;
+    if (make_split(s, M, kd, &p) || make_split(s, M, kd_wide, &p)) return p;
   }
   // STREAM / FULL: aim for at least one down workgroup per CU (256 CUs)
   const int64_t target = 256;

@@ -69,15 +69,6 @@ __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\
 // logistic function through the hardware 2^x and reciprocal: 1/(1 + 2^(-v*log2 e))
 __device__ __forceinline__ float sigmoid_f(float v) { return __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
-// ---------------------------------------------------------------------------
-// K1: COMBINE + sums of squares + down/inject partial contraction.
-// Workgroup = (token tile of TM rows) x (K chunk [kbeg, kbeg+KC) inside one
-// stream) x (n tile of NW*NBW 16-row blocks of the down/inject rows). The
-// activation tile of each LDS stage (TM x KS) is combined once per workgroup
-// and shared by all waves through LDS (MFMA B operand); each wave streams its
-// own weight rows straight from global memory into registers (A operand),
-// one stage ahead of the MFMAs.
-// ---------------------------------------------------------------------------
 struct DownArgs {
   const uint16_t* R;
   const uint16_t* y;
@@ -98,191 +89,173 @@ struct DownArgs {
   float* SS;  // [nkc][Mpad] partial sums of squares
 };
 
-template <int TM, int NW, int NBW, int KS>
-__global__ __launch_bounds__(NW * 64) void hcgr_k1_down(DownArgs a) {
+// ---------------------------------------------------------------------------
+// hcgr_k1_dec (SPLIT plan, decode sizes): COMBINE + per-chunk sums of squares
+// + unscaled partial down/inject products.
+// Workgroup = (K chunk of KC columns inside one stream) x (row tile of RB
+// 16-row blocks) x (token tile of TM rows). NW = RB*KW waves; wave (rb, kw)
+// contracts block rb over the kw-th slice (KC/KW columns) of the chunk, and
+// the KW slices are summed through LDS. Every global load the workgroup needs
+// (weight fragments straight into MFMA A registers, the R/y/Wnorm chunks of
+// the activation tile) is issued before any arithmetic, through range-limited
+// buffer descriptors (rows past M read as zero), so the workgroup waits for
+// one memory round trip; iw is formed while the loads are in flight.
+// Partials P[chunk][row][token] and sums of squares SS[chunk][token] are
+// stored for valid tokens only.
+// ---------------------------------------------------------------------------
+template <int TM, int RB, int KW, int KC>
+__global__ __launch_bounds__(RB * KW * 64) void hcgr_k1_dec(DownArgs a) {
+  constexpr int NW = RB * KW;
   constexpr int NT = NW * 64;
-  constexpr int CPR = KS / 8;               // 16-byte chunks per tile row
-  constexpr int NCH = TM * CPR;             // chunks per stage
-  constexpr int CPT = (NCH + NT - 1) / NT;  // chunks per thread
-  constexpr int LDA = KS + 8;               // padded LDS row, bf16 elements
+  constexpr int KPW = KC / KW;   // columns per wave
+  constexpr int NKS = KPW / 32;  // MFMA k steps per wave
+  static_assert(NKS >= 1 && KPW % 32 == 0, "whole k steps per wave");
+  constexpr int CPR = KC / 8;    // 16-byte chunks per token row of the tile
+  constexpr int NCH = TM * CPR;
+  constexpr int CPT = (NCH + NT - 1) / NT;
+  constexpr int LDA = KC + 8;
   constexpr int NTB = TM / 16;
-  constexpr int NKS = KS / 32;
 
-  __shared__ __attribute__((aligned(16))) uint16_t act[2][TM * LDA];
-  __shared__ float ssp[NCH];
+  __shared__ __attribute__((aligned(16))) uint16_t act[TM * LDA];
   __shared__ float iwh[TM], iwl[TM];
+  __shared__ float ssp[NCH];
+  __shared__ __attribute__((aligned(16))) float red[KW > 1 ? (KW - 1) * RB * NTB * 256 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = wave % RB, kw = wave / RB;
   const int kc = blockIdx.x % a.nkc;
-  const int nt = blockIdx.x / a.nkc;
+  const int rt = blockIdx.x / a.nkc;
   const int64_t m0 = (int64_t)blockIdx.y * TM;
-  const int kbeg = kc * a.KC;
+  const int rows = (int)min((int64_t)TM, a.M - m0);
+  const int kbeg = kc * KC;
   const int s = kbeg / a.HS;
-  const bool lead = (nt == 0);  // the n-tile-0 workgroups write R2 and the sums of squares
-  const int nstage = a.KC / KS;
+  const int cst = kbeg - s * a.HS;
+  const bool lead = rt == 0;  // row tile 0 writes R2 and the sums of squares
   const int koff = 8 * (lane >> 4);
+  // 0. injection logit of this thread's token (clamped row: no branch)
+  const uint16_t injb = a.inj[(m0 + min(tid % TM, rows - 1)) * a.ld_inj + s];
+  const uint32_t rowb = (uint32_t)a.K * 2u;
+  const int nblk = (a.n_rows + 15) / 16;
 
-  // (COMBINE) iw = 2 * sigmoid(inj[s] / HC) for this stream, per token row.
-  // Formed in fp64 and kept as an fp32 pair iw = hi + lo (~48 bits): when R
-  // and y*iw nearly cancel, R2 is far smaller than y and a single fp32 iw
-  // would put an error of |y| * 2^-24 on it, several bf16 ulps of R2.
+  // 1. weight fragments of this wave's block (rows past the matrix read 0)
+  const int nb = rt * RB + rb;
+  const bool bval = nb < nblk;  // wave-uniform
+  const bool down = nb * 16 < a.r || !a.w1;
+  const rsrc_t rW = down ? make_rsrc(a.w0, (uint32_t)(a.w1 ? a.r : a.n_rows) * rowb)
+                         : make_rsrc(a.w1, (uint32_t)a.HC * rowb);
+  const uint32_t wrow = (uint32_t)((down ? nb * 16 : nb * 16 - a.r) + (lane & 15)) * rowb;
+  uint4 wf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) wf[ks] = bld16(rW, wrow + (uint32_t)(kbeg + kw * KPW + ks * 32 + koff) * 2u);
+
+  // 2. activation chunks (R, y, Wnorm); a thread's chunks share one column
+  const rsrc_t rR = make_rsrc(a.R + m0 * a.K, (uint32_t)rows * rowb);
+  const rsrc_t rY = make_rsrc(a.y + m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
+  const rsrc_t rWn = make_rsrc(a.wn, a.folded ? 0u : (uint32_t)(a.wn_full ? a.K : a.HS) * 2u);
+  uint4 rv[CPT], yv[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int q = min(tid + j * NT, NCH - 1);
+    const uint32_t t = q / CPR, col = (q % CPR) * 8;
+    rv[j] = bld16(rR, t * rowb + (uint32_t)(kbeg + col) * 2u);
+    yv[j] = bld16(rY, (t * (uint32_t)a.HS + cst + col) * 2u);
+  }
+  uint4 wv[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int q = min(tid + j * NT, NCH - 1);
+    wv[j] = bld16(rWn, ((a.wn_full ? (uint32_t)(s * a.HS) : 0u) + cst + (q % CPR) * 8) * 2u);
+  }
+
+  // 3. (COMBINE) iw = 2*sigmoid(inj/HC) for this stream, fp64 -> fp32 hi + lo
+  //    (R2 = (R + y*hi) + y*lo stays within an ulp of R2 under cancellation)
   if (tid < TM) {
-    const int64_t m = m0 + tid;
     double v = 0.0;
-    if (m < a.M) v = 2.0 / (1.0 + exp(-(double)bf1(a.inj[m * a.ld_inj + s]) / (double)a.HC));
+    if (tid < rows) v = 2.0 / (1.0 + exp(-(double)bf1(injb) / (double)a.HC));
     const float hi = (float)v;
     iwh[tid] = hi;
     iwl[tid] = (float)(v - (double)hi);
   }
-
-  // weight rows of this wave (A operand rows = down/inject output rows n)
-  const uint16_t* wrow[NBW];
-  int nblk[NBW];
-#pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    const int nb = nt * (NW * NBW) + wave + NW * i;
-    const int n = nb * 16 + (lane & 15);
-    nblk[i] = nb;
-    if (n < a.r) wrow[i] = a.w0 + (int64_t)n * a.K;
-    else if (n < a.n_rows) wrow[i] = a.w1 ? a.w1 + (int64_t)(n - a.r) * a.K : a.w0 + (int64_t)n * a.K;
-    else wrow[i] = nullptr;
-  }
-
-  uint4 wnx[NBW][NKS];
-  auto load_w = [&](int kst) {
-#pragma unroll
-    for (int i = 0; i < NBW; ++i)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        wnx[i][ks] = wrow[i] ? ld16(wrow[i] + kst + ks * 32 + koff) : make_uint4(0, 0, 0, 0);
-  };
-
-  uint4 rv[CPT], yv[CPT], wv[CPT];
-  auto load_a = [&](int kst) {
-    const int cst = kst - s * a.HS;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int q = tid + j * NT;
-      rv[j] = yv[j] = wv[j] = make_uint4(0, 0, 0, 0);
-      if (q < NCH) {
-        const int t = q / CPR;
-        const int col = (q % CPR) * 8;
-        const int64_t m = m0 + t;
-        if (m < a.M) {
-          rv[j] = ld16(a.R + m * a.K + kst + col);
-          yv[j] = ld16(a.y + m * a.HS + cst + col);
-        }
-        if (!a.folded) wv[j] = ld16(a.wn + (a.wn_full ? kst + col : cst + col));
-      }
-    }
-  };
-
-  float ss[CPT];
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) ss[j] = 0.0f;
-
-  // (COMBINE) R2 = R + y*iw in fp32; sum of squares; R2 -> bf16 output;
-  // activation R2*(1+Wnorm) (or R2 when the weight is folded) -> LDS.
-  auto store_a = [&](int kst, int buf) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int q = tid + j * NT;
-      if (q < NCH) {
-        const int t = q / CPR;
-        const int col = (q % CPR) * 8;
-        const float ih = iwh[t];
-        const float il = iwl[t];
-        const uint32_t rw[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
-        const uint32_t yw[4] = {yv[j].x, yv[j].y, yv[j].z, yv[j].w};
-        const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
-        uint32_t o2[4], ou[4];
-        float acc = ss[j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // R2 = (R + y*hi) + y*lo: each fma rounds once, relative to R2 itself
-          const float r0 = fmaf(bf_lo(yw[e]), il, fmaf(bf_lo(yw[e]), ih, bf_lo(rw[e])));
-          const float r1 = fmaf(bf_hi(yw[e]), il, fmaf(bf_hi(yw[e]), ih, bf_hi(rw[e])));
-          acc = fmaf(r0, r0, acc);
-          acc = fmaf(r1, r1, acc);
-          o2[e] = pack_bf2(r0, r1);
-          if (a.folded) ou[e] = o2[e];
-          else ou[e] = pack_bf2(r0 * (1.0f + bf_lo(ww[e])), r1 * (1.0f + bf_hi(ww[e])));
-        }
-        ss[j] = acc;
-        const int64_t m = m0 + t;
-        if (lead && m < a.M) st16(a.R2 + m * a.K + kst + col, make_uint4(o2[0], o2[1], o2[2], o2[3]));
-        st16(&act[buf][t * LDA + col], make_uint4(ou[0], ou[1], ou[2], ou[3]));
-      }
-    }
-  };
-
-  f32x4_t acc[NBW][NTB];
-#pragma unroll
-  for (int i = 0; i < NBW; ++i)
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) acc[i][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  load_w(kbeg);
-  load_a(kbeg);
-  __syncthreads();  // iwh/iwl visible
-  store_a(kbeg, 0);
   __syncthreads();
 
-  uint4 wcur[NBW][NKS];
-  for (int st = 0; st < nstage; ++st) {
-    const int kst = kbeg + st * KS;
+  // 4. R2 = R + y*iw (fp32), sum of squares, R2 -> bf16 output, activation
+  //    R2*(1+Wnorm) -> LDS (Wnorm reads as 0 for folded weights)
+  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, lead ? (uint32_t)rows * rowb : 0u);
 #pragma unroll
-    for (int i = 0; i < NBW; ++i)
+  for (int j = 0; j < CPT; ++j) {
+    const int q = tid + j * NT;
+    if (CPT * NT > NCH && q >= NCH) break;
+    const int t = q / CPR, col = (q % CPR) * 8;
+    const float ih = iwh[t], il = iwl[t];
+    const uint32_t rw[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
+    const uint32_t yw[4] = {yv[j].x, yv[j].y, yv[j].z, yv[j].w};
+    const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+    uint32_t o2[4], ou[4];
+    float acc = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) wcur[i][ks] = wnx[i][ks];
-    const bool more = (st + 1 < nstage);
-    if (more) {
-      load_w(kst + KS);
-      load_a(kst + KS);
+    for (int e = 0; e < 4; ++e) {
+      const float r0 = fmaf(bf_lo(yw[e]), il, fmaf(bf_lo(yw[e]), ih, bf_lo(rw[e])));
+      const float r1 = fmaf(bf_hi(yw[e]), il, fmaf(bf_hi(yw[e]), ih, bf_hi(rw[e])));
+      acc = fmaf(r0, r0, acc);
+      acc = fmaf(r1, r1, acc);
+      o2[e] = pack_bf2(r0, r1);
+      ou[e] = pack_bf2(r0 * (1.0f + bf_lo(ww[e])), r1 * (1.0f + bf_hi(ww[e])));
     }
-    const uint16_t* buf = act[st & 1];
+    ssp[q] = acc;
+    bst16(rR2, (uint32_t)t * rowb + (uint32_t)(kbeg + col) * 2u, make_uint4(o2[0], o2[1], o2[2], o2[3]));
+    st16(&act[t * LDA + col], make_uint4(ou[0], ou[1], ou[2], ou[3]));
+  }
+  __syncthreads();
+
+  // 5. contraction of this wave's block over its slice of the chunk
+  f32x4_t acc[NTB];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+  for (int tb = 0; tb < NTB; ++tb) acc[tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  if (bval) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        const uint4 b = *reinterpret_cast<const uint4*>(buf + (tb * 16 + (lane & 15)) * LDA + ks * 32 + koff);
-#pragma unroll
-        for (int i = 0; i < NBW; ++i) acc[i][tb] = mfma16(wcur[i][ks], b, acc[i][tb]);
+        const uint4 b =
+            *reinterpret_cast<const uint4*>(&act[(tb * 16 + (lane & 15)) * LDA + kw * KPW + ks * 32 + koff]);
+        acc[tb] = mfma16(wf[ks], b, acc[tb]);
       }
-    }
-    if (more) store_a(kst + KS, (st + 1) & 1);
-    __syncthreads();
   }
-
-  // partial sums: D[row n][col token]
+  // 6. sum the KW slices: waves kw > 0 hand their accumulators to wave kw = 0
+  if constexpr (KW > 1) {
+    if (kw > 0) {
 #pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    if (nblk[i] * 16 >= a.NP) continue;
+      for (int tb = 0; tb < NTB; ++tb)
+        *reinterpret_cast<f32x4_t*>(&red[(((kw - 1) * RB + rb) * NTB + tb) * 256 + lane * 4]) = acc[tb];
+    }
+    __syncthreads();
+    if (kw == 0) {
+#pragma unroll
+      for (int k2 = 1; k2 < KW; ++k2)
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+          acc[tb] += *reinterpret_cast<const f32x4_t*>(&red[(((k2 - 1) * RB + rb) * NTB + tb) * 256 + lane * 4]);
+    }
+  }
+  if (kw == 0 && bval) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
-      const int64_t m = m0 + tb * 16 + (lane & 15);
+      const int t = tb * 16 + (lane & 15);
+      if (t >= rows) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = nblk[i] * 16 + 4 * (lane >> 4) + q;
-        a.P[((int64_t)kc * a.NP + n) * a.Mpad + m] = acc[i][tb][q];
+        const int n = nb * 16 + 4 * (lane >> 4) + q;
+        a.P[((int64_t)kc * a.NP + n) * a.Mpad + m0 + t] = acc[tb][q];
       }
     }
   }
-  // per-row sum of squares of this chunk, in a fixed order (deterministic)
-  if (lead) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int q = tid + j * NT;
-      if (q < NCH) ssp[q] = ss[j];
-    }
-    __syncthreads();
-    if (tid < TM) {
-      float t = 0.0f;
-      for (int c = 0; c < CPR; ++c) t += ssp[tid * CPR + c];
-      a.SS[(int64_t)kc * a.Mpad + m0 + tid] = t;
-    }
+  // 7. the chunk's sum of squares per token, summed in a fixed order
+  if (lead && tid < rows) {
+    float t = 0.0f;
+    for (int c = 0; c < CPR; ++c) t += ssp[tid * CPR + c];
+    a.SS[(int64_t)kc * a.Mpad + m0 + tid] = t;
   }
 }
 
@@ -314,6 +287,7 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
   return v;
 }
 
+template <int CPL>
 __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -322,23 +296,25 @@ __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
   if (n >= a.n_rows) return;  // whole wave leaves together
   const int64_t m = (wid % mblocks) * 16 + (lane & 15);
   const int g = lane >> 4;
-  const int kcps = a.kcps;  // <= 4 * kRedPerLane
-  float sv[4][kRedPerLane], pv[4][kRedPerLane];
+  const int kcps = a.kcps;  // <= 4 * CPL
+  float sv[4][CPL], pv[4][CPL];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int i = 0; i < kRedPerLane; ++i) {
+    for (int i = 0; i < CPL; ++i) {
       const int c = g + 4 * i;
-      const int64_t kc = (int64_t)s * kcps + c;
-      sv[s][i] = c < kcps ? a.SS[kc * a.Mpad + m] : 0.0f;
-      pv[s][i] = c < kcps ? a.P[(kc * a.NP + n) * a.Mpad + m] : 0.0f;
+      const int64_t kc = (int64_t)s * kcps + min(c, kcps - 1);  // clamped: no branch around the load
+      const float sl = a.SS[kc * a.Mpad + m];
+      const float pl = a.P[(kc * a.NP + n) * a.Mpad + m];
+      sv[s][i] = c < kcps ? sl : 0.0f;
+      pv[s][i] = c < kcps ? pl : 0.0f;
     }
   float ss[4], ps[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     float t = 0.0f, u = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kRedPerLane; ++i) {
+    for (int i = 0; i < CPL; ++i) {
       t += sv[s][i];
       u += pv[s][i];
     }
@@ -423,17 +399,28 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k2_up_mix(UpArgs a) {
       const int64_t m = m0 + tb * 16 + (lane & 15);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        pr2[tb][q] = m < a.M ? bf1(a.R2[m * a.K + q * a.HS + c]) : 0.0f;
-        prr[tb][q] = m < a.M ? a.rrms[m * 4 + q] : 0.0f;
+        const int64_t mc = m < a.M ? m : a.M - 1;  // clamped: no branch around the load
+        pr2[tb][q] = bf1(a.R2[mc * a.K + q * a.HS + c]);
+        prr[tb][q] = a.rrms[mc * 4 + q];
       }
     }
   }
 
+  // h tile -> LDS: every load is issued before the first LDS store (a
+  // compile-time count for r <= 512, clamped past the tile: no branch around
+  // a load), so staging costs one memory round trip
   const int cpr = a.r / 8;
-  for (int q = tid; q < TM * cpr; q += NT) {
-    const int t = q / cpr;
-    const int col = (q % cpr) * 8;
-    st16(&hl[t * ldh + col], ld16(a.h + (m0 + t) * a.r + col));
+  constexpr int HPT = TM * 64 / NT;
+  uint4 hv[HPT];
+#pragma unroll
+  for (int j = 0; j < HPT; ++j) {
+    const int q = min(tid + j * NT, TM * cpr - 1);
+    hv[j] = ld16(a.h + (m0 + q / cpr) * a.r + (q % cpr) * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < HPT; ++j) {
+    const int q = tid + j * NT;
+    if (q < TM * cpr) st16(&hl[(q / cpr) * ldh + (q % cpr) * 8], hv[j]);
   }
   __syncthreads();
 
@@ -1047,9 +1034,32 @@ __global__ __launch_bounds__(256) void hcgr_k2_tile(TileArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int TM, int NW, int NBW, int KS>
-static void launch_k1(const DownArgs& d, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((hcgr_k1_down<TM, NW, NBW, KS>), grid, dim3(NW * 64), 0, st, d);
+template <int TM, int RB, int KW, int KC>
+static void launch_kd(const DownArgs& d, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((hcgr_k1_dec<TM, RB, KW, KC>), grid, dim3(RB * KW * 64), 0, st, d);
+}
+static void launch_kd_variant(int v, const DownArgs& d, dim3 grid, hipStream_t st) {
+  switch (v) {
+    case KD_T16_R7_K1_C128: launch_kd<16, 7, 1, 128>(d, grid, st); break;
+    case KD_T16_R1_K4_C512: launch_kd<16, 1, 4, 512>(d, grid, st); break;
+    case KD_T16_R3_K1_C256: launch_kd<16, 3, 1, 256>(d, grid, st); break;
+    case KD_T16_R3_K2_C512: launch_kd<16, 3, 2, 512>(d, grid, st); break;
+    case KD_T32_R7_K1_C128: launch_kd<32, 7, 1, 128>(d, grid, st); break;
+    case KD_T32_R1_K4_C512: launch_kd<32, 1, 4, 512>(d, grid, st); break;
+    case KD_T32_R3_K1_C256: launch_kd<32, 3, 1, 256>(d, grid, st); break;
+    case KD_T32_R3_K2_C512: launch_kd<32, 3, 2, 512>(d, grid, st); break;
+    case KD_T64_R7_K1_C128: launch_kd<64, 7, 1, 128>(d, grid, st); break;
+    default: launch_kd<64, 3, 1, 256>(d, grid, st); break;
+  }
+}
+static void launch_reduce(int cpl, const ReduceArgs& r, dim3 grid, hipStream_t st) {
+  switch (cpl) {
+    case 1: hipLaunchKernelGGL(hcgr_k1_reduce<1>, grid, dim3(256), 0, st, r); break;
+    case 2: hipLaunchKernelGGL(hcgr_k1_reduce<2>, grid, dim3(256), 0, st, r); break;
+    case 3: hipLaunchKernelGGL(hcgr_k1_reduce<3>, grid, dim3(256), 0, st, r); break;
+    case 5: hipLaunchKernelGGL(hcgr_k1_reduce<5>, grid, dim3(256), 0, st, r); break;
+    default: hipLaunchKernelGGL(hcgr_k1_reduce<8>, grid, dim3(256), 0, st, r); break;
+  }
 }
 template <int TM, int NW, int RBW>
 static void launch_k2(const UpArgs& u, dim3 grid, size_t lds, hipStream_t st) {
@@ -1091,21 +1101,17 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   d.inv_hc = 1.0f / (float)s.hc;
   d.R2 = f.R2; d.P = P; d.SS = SS;
   dim3 g1((unsigned)(p.ntiles_n * p.nkc), (unsigned)(p.mpad / p.tm));
-  switch (p.k1) {
-    case K1_T16: launch_k1<16, 7, 1, 128>(d, g1, st); break;
-    case K1_T32: launch_k1<32, 7, 1, 128>(d, g1, st); break;
-    default: launch_k1<64, 7, 1, 128>(d, g1, st); break;
-  }
+  launch_kd_variant(p.k1, d, g1, st);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return (int)e;
-
   ReduceArgs r;
   r.P = P; r.SS = SS; r.Mpad = p.mpad; r.M = f.M;
   r.NP = s.np(); r.kcps = p.kcps; r.HS = s.hs; r.HC = s.hc; r.r = s.r; r.n_rows = s.n_rows();
   r.eps = s.eps; r.inv_hc = 1.0f / (float)s.hc; r.inv_hs = 1.0f / (float)s.hs;
   r.rrms = f.rrms; r.h = H; r.inj_next = f.inj_next; r.ld_inj_next = f.ld_inj_next;
   const int64_t waves = (int64_t)s.n_rows() * (p.mpad / 16);
-  hipLaunchKernelGGL(hcgr_k1_reduce, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, r);
-  if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return (int)e;
+  launch_reduce(red_cpl(p.kcps), r, dim3((unsigned)((waves + 3) / 4)), st);
+  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  if ((e = mark(2)) != hipSuccess) return (int)e;
 
   UpArgs u;
   u.h = H; u.Mpad = p.mpad; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = K;

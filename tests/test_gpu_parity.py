@@ -233,6 +233,32 @@ def test_workspace_reuse_across_sizes(H, op, weights):
     check_all(res[7], run_oracle(inp))
 
 
+def test_decode_interleaved_stress(H, op, weights):
+    """Many back-to-back decode-size calls of four sizes interleaved on one
+    workspace (cross-workgroup partials written by one kernel and summed by
+    the next): bitwise-identical results every time, matching the oracle."""
+    ws = torch.empty(max(H.hcgr_workspace_size(op.handle, 64), 256), dtype=torch.uint8, device="cuda")
+    sizes = (5, 32, 64, 1)
+    inps = {M: synth.make_inputs(M, SHAPE, seed=20 + M, device="cuda", weights=weights) for M in sizes}
+    outs = {M: op.alloc_outputs(M) for M in sizes}
+    first = {}
+    for rep in range(25):
+        for M in sizes:
+            inp, out = inps[M], outs[M]
+            op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"], out=out,
+                       workspace=ws)
+            if rep == 0:
+                torch.cuda.synchronize()
+                first[M] = {k: out[k].clone() for k in ("R2", "rrms", "inj_next", "x")}
+            elif rep % 6 == 0 or rep == 24:
+                torch.cuda.synchronize()
+                for k in first[M]:
+                    assert torch.equal(first[M][k], out[k]), (rep, M, k)
+    torch.cuda.synchronize()
+    for M in sizes:
+        check_all(outs[M], run_oracle(inps[M]))
+
+
 def test_graph_capture_replays(op, weights):
     """hcgr_forward captured into a HIP graph: several replays with new input
     values written between them, each checked against an eager call."""
