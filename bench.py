@@ -62,8 +62,9 @@ def kernel_bytes(name, M, merged=False, plan=""):
         return wdown + M * (act_in + K * 2)     # + R2 out
     if name == "hcgr_k1_reduce":
         return M * (HC * 4 + HC * 2)            # rrms, inj_next out
-    if name == "hcgr_k1_full":
-        out = K * 2 + HC * 4 + (HC * 2 if "plan=full" in plan else 0)
+    if name in ("hcgr_k1_full", "hcgr_k1_tile"):
+        writes_inj = "plan=full" in plan or "streams/wg=4" in plan
+        out = K * 2 + HC * 4 + (HC * 2 if writes_inj else 0)
         return wdown + M * (act_in + out)
     if name == "hcgr_k1_sum":
         return M * HC * 2                       # inj_next out
@@ -73,7 +74,7 @@ def kernel_bytes(name, M, merged=False, plan=""):
 
 
 def kernel_flops(name, M):
-    if name in ("hcgr_k1_dec", "hcgr_k1_full"):
+    if name in ("hcgr_k1_dec", "hcgr_k1_full", "hcgr_k1_tile"):
         return M * 2 * (R_LOW + HC) * K
     if name in ("hcgr_k2_up_mix", "hcgr_k2_tile"):
         return M * 2 * R_LOW * K
@@ -85,6 +86,8 @@ def stage_names(plan: str):
     a plan has no kernel between two marks)."""
     if "plan=split" in plan:
         return ("hcgr_k1_dec", "hcgr_k1_reduce", "hcgr_k2_up_mix")
+    if "plan=tile" in plan:
+        return ("hcgr_k1_tile", "hcgr_k1_sum" if "streams/wg=1" in plan else None, "hcgr_k2_tile")
     if "plan=stream" in plan:
         return ("hcgr_k1_full", "hcgr_k1_sum", "hcgr_k2_tile")
     return ("hcgr_k1_full", None, "hcgr_k2_tile")

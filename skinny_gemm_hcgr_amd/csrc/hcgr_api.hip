@@ -193,6 +193,14 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
                (long long)M, (long long)p.mpad, a.tm, a.rb, a.kw, p.kc, p.nkc, p.ntiles_n, p.ntiles_n * p.nkc,
                (long long)(p.mpad / p.tm), (long long)(s.n_rows() * (p.mpad / 16)), b.tm, b.nw, p.cb,
                s.hs / p.cb, (long long)(p.mpad / p.tm), p.ws_bytes);
+    } else if (p.kind == hcgr::PLAN_TILE) {
+      hcgr::KTShape t = hcgr::kt_shape(p.kt);
+      snprintf(buf, len,
+               "M=%lld plan=tile | k1_tile tm=%d waves=8 stage_k=64 streams/wg=%d row_splits=%d grid=%lld%s | "
+               "k2_tile tm=%d channels=%d grid=%dx%lld | workspace=%zu",
+               (long long)M, (int)hcgr::kTileTm, p.spw, p.nsplit,
+               (long long)(hcgr::cdiv(M, hcgr::kTileTm) * p.nsplit * (4 / p.spw)), p.spw == 1 ? " | k1_sum" : "",
+               t.tm, t.cb, s.hs / t.cb, (long long)hcgr::cdiv(M, t.tm), p.ws_bytes);
     } else {
       hcgr::KFShape f = hcgr::kf_shape(p.kf);
       hcgr::KTShape t = hcgr::kt_shape(p.kt);

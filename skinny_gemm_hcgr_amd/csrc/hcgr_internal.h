@@ -7,7 +7,7 @@
 // contract a stretch of one stream before that stream's RMS is known and
 // scale the partial once the stream's sum of squares is complete.
 //
-// Three plans, chosen by the token count M (make_plan):
+// Four plans, chosen by the token count M (make_plan):
 //   SPLIT  (decode sizes). Weight streaming over every CU:
 //     K1  hcgr_k1_dec     COMBINE + sums of squares + unscaled partials P for a
 //                         (token tile, K chunk inside one stream, row tile)
@@ -15,7 +15,14 @@
 //                         scales, SiLU(./HC) -> h (workspace), inj_next
 //     K2  hcgr_k2_up_mix  up contraction on MFMA tiles whose 16 rows are
 //                         4 channels x 4 streams; sigmoid + MIX in registers
-//   STREAM (mid sizes) and FULL (large sizes). Activation streaming:
+//   TILE (large sizes). Activation streaming with LDS-staged weights:
+//     K1  hcgr_k1_tile    a workgroup owns 64 tokens and every down/inject
+//                         row (or a row split); weights, R and y arrive in
+//                         LDS by direct global->LDS loads, 2-3 stages deep;
+//                         four streams per workgroup (h and inj_next out) or
+//                         one (rrms_s * P_s out, summed by hcgr_k1_sum)
+//     K2  hcgr_k2_tile    as below
+//   STREAM (mid sizes) and FULL. Activation streaming:
 //     K1  hcgr_k1_full    a workgroup owns a token tile and every down/inject
 //                         row (or a row split) and runs over one stream
 //                         (STREAM) or all four (FULL) with two accumulator
@@ -35,7 +42,7 @@
 
 namespace hcgr {
 
-enum PlanKind { PLAN_SPLIT = 0, PLAN_STREAM = 1, PLAN_FULL = 2 };
+enum PlanKind { PLAN_SPLIT = 0, PLAN_STREAM = 1, PLAN_FULL = 2, PLAN_TILE = 3 };
 
 // SPLIT-plan down kernel variants: token tile, 16-row blocks per workgroup,
 // waves splitting each block's k range, columns per chunk.
@@ -116,6 +123,12 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest M served by the SPLIT plan.
 constexpr int64_t kSplitMaxM = 64;
+// TILE plan: 64-token down kernel (hcgr_k1_tile) with at most 24 16-row
+// blocks per workgroup (4 row quarters of 6); taken with one stream per workgroup from kTileMinM
+// tokens, with all four once the token tiles alone fill the chip.
+constexpr int64_t kTileTm = 64;
+constexpr int kTileMaxBlk = 24;
+constexpr int64_t kTileMinM = 8192;
 
 // SPLIT plan with down-kernel variant kd; false when the stream width does
 // not split into chunks of the variant (the caller then takes another plan).
@@ -155,8 +168,25 @@ inline Plan make_plan(const Shape& s, int64_t M) {
     const int kd_wide = M <= 16 ? KD_T16_R3_K2_C512 : M <= 32 ? KD_T32_R3_K2_C512 : KD_T64_R3_K1_C256;
     if (make_split(s, M, kd, &p) || make_split(s, M, kd_wide, &p)) return p;
   }
-  // STREAM / FULL: aim for at least one down workgroup per CU (256 CUs)
+  // STREAM / FULL / TILE: aim for at least one down workgroup per CU (256 CUs)
   const int64_t target = 256;
+  const int64_t tiles = cdiv(M, kTileTm);
+  const int tsplit = (int)cdiv(s.nblk(), kTileMaxBlk);  // row splits of the tile down kernel
+  if (tiles * tsplit >= target || (M >= kTileMinM && tiles * 4 * tsplit >= target)) {
+    p.kind = PLAN_TILE;
+    p.spw = tiles * tsplit >= target ? 4 : 1;
+    p.nsplit = tsplit;
+    p.kt = KT_T64;
+    p.tm = kTileTm;
+    const int tm2 = kt_shape(p.kt).tm;
+    p.mpad = cdiv(M, tm2) * tm2;
+    p.mq = tiles * kTileTm;
+    p.off_h = 0;
+    p.off_q = align256((size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
+    p.ws_bytes = p.off_q;
+    if (p.spw == 1) p.ws_bytes = align256(p.off_q + (size_t)s.hc * (size_t)p.mq * np * sizeof(float));
+    return p;
+  }
   const KFShape f64 = kf_shape(KF_T64);
   const int nmin = (int)cdiv(s.nblk(), (int64_t)f64.nw * f64.bpw);  // row splits the blocks need
   if (cdiv(M, 64) * nmin >= target) {

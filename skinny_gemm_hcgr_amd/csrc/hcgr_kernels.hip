@@ -42,6 +42,7 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 // Buffer resource over [base, base + bytes): loads past the range return 0
 // and stores past it are dropped. Word 3 (0x00020000) is the 32-bit data
 // format that gfx9-family raw buffer descriptors use.
@@ -780,6 +781,347 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_full(FullArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// hcgr_k1_tile (large token counts): COMBINE + N + down/inject contraction
+// for a tile of TM = 64 tokens, with every operand staged through LDS by
+// direct global->LDS loads (buffer_load ... lds, 8 rows x 128 bytes per wave
+// instruction).
+// Workgroup = (token tile) x (row split: 16-row blocks [b0, b1), at most 24)
+// x (stream group: SPW = 4 streams, or SPW = 1 stream whose rrms-scaled
+// partial goes to the workspace). Eight waves, two per SIMD: wave (rq, th)
+// owns row quarter rq of the blocks (at most 6) and token half th (two MFMA
+// column blocks of 16 tokens).
+// A stage is 64 columns of k, one 128-byte line per matrix row. Weight
+// stages are double buffered and R/y stages triple buffered: while stage i
+// is combined and contracted, the weights of stage i+1 and the R/y rows of
+// stages i+1 and i+2 are in flight. Four waves load only R/y and four only
+// weights, each the same count every stage, so the wait at the top of a
+// stage names an exact count and never waits for HBM on behalf of weights. Inside each 128-byte LDS row the 16-byte chunk c of row t
+// sits in slot c ^ (t & 7), which spreads MFMA fragment reads (16 rows, one
+// chunk) over the banks. COMBINE reads R/y from LDS, stores R2 to HBM and
+// writes the bf16 activation R2*(1+Wnorm) over R in place; the MFMA step
+// reads weight (A) and activation (B) fragments from LDS. Streams are the
+// outer loop: at a stream end the stream's sum of squares gives rrms and,
+// with SPW = 4, the stream accumulator is folded into the rrms-scaled total.
+// ---------------------------------------------------------------------------
+struct Tile1Args {
+  const uint16_t* R;
+  const uint16_t* y;
+  const uint16_t* inj;
+  int64_t ld_inj;
+  const uint16_t* wn;
+  int wn_len;
+  int folded;
+  const uint16_t* w0;  // down rows: Wd [r,K], or rows 0..r-1 of Wm
+  const uint16_t* w1;  // inject rows: Wi [HC,K], or rows r..r+HC-1 of Wm
+  int64_t M;
+  int K, HS, HC, r, nblk, nsplit;
+  float eps, inv_hc, inv_hs;
+  uint16_t* R2;
+  float* rrms;
+  uint16_t* h;  // [>= M, r]        (SPW = 4)
+  uint16_t* inj_next;
+  int64_t ld_inj_next;
+  float* Q;  // [HC][Mq][NP] rrms-scaled per-stream partials (SPW = 1)
+  int64_t Mq;
+  int NP;
+};
+
+template <int SPW>
+__global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
+  constexpr int TM = (int)kTileTm, NT = 512, BPW = kTileMaxBlk / 4, NTB = 2;
+  constexpr int WGRP = kTileMaxBlk * 2 / 4;  // 8-row weight groups per loading wave per stage
+  // R/y stage buffer: R rows, y rows, then the stage's 64 Wnorm values (1 KB slot)
+  constexpr int WBYTES = kTileMaxBlk * 16 * 128, ABYTES = TM * 128, RYB = 2 * ABYTES + 1024;
+  constexpr int NSET = SPW == 4 ? 1 : 0;  // rrms-scaled total kept in registers
+  static_assert(TM == 64 && NTB == 2 && BPW * 4 == kTileMaxBlk && WGRP * 4 == 2 * kTileMaxBlk, "tile shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t w_0[WBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t w_1[WBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ry[3 * RYB];
+  __shared__ float iwh[SPW][TM], iwl[SPW][TM], rrs[SPW][TM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rq = wave & 3, th = wave >> 2;
+  constexpr int NG = 4 / SPW;
+  const int sg = (int)(blockIdx.x % NG);
+  const int split = (int)((blockIdx.x / NG) % a.nsplit);
+  const int64_t m0 = (int64_t)(blockIdx.x / (NG * a.nsplit)) * TM;
+  const int rows = (int)min((int64_t)TM, a.M - m0);
+  const int s_first = sg * SPW;
+  const int b0 = split * a.nblk / a.nsplit, b1 = (split + 1) * a.nblk / a.nsplit;
+  const int nbw = b1 - b0;
+  const int qb0 = rq * nbw / 4;                 // first block of this wave, relative to b0
+  const int wcnt = (rq + 1) * nbw / 4 - qb0;    // blocks of this wave (<= BPW)
+  const bool lead = split == 0;
+  const int HS = a.HS;
+  const uint32_t rowb = (uint32_t)a.K * 2u;
+
+  const rsrc_t rR = make_rsrc(a.R + m0 * a.K, (uint32_t)rows * rowb);
+  const rsrc_t rY = make_rsrc(a.y + m0 * HS, (uint32_t)rows * (uint32_t)HS * 2u);
+  const rsrc_t rWn = make_rsrc(a.wn, a.folded ? 0u : (uint32_t)a.wn_len * 2u);  // folded: reads 0 -> factor 1
+  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, lead ? (uint32_t)rows * rowb : 0u);
+  const rsrc_t rW0 = make_rsrc(a.w0, (uint32_t)a.r * rowb);
+  const rsrc_t rW1 = make_rsrc(a.w1, (uint32_t)a.HC * rowb);  // rows past HC read as zero
+
+  // (COMBINE) iw = 2*sigmoid(inj/HC) in fp64, kept as fp32 hi + lo
+  for (int i = tid; i < SPW * TM; i += NT) {
+    const int sl = i / TM, t = i % TM;
+    double v = 0.0;
+    if (t < rows) v = 2.0 / (1.0 + exp(-(double)bf1(a.inj[(m0 + t) * a.ld_inj + s_first + sl]) / (double)a.HC));
+    const float hi = (float)v;
+    iwh[sl][t] = hi;
+    iwl[sl][t] = (float)(v - (double)hi);
+  }
+
+  // chunk this lane moves inside its 128-byte row (rows t with t & 7 == lane >> 3)
+  const uint32_t swz = (uint32_t)((lane & 7) ^ (lane >> 3));
+  const uint32_t grow = (uint32_t)(lane >> 3);  // row inside an 8-row group
+  // Loads are split by kind so that no wait for an L2-resident weight stage
+  // queues behind R/y rows coming from HBM (a wave's loads complete in issue
+  // order): waves 0-3 load R and y (8-token groups lw and lw + 4 of each),
+  // waves 4-7 load weights (8-row groups g = lw + 4 j).
+  const bool wloader = wave >= 4;
+  const int lw = wave & 3;
+  uint32_t woff[WGRP];
+  uint32_t winj = 0;  // bit j: group j holds inject rows
+#pragma unroll
+  for (int j = 0; j < WGRP; ++j) {
+    const int g = lw + 4 * j;
+    const int n = b0 * 16 + g * 8;  // r is a multiple of 8, so a group never straddles r
+    const bool down = n < a.r;
+    woff[j] = g < 2 * nbw ? (uint32_t)((down ? n : n - a.r) + (int)grow) * rowb + swz * 16u : 0x80000000u;
+    if (!down) winj |= 1u << j;
+  }
+  winj = __builtin_amdgcn_readfirstlane(winj);
+  const uint32_t tR = (uint32_t)(lw * 8) + grow;  // token row this lane loads (groups lw and lw + 4)
+  const uint32_t offR = tR * rowb + swz * 16u, offY = tR * (uint32_t)HS * 2u + swz * 16u;
+  const uint32_t wnc = a.folded ? 0u : (a.wn_len == HS ? 0u : 1u);  // Wnorm indexed by k
+  const uint32_t wn_lane = lane < 8 ? (uint32_t)lane * 16u : 0x80000000u;  // 8 lanes x 16 bytes = 64 values
+
+  auto issue_w = [&](int s, int c0, uint8_t* wbuf) {
+    const uint32_t kb = (uint32_t)(s * HS + c0) * 2u;
+    if (!wloader) return;
+#pragma unroll
+    for (int j = 0; j < WGRP; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((winj >> j) & 1u ? rW1 : rW0,
+                                               (lds_void_t*)(wbuf + (lw + 4 * j) * 1024), 16, woff[j] + kb, 0, 0, 0);
+  };
+  auto issue_ry = [&](int s, int c0, int b) {
+    if (wloader) return;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint8_t* base = ry + b * RYB + (lw + 4 * j) * 1024;
+      const uint32_t tb = (uint32_t)(32 * j);  // + 4 groups of 8 tokens
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rR, (lds_void_t*)base, 16, offR + tb * rowb + (uint32_t)(s * HS + c0) * 2u,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rY, (lds_void_t*)(base + ABYTES), 16,
+                                               offY + tb * (uint32_t)HS * 2u + (uint32_t)c0 * 2u, 0, 0, 0);
+    }
+    if (lw == 0)  // the stage's Wnorm values (folded weights: a zero-length range, so 0 and a factor of 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rWn, (lds_void_t*)(ry + b * RYB + 2 * ABYTES), 16,
+                                               wn_lane + ((wnc ? (uint32_t)(s * HS) : 0u) + (uint32_t)c0) * 2u, 0, 0, 0);
+  };
+
+  // COMBINE chunk of this thread: token tid >> 3, LDS slot tid & 7
+  const int tok = tid >> 3;
+  const uint32_t la_off = (uint32_t)(tok * 128 + (tid & 7) * 16);
+  const uint32_t ry_lds = (uint32_t)(uintptr_t)(lds_u8_t*)ry;
+  float ss = 0.0f, ih = 0.0f, il = 0.0f;
+  auto combine = [&](int s, int c0, int b) {
+    // R, y and Wnorm chunks in one block of LDS reads. The stage wait already
+    // covers their global->LDS loads; reading them in asm keeps the compiler
+    // from adding a wait for the loads of later stages into the other buffers.
+    const uint32_t la = ry_lds + (uint32_t)(b * RYB) + la_off;
+    const uint32_t lwn = ry_lds + (uint32_t)(b * RYB + 2 * ABYTES) + swz * 16u;
+    u32x4_t rq4, yq4, wq4;
+    asm volatile(
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b128 %1, %3 offset:8192\n\t"
+        "ds_read_b128 %2, %4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(rq4), "=&v"(yq4), "=&v"(wq4)  // early clobber: results return while later reads still need la
+        : "v"(la), "v"(lwn)
+        : "memory");
+    const uint32_t ww[4] = {wq4[0], wq4[1], wq4[2], wq4[3]};
+    static_assert(ABYTES == 8192, "offset above");
+    uint32_t o2[4], ou[4];
+    float acc = ss;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float r0 = fmaf(bf_lo(yq4[e]), il, fmaf(bf_lo(yq4[e]), ih, bf_lo(rq4[e])));
+      const float r1 = fmaf(bf_hi(yq4[e]), il, fmaf(bf_hi(yq4[e]), ih, bf_hi(rq4[e])));
+      acc = fmaf(r0, r0, acc);
+      acc = fmaf(r1, r1, acc);
+      o2[e] = pack_bf2(r0, r1);
+      ou[e] = pack_bf2(r0 * (1.0f + bf_lo(ww[e])), r1 * (1.0f + bf_hi(ww[e])));
+    }
+    ss = acc;
+    bst16(rR2, (uint32_t)tok * rowb + (uint32_t)(s * HS + c0) * 2u + swz * 16u, make_uint4(o2[0], o2[1], o2[2], o2[3]));
+    const u32x4_t ov = {ou[0], ou[1], ou[2], ou[3]};
+    asm volatile("ds_write_b128 %0, %1" : : "v"(la), "v"(ov) : "memory");  // activation over R in place
+  };
+
+  f32x4_t acc_s[BPW][NTB];
+  f32x4_t acc_t[NSET ? BPW : 1][NSET ? NTB : 1];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i)
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) acc_s[i][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (NSET) {
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) acc_t[i][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // (G1, INJ) contraction of one stage: A = weight rows, B = activation
+  const uint32_t bfr_off = (uint32_t)((th * (TM / 2) + (lane & 15)) * 128);
+  auto contract = [&](const uint8_t* wbuf, int b) {
+    // activation fragments of both k halves in one block of LDS reads (asm,
+    // for the reason given in COMBINE)
+    u32x4_t bq[2][NTB];
+    const uint32_t ba = ry_lds + (uint32_t)(b * RYB) + bfr_off;
+    const uint32_t b0a = ba + (uint32_t)((((lane >> 4)) ^ (lane & 7)) * 16);
+    const uint32_t b1a = ba + (uint32_t)(((4 + (lane >> 4)) ^ (lane & 7)) * 16);
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:2048\n\t"
+        "ds_read_b128 %2, %5\n\t"
+        "ds_read_b128 %3, %5 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(bq[0][0]), "=&v"(bq[0][1]), "=&v"(bq[1][0]), "=&v"(bq[1][1])  // early clobber, as in COMBINE
+        : "v"(b0a), "v"(b1a)
+        : "memory");
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int slot = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {  // blocks past wcnt compute unused values (qb0 + i < kTileMaxBlk)
+        const uint4 af = *reinterpret_cast<const uint4*>(wbuf + ((qb0 + i) * 16 + (lane & 15)) * 128 + slot);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+          acc_s[i][tb] = mfma16(af, __builtin_bit_cast(uint4, bq[ks][tb]), acc_s[i][tb]);
+      }
+    }
+  };
+
+  // Stage parameters: (s, c) of the current stage and the next two (past the
+  // last stage they stay on it: the extra loads reload it into free buffers).
+  const int s_last = s_first + SPW - 1;
+  auto advance = [&](int& s, int& c) {
+    if (c + 64 < HS) c += 64;
+    else if (s < s_last) { c = 0; ++s; }
+  };
+  int s1 = s_first, c1 = 0, s2 = s_first, c2 = 0;
+  advance(s1, c1);
+  advance(s2, c2);
+  advance(s2, c2);
+  int bcur = 0;  // R/y buffer of the current stage
+
+  // One stage. On entry a weight wave may have in flight this stage's
+  // weights and the R2 store of the previous stage; an R/y wave the R/y (and,
+  // wave 0, Wnorm) loads of this stage and of the next one, in issue order,
+  // and R2 stores. Loads complete in issue order but a store may complete
+  // before earlier loads, so a wait counts loads only: weight waves wait for
+  // everything, R/y waves for all but the next stage's loads (4, wave 0: 5).
+  auto stage = [&](int s, int c0, uint8_t* wc, uint8_t* wnx) {
+    if (wloader) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (lw == 0) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    lds_sync();  // every wave's loads of this stage have landed; the previous stage is fully consumed
+    issue_w(s1, c1, wnx);
+    const int bnx = bcur == 0 ? 2 : bcur - 1;  // (stage + 2) % 3
+    issue_ry(s2, c2, bnx);
+    combine(s, c0, bcur);
+    lds_sync();
+    contract(wc, bcur);
+    bcur = bcur == 2 ? 0 : bcur + 1;
+    s1 = s2; c1 = c2;
+    advance(s2, c2);
+  };
+
+  issue_w(s_first, 0, w_0);
+  issue_ry(s_first, 0, 0);
+  issue_ry(s1, c1, 1);
+  for (int sl = 0; sl < SPW; ++sl) {
+    const int s = s_first + sl;
+    for (int c0 = 0; c0 < HS; c0 += 128) {  // stages in pairs: weights alternate w_0, w_1
+      if (c0 == 0) {  // iw of this thread's token for the stream (written before the first barrier)
+        lds_sync();
+        ih = iwh[sl][tok];
+        il = iwl[sl][tok];
+      }
+      stage(s, c0, w_0, w_1);
+      stage(s, c0 + 64, w_1, w_0);
+    }
+    // (N) stream end: rrms per token from the stream's sum of squares
+    float v = ss;
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    ss = 0.0f;
+    if ((tid & 7) == 0) rrs[sl][tok] = 1.0f / sqrtf(v * a.inv_hs + a.eps);
+    lds_sync();
+    if constexpr (NSET) {
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        const float rr = rrs[sl][th * (TM / 2) + tb * 16 + (lane & 15)];
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc_t[i][tb][q] = fmaf(rr, acc_s[i][tb][q], acc_t[i][tb][q]);
+          acc_s[i][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+      }
+    }
+  }
+  // the loads issued past the last stage must land before the LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (lead)
+    for (int i = tid; i < SPW * TM; i += NT) {
+      const int sl = i / TM, t = i % TM;
+      if (t < rows) a.rrms[(m0 + t) * 4 + s_first + sl] = rrs[sl][t];
+    }
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    if (i >= wcnt) continue;
+    const int n0 = (b0 + qb0 + i) * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const int t = th * (TM / 2) + tb * 16 + (lane & 15);
+      if (t >= rows) continue;
+      const int64_t m = m0 + t;
+      if constexpr (NSET) {
+        const f32x4_t v = acc_t[i][tb];
+        if (n0 < a.r) {
+          float z[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) z[q] = v[q] * a.inv_hc;
+          uint2 o;
+          o.x = pack_bf2(z[0] * sigmoid_f(z[0]), z[1] * sigmoid_f(z[1]));  // (G1) SiLU(lora / HC)
+          o.y = pack_bf2(z[2] * sigmoid_f(z[2]), z[3] * sigmoid_f(z[3]));
+          *reinterpret_cast<uint2*>(a.h + m * a.r + n0) = o;
+        } else if (n0 < a.r + a.HC) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n0 + q < a.r + a.HC) a.inj_next[m * a.ld_inj_next + (n0 - a.r + q)] = to_bf(v[q]);  // (INJ)
+        }
+      } else {
+        const float rr = rrs[0][t];
+        if (n0 < a.r + a.HC) {
+          f32x4_t v = acc_s[i][tb];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] *= rr;
+          *reinterpret_cast<f32x4_t*>(a.Q + ((int64_t)s_first * a.Mq + m) * a.NP + n0) = v;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // hcgr_k1_sum (STREAM plan): v = sum_s rrms_s P_s for each token and row;
 // down rows -> h = SiLU(v/HC) (bf16), inject rows -> inj_next. One thread per
 // (token, 8 consecutive rows).
@@ -1137,6 +1479,19 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   const int K = (int)s.k();
   const KFShape fs = kf_shape(p.kf);
 
+  if (p.kind == PLAN_TILE) {
+    Tile1Args a;
+    a.R = f.R; a.y = f.y; a.inj = f.inj; a.ld_inj = f.ld_inj;
+    a.wn = f.wnorm; a.wn_len = s.wn_full ? K : s.hs; a.folded = s.merged ? 1 : 0;
+    a.w0 = f.wd; a.w1 = s.merged ? f.wd + (size_t)s.r * (size_t)K : f.wi;
+    a.M = f.M; a.K = K; a.HS = s.hs; a.HC = s.hc; a.r = s.r; a.nblk = s.nblk(); a.nsplit = p.nsplit;
+    a.eps = s.eps; a.inv_hc = 1.0f / (float)s.hc; a.inv_hs = 1.0f / (float)s.hs;
+    a.R2 = f.R2; a.rrms = f.rrms; a.h = H; a.inj_next = f.inj_next; a.ld_inj_next = f.ld_inj_next;
+    a.Q = Q; a.Mq = p.mq; a.NP = s.np();
+    const dim3 g1((unsigned)(cdiv(f.M, kTileTm) * p.nsplit * (4 / p.spw)));
+    if (p.spw == 4) hipLaunchKernelGGL(hcgr_k1_tile<4>, g1, dim3(512), 0, st, a);
+    else hipLaunchKernelGGL(hcgr_k1_tile<1>, g1, dim3(512), 0, st, a);
+  } else {
   FullArgs a;
   a.R = f.R; a.y = f.y; a.inj = f.inj; a.ld_inj = f.ld_inj;
   a.wn = f.wnorm; a.wn_len = s.wn_full ? K : s.hs;
@@ -1151,9 +1506,10 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     case KF_T32: launch_kf<32, 8, 3, 128>(a, g1, st); break;
     default: launch_kf<64, 8, 3, 64>(a, g1, st); break;
   }
+  }
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return (int)e;
 
-  if (p.kind == PLAN_STREAM) {
+  if (p.kind == PLAN_STREAM || (p.kind == PLAN_TILE && p.spw == 1)) {
     SumArgs sa;
     sa.Q = Q; sa.Mq = p.mq; sa.M = f.M; sa.NP = s.np(); sa.r = s.r; sa.n_rows = s.n_rows();
     sa.inv_hc = 1.0f / (float)s.hc; sa.h = H; sa.inj_next = f.inj_next; sa.ld_inj_next = f.ld_inj_next;

@@ -145,6 +145,39 @@ def test_strided_injection_and_layer_chaining(op, weights):
     check_all(out2, run_oracle(inp2))
 
 
+@pytest.mark.parametrize("hs,r,M", [(1024, 512, 16384), (640, 64, 8192), (2560, 320, 16420)])
+def test_tile_plan_shapes(H, hs, r, M):
+    """Large-M down kernel on other shapes: r = 512 (33 row blocks, two row
+    splits per token tile), a short stream (HS = 640: 10 stages, a partial
+    trip of the 6-stage loop) with one stream per workgroup, and a token count
+    whose last tile is partial."""
+    shape = synth.Shape(hs=hs, r=r)
+    o = H.HCGR(H.Config(hs=hs, r=r), 0)
+    plan = H.hcgr_describe_plan(o.cfg, M)
+    _say(f"[parity] tile shapes hs={hs} r={r} M={M}: {plan}")
+    assert "plan=tile" in plan
+    inp = synth.make_inputs(M, shape, seed=11, device="cuda")
+    out = gpu_forward(o, inp)
+    rows = sample_rows(M, 64)
+    cfg = oracle.OracleConfig(hs=hs, r=r)
+    idx = torch.as_tensor(rows, device="cuda")
+    ref = oracle.forward(cfg, inp["R"][idx].cpu(), inp["y"][idx].cpu(), inp["inj"][idx].cpu(), inp["wnorm"].cpu(),
+                         inp["wd"].cpu(), inp["wi"].cpu(), inp["wu"].cpu())
+    check_all(out, ref, rows)
+    o.close()
+
+
+def test_full_width_wnorm_large(H):
+    """Wnorm indexed by k (length HC*HS) on the large-M path."""
+    o = H.HCGR(H.Config(wnorm_len=SHAPE.k), 0)
+    M = 16384
+    inp = synth.make_inputs(M, SHAPE, seed=12, device="cuda", wnorm_full=True)
+    out = gpu_forward(o, inp)
+    rows = sample_rows(M, 48)
+    check_all(out, run_oracle(inp, rows, wnorm_full=True), rows)
+    o.close()
+
+
 def test_full_width_wnorm(H):
     o = H.HCGR(H.Config(wnorm_len=SHAPE.k), 0)
     inp = synth.make_inputs(40, SHAPE, seed=5, device="cuda", wnorm_full=True)
