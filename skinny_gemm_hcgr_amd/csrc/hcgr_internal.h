@@ -123,12 +123,12 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest M served by the SPLIT plan.
 constexpr int64_t kSplitMaxM = 64;
-// TILE plan: 64-token down kernel (hcgr_k1_tile) with at most 24 16-row
-// blocks per workgroup (4 row quarters of 6); taken with one stream per workgroup from kTileMinM
+// TILE plan: 64-token down kernel (hcgr_k1_tile) with at most 22 16-row
+// blocks per workgroup (4 row quarters of at most 6); taken with one stream per workgroup from kTileMinM
 // tokens, with all four once the token tiles alone fill the chip.
 constexpr int64_t kTileTm = 64;
-constexpr int kTileMaxBlk = 24;
-constexpr int64_t kTileMinM = 8192;
+constexpr int kTileMaxBlk = 22;
+constexpr int64_t kTileMinM = 4096;
 
 // SPLIT plan with down-kernel variant kd; false when the stream width does
 // not split into chunks of the variant (the caller then takes another plan).

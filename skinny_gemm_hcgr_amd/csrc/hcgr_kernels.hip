@@ -785,23 +785,27 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_full(FullArgs a) {
 // for a tile of TM = 64 tokens, with every operand staged through LDS by
 // direct global->LDS loads (buffer_load ... lds, 8 rows x 128 bytes per wave
 // instruction).
-// Workgroup = (token tile) x (row split: 16-row blocks [b0, b1), at most 24)
+// Workgroup = (token tile) x (row split: 16-row blocks [b0, b1), at most 22)
 // x (stream group: SPW = 4 streams, or SPW = 1 stream whose rrms-scaled
 // partial goes to the workspace). Eight waves, two per SIMD: wave (rq, th)
 // owns row quarter rq of the blocks (at most 6) and token half th (two MFMA
 // column blocks of 16 tokens).
-// A stage is 64 columns of k, one 128-byte line per matrix row. Weight
-// stages are double buffered and R/y stages triple buffered: while stage i
-// is combined and contracted, the weights of stage i+1 and the R/y rows of
-// stages i+1 and i+2 are in flight. Four waves load only R/y and four only
-// weights, each the same count every stage, so the wait at the top of a
-// stage names an exact count and never waits for HBM on behalf of weights. Inside each 128-byte LDS row the 16-byte chunk c of row t
-// sits in slot c ^ (t & 7), which spreads MFMA fragment reads (16 rows, one
-// chunk) over the banks. COMBINE reads R/y from LDS, stores R2 to HBM and
-// writes the bf16 activation R2*(1+Wnorm) over R in place; the MFMA step
-// reads weight (A) and activation (B) fragments from LDS. Streams are the
-// outer loop: at a stream end the stream's sum of squares gives rrms and,
-// with SPW = 4, the stream accumulator is folded into the rrms-scaled total.
+// A stage is 64 columns of k, one 128-byte line per matrix row. The loop is
+// software pipelined with one barrier per iteration: iteration i contracts
+// stage i (weights and activation from LDS into v_mfma_f32_16x16x32_bf16)
+// while it combines stage i+1 (R and y from LDS -> R2 to HBM, bf16
+// activation R2*(1+Wnorm) written over R in place), so the VALU work of one
+// may overlap the matrix and LDS work of the other. Weights are double
+// buffered (stage i+1 loads during iteration i) and R/y/Wnorm use a ring of
+// four (stage i+3 loads during iteration i). Waves 0-3 issue only R/y
+// loads and waves 4-7 only weight loads: a wave's loads complete in issue
+// order, so a weight wait never queues behind HBM misses, and each wave
+// issues a fixed count per stage, so the wait at the top of an iteration
+// names an exact count. Inside each 128-byte LDS row the 16-byte chunk c of
+// row t sits in slot c ^ (t & 7), which spreads MFMA fragment reads (16
+// rows, one chunk) over the banks. At each stream end the stream's sum of
+// squares gives rrms and, with SPW = 4, the stream accumulator is folded
+// into the rrms-scaled total (two accumulator sets).
 // ---------------------------------------------------------------------------
 struct Tile1Args {
   const uint16_t* R;
@@ -828,15 +832,16 @@ struct Tile1Args {
 
 template <int SPW>
 __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
-  constexpr int TM = (int)kTileTm, NT = 512, BPW = kTileMaxBlk / 4, NTB = 2;
+  constexpr int TM = (int)kTileTm, NT = 512, BPW = 6, NTB = 2, NRY = 4;
   constexpr int WGRP = kTileMaxBlk * 2 / 4;  // 8-row weight groups per loading wave per stage
   // R/y stage buffer: R rows, y rows, then the stage's 64 Wnorm values (1 KB slot)
   constexpr int WBYTES = kTileMaxBlk * 16 * 128, ABYTES = TM * 128, RYB = 2 * ABYTES + 1024;
   constexpr int NSET = SPW == 4 ? 1 : 0;  // rrms-scaled total kept in registers
-  static_assert(TM == 64 && NTB == 2 && BPW * 4 == kTileMaxBlk && WGRP * 4 == 2 * kTileMaxBlk, "tile shape");
+  static_assert(TM == 64 && WGRP * 4 == 2 * kTileMaxBlk && (kTileMaxBlk * 3) / 4 + BPW <= kTileMaxBlk + 1,
+                "tile shape: every wave's blocks (read or not) lie inside the weight buffer");
   __shared__ __attribute__((aligned(1024))) uint8_t w_0[WBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t w_1[WBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t ry[3 * RYB];
+  __shared__ __attribute__((aligned(1024))) uint8_t ry[NRY * RYB];
   __shared__ float iwh[SPW][TM], iwl[SPW][TM], rrs[SPW][TM];
 
   const int tid = threadIdx.x;
@@ -851,10 +856,11 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   const int s_first = sg * SPW;
   const int b0 = split * a.nblk / a.nsplit, b1 = (split + 1) * a.nblk / a.nsplit;
   const int nbw = b1 - b0;
-  const int qb0 = rq * nbw / 4;                 // first block of this wave, relative to b0
-  const int wcnt = (rq + 1) * nbw / 4 - qb0;    // blocks of this wave (<= BPW)
+  const int qb0 = rq * nbw / 4;               // first block of this wave, relative to b0
+  const int wcnt = (rq + 1) * nbw / 4 - qb0;  // blocks of this wave (<= BPW)
   const bool lead = split == 0;
   const int HS = a.HS;
+  const int nst = SPW * (HS / 64);
   const uint32_t rowb = (uint32_t)a.K * 2u;
 
   const rsrc_t rR = make_rsrc(a.R + m0 * a.K, (uint32_t)rows * rowb);
@@ -877,10 +883,8 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   // chunk this lane moves inside its 128-byte row (rows t with t & 7 == lane >> 3)
   const uint32_t swz = (uint32_t)((lane & 7) ^ (lane >> 3));
   const uint32_t grow = (uint32_t)(lane >> 3);  // row inside an 8-row group
-  // Loads are split by kind so that no wait for an L2-resident weight stage
-  // queues behind R/y rows coming from HBM (a wave's loads complete in issue
-  // order): waves 0-3 load R and y (8-token groups lw and lw + 4 of each),
-  // waves 4-7 load weights (8-row groups g = lw + 4 j).
+  // waves 0-3 load R, y (8-token groups lw and lw + 4 of each) and, wave 0,
+  // Wnorm; waves 4-7 load weights (8-row groups g = lw + 4 j)
   const bool wloader = wave >= 4;
   const int lw = wave & 3;
   uint32_t woff[WGRP];
@@ -929,9 +933,10 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   const uint32_t ry_lds = (uint32_t)(uintptr_t)(lds_u8_t*)ry;
   float ss = 0.0f, ih = 0.0f, il = 0.0f;
   auto combine = [&](int s, int c0, int b) {
-    // R, y and Wnorm chunks in one block of LDS reads. The stage wait already
-    // covers their global->LDS loads; reading them in asm keeps the compiler
-    // from adding a wait for the loads of later stages into the other buffers.
+    // R, y and Wnorm chunks in one block of LDS reads. The iteration wait
+    // already covers their global->LDS loads; reading them in asm keeps the
+    // compiler from adding a wait for the loads of later stages into the
+    // other buffers.
     const uint32_t la = ry_lds + (uint32_t)(b * RYB) + la_off;
     const uint32_t lwn = ry_lds + (uint32_t)(b * RYB + 2 * ABYTES) + swz * 16u;
     u32x4_t rq4, yq4, wq4;
@@ -943,7 +948,6 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
         : "=&v"(rq4), "=&v"(yq4), "=&v"(wq4)  // early clobber: results return while later reads still need la
         : "v"(la), "v"(lwn)
         : "memory");
-    const uint32_t ww[4] = {wq4[0], wq4[1], wq4[2], wq4[3]};
     static_assert(ABYTES == 8192, "offset above");
     uint32_t o2[4], ou[4];
     float acc = ss;
@@ -954,12 +958,21 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
       acc = fmaf(r0, r0, acc);
       acc = fmaf(r1, r1, acc);
       o2[e] = pack_bf2(r0, r1);
-      ou[e] = pack_bf2(r0 * (1.0f + bf_lo(ww[e])), r1 * (1.0f + bf_hi(ww[e])));
+      ou[e] = pack_bf2(r0 * (1.0f + bf_lo(wq4[e])), r1 * (1.0f + bf_hi(wq4[e])));
     }
     ss = acc;
     bst16(rR2, (uint32_t)tok * rowb + (uint32_t)(s * HS + c0) * 2u + swz * 16u, make_uint4(o2[0], o2[1], o2[2], o2[3]));
     const u32x4_t ov = {ou[0], ou[1], ou[2], ou[3]};
     asm volatile("ds_write_b128 %0, %1" : : "v"(la), "v"(ov) : "memory");  // activation over R in place
+  };
+  // (N) the stream's sum of squares -> rrms of this thread's token
+  auto stream_rrms = [&](int sl) {
+    float v = ss;
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    ss = 0.0f;
+    if ((tid & 7) == 0) rrs[sl][tok] = 1.0f / sqrtf(v * a.inv_hs + a.eps);
   };
 
   f32x4_t acc_s[BPW][NTB];
@@ -997,7 +1010,7 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
     for (int ks = 0; ks < 2; ++ks) {
       const int slot = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) {  // blocks past wcnt compute unused values (qb0 + i < kTileMaxBlk)
+      for (int i = 0; i < BPW; ++i) {  // blocks past wcnt compute unused values (inside the buffer)
         const uint4 af = *reinterpret_cast<const uint4*>(wbuf + ((qb0 + i) * 16 + (lane & 15)) * 128 + slot);
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
@@ -1005,64 +1018,7 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
       }
     }
   };
-
-  // Stage parameters: (s, c) of the current stage and the next two (past the
-  // last stage they stay on it: the extra loads reload it into free buffers).
-  const int s_last = s_first + SPW - 1;
-  auto advance = [&](int& s, int& c) {
-    if (c + 64 < HS) c += 64;
-    else if (s < s_last) { c = 0; ++s; }
-  };
-  int s1 = s_first, c1 = 0, s2 = s_first, c2 = 0;
-  advance(s1, c1);
-  advance(s2, c2);
-  advance(s2, c2);
-  int bcur = 0;  // R/y buffer of the current stage
-
-  // One stage. On entry a weight wave may have in flight this stage's
-  // weights and the R2 store of the previous stage; an R/y wave the R/y (and,
-  // wave 0, Wnorm) loads of this stage and of the next one, in issue order,
-  // and R2 stores. Loads complete in issue order but a store may complete
-  // before earlier loads, so a wait counts loads only: weight waves wait for
-  // everything, R/y waves for all but the next stage's loads (4, wave 0: 5).
-  auto stage = [&](int s, int c0, uint8_t* wc, uint8_t* wnx) {
-    if (wloader) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (lw == 0) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    lds_sync();  // every wave's loads of this stage have landed; the previous stage is fully consumed
-    issue_w(s1, c1, wnx);
-    const int bnx = bcur == 0 ? 2 : bcur - 1;  // (stage + 2) % 3
-    issue_ry(s2, c2, bnx);
-    combine(s, c0, bcur);
-    lds_sync();
-    contract(wc, bcur);
-    bcur = bcur == 2 ? 0 : bcur + 1;
-    s1 = s2; c1 = c2;
-    advance(s2, c2);
-  };
-
-  issue_w(s_first, 0, w_0);
-  issue_ry(s_first, 0, 0);
-  issue_ry(s1, c1, 1);
-  for (int sl = 0; sl < SPW; ++sl) {
-    const int s = s_first + sl;
-    for (int c0 = 0; c0 < HS; c0 += 128) {  // stages in pairs: weights alternate w_0, w_1
-      if (c0 == 0) {  // iw of this thread's token for the stream (written before the first barrier)
-        lds_sync();
-        ih = iwh[sl][tok];
-        il = iwl[sl][tok];
-      }
-      stage(s, c0, w_0, w_1);
-      stage(s, c0 + 64, w_1, w_0);
-    }
-    // (N) stream end: rrms per token from the stream's sum of squares
-    float v = ss;
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    ss = 0.0f;
-    if ((tid & 7) == 0) rrs[sl][tok] = 1.0f / sqrtf(v * a.inv_hs + a.eps);
-    lds_sync();
+  auto fold = [&](int sl) {  // stream end: total += rrms_s * stream accumulator
     if constexpr (NSET) {
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
@@ -1075,9 +1031,73 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
         }
       }
     }
+  };
+
+  // Stage parameters (stream, column) of stages i+1 and i+3 (past the last
+  // stage they stay on it: those loads refill free buffers and are not used).
+  const int s_last = s_first + SPW - 1;
+  auto advance = [&](int& s, int& c) {
+    if (c + 64 < HS) c += 64;
+    else if (s < s_last) { c = 0; ++s; }
+  };
+  int s1 = s_first, c1 = 0, s2, c2, s3, c3;
+  advance(s1, c1);
+  s2 = s1; c2 = c1; advance(s2, c2);
+  s3 = s2; c3 = c2; advance(s3, c3);
+
+  // Iteration st. On entry a weight wave may have in flight the weights of
+  // stage st and R2 stores; an R/y wave the R/y (wave 0: and Wnorm) loads of
+  // stages st+1 and st+2, in issue order, and R2 stores. Loads complete in
+  // issue order but a store may complete before earlier loads, so a wait
+  // counts loads only: weight waves wait for everything, R/y waves for all
+  // but the loads of stage st+2 (4; wave 0: 5).
+  auto iteration = [&](int st, int s, int c0, uint8_t* wc, uint8_t* wnx) {
+    if (wloader) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (lw == 0) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    lds_sync();  // loads of stage st (weights) and st+1 (R/y) landed; iteration st-1 fully done
+    const int b = st & (NRY - 1);
+    issue_w(s1, c1, wnx);
+    issue_ry(s3, c3, (st + 3) & (NRY - 1));
+    if (st + 1 < nst) {
+      if (c1 == 0) {  // stage st+1 opens stream s1
+        ih = iwh[s1 - s_first][tok];
+        il = iwl[s1 - s_first][tok];
+      }
+      combine(s1, c1, (st + 1) & (NRY - 1));
+      if (c1 + 64 == HS) stream_rrms(s1 - s_first);  // stage st+1 closes stream s1
+    }
+    contract(wc, b);
+    if (c0 + 64 == HS) fold(s - s_first);  // stage st closed stream s (its rrms is visible since the barrier)
+    s1 = s2; c1 = c2;
+    s2 = s3; c2 = c3;
+    advance(s3, c3);
+  };
+
+  // prologue: weights of stage 0, R/y of stages 0-2; COMBINE of stage 0
+  issue_w(s_first, 0, w_0);
+  issue_ry(s_first, 0, 0);
+  issue_ry(s1, c1, 1);
+  issue_ry(s2, c2, 2);
+  if (!wloader) {
+    if (lw == 0) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  }
+  lds_sync();  // R/y of stage 0 and the iw table
+  ih = iwh[0][tok];
+  il = iwl[0][tok];
+  combine(s_first, 0, 0);
+  // iterations in pairs: weights alternate w_0, w_1 (nst is even)
+  int s = s_first, c0 = 0;
+  for (int st = 0; st < nst; st += 2) {
+    iteration(st, s, c0, w_0, w_1);
+    advance(s, c0);
+    iteration(st + 1, s, c0, w_1, w_0);
+    advance(s, c0);
   }
   // the loads issued past the last stage must land before the LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   if (lead)
     for (int i = tid; i < SPW * TM; i += NT) {
