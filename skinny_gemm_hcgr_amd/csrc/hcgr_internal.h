@@ -21,7 +21,7 @@
 //                         LDS by direct global->LDS loads, 2-3 stages deep;
 //                         four streams per workgroup (h and inj_next out) or
 //                         one (rrms_s * P_s out, summed by hcgr_k1_sum)
-//     K2  hcgr_k2_tile    as below
+//     K2  hcgr_k2_stage   as below
 //   STREAM (mid sizes) and FULL. Activation streaming:
 //     K1  hcgr_k1_full    a workgroup owns a token tile and every down/inject
 //                         row (or a row split) and runs over one stream
@@ -31,10 +31,10 @@
 //                         directly; STREAM writes rrms_s * P_s per stream
 //     K1s hcgr_k1_sum     (STREAM only) sums the four scaled partials,
 //                         SiLU(./HC) -> h, inj_next
-//     K2  hcgr_k2_tile    h . Wu^T on MFMA with h and Wu staged through LDS,
-//                         the R2 tile prefetched into LDS by direct
-//                         global->LDS loads during the contraction, and the
-//                         sigmoid + MIX epilogue in registers
+//     K2  hcgr_k2_stage   h . Wu^T on MFMA for 128 tokens x 32 channels with
+//                         h and Wu staged through LDS by direct global->LDS
+//                         loads, R2 and rrms in registers, and the sigmoid +
+//                         MIX epilogue in registers
 #pragma once
 
 #include <stddef.h>
@@ -82,10 +82,12 @@ inline KFShape kf_shape(int v) {
   return t[v];
 }
 // Tiled up kernel variants: token tile, channel tile (x 4 streams).
-enum KTVariant { KT_T64 = 0, KT_NVAR };
+// KT_T64: hcgr_k2_tile (register-staged operands); KT_S128: hcgr_k2_stage
+// (operands staged by direct global->LDS loads).
+enum KTVariant { KT_T64 = 0, KT_S128 = 1, KT_NVAR };
 struct KTShape { int tm, cb; };
 inline KTShape kt_shape(int v) {
-  static const KTShape t[KT_NVAR] = {{64, 64}};
+  static const KTShape t[KT_NVAR] = {{64, 64}, {128, 32}};
   return t[v];
 }
 
@@ -176,7 +178,7 @@ inline Plan make_plan(const Shape& s, int64_t M) {
     p.kind = PLAN_TILE;
     p.spw = tiles * tsplit >= target ? 4 : 1;
     p.nsplit = tsplit;
-    p.kt = KT_T64;
+    p.kt = KT_S128;
     p.tm = kTileTm;
     const int tm2 = kt_shape(p.kt).tm;
     p.mpad = cdiv(M, tm2) * tm2;
@@ -206,7 +208,7 @@ inline Plan make_plan(const Shape& s, int64_t M) {
     p.nsplit = nmin;
     while (cdiv(M, 32) * p.nsplit < target && p.nsplit * 2 <= s.nblk()) p.nsplit *= 2;
   }
-  p.kt = KT_T64;
+  p.kt = KT_S128;
   const int tm1 = kf_shape(p.kf).tm, tm2 = kt_shape(p.kt).tm;
   p.tm = tm1;
   p.mpad = cdiv(M, tm2) * tm2;  // h rows the up kernel may read

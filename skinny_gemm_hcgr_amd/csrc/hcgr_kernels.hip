@@ -1396,6 +1396,198 @@ __global__ __launch_bounds__(256) void hcgr_k2_tile(TileArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// hcgr_k2_stage: (G2) + (MIX) for a tile of 128 tokens x 32 channels (x 4
+// streams = 128 gate columns), 4 waves; wave (ch, th) owns channels ch*16..
+// and tokens th*64.. as 4 x 4 MFMA tiles (A = Wu rows, B = h rows). h and Wu
+// stream through LDS in stages of 64 k (one 128-byte line per row) by direct
+// global->LDS loads, double buffered (64 KB per workgroup, so two workgroups
+// share a CU and one's waits overlap the other's work). Fragment reads are
+// batched asm blocks (every LDS read they make is covered by the stage
+// wait). Inside a 16-row MFMA block, row 4j+s is stream s of channel 4j+gb
+// of the wave's block gb, so lane l ends with the 4 streams of channels
+// 4*(l/16)+gb, gb = 0..3, of token l%16: the MIX sum over streams is
+// lane-local and each lane moves 8 contiguous bytes of R2 and x per stream
+// and token. R2 and rrms go to registers once the first two stages are in
+// flight. Workgroups b and b+8 (the same XCD) take the two 32-channel halves
+// of a 64-channel group, so the second half of every 128-byte R2 line is an
+// L2 hit, and each XCD sees a fixed subset of channel groups (their Wu
+// slices stay in its L2).
+// ---------------------------------------------------------------------------
+struct StageArgs {
+  const uint16_t* h;  // [>= M, r]
+  int64_t M;
+  int r, HS, K;
+  const uint16_t* wu;
+  const uint16_t* R2;
+  const float* rrms;
+  const uint16_t* wn;
+  int wn_len;
+  uint16_t* x;
+  int npairs;  // 64-channel groups (HS / 64)
+};
+
+__global__ __launch_bounds__(256, 2) void hcgr_k2_stage(StageArgs a) {
+  constexpr int TM = 128, CG = 32, SB = 16384;  // tokens, channels per workgroup, bytes per h (or Wu) stage
+  __shared__ __attribute__((aligned(1024))) uint8_t hb_0[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t hb_1[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t wb_0[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t wb_1[SB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ch = wave & 1, th = wave >> 1;
+  // workgroup -> (token tile, 32-channel group): b and b + 8 share a 64-channel pair
+  const int b = (int)blockIdx.x;
+  const int pair_idx = (b >> 4) * 8 + (b & 7);  // token tile major, 64-channel pair minor
+  const int half = (b >> 3) & 1;
+  const int64_t tile = pair_idx / a.npairs;
+  const int c0 = (pair_idx % a.npairs) * 64 + half * CG;
+  const int64_t m0 = tile * TM;
+  if (m0 >= a.M) return;  // grid rounded up to 16 workgroups
+  const int rows = (int)min((int64_t)TM, a.M - m0);
+  const uint32_t rowb = (uint32_t)a.K * 2u, hrow = (uint32_t)a.r * 2u;
+  const int nstage = (a.r + 63) / 64;
+
+  const rsrc_t rH = make_rsrc(a.h + m0 * a.r, (uint32_t)rows * hrow);
+  const rsrc_t rWu = make_rsrc(a.wu, (uint32_t)a.K * hrow);
+  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, (uint32_t)rows * rowb);
+  const rsrc_t rRr = make_rsrc(a.rrms + m0 * 4, (uint32_t)rows * 16u);
+  const rsrc_t rX = make_rsrc(a.x + m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
+
+  // DMA: 8-row groups g = wave + 4 i (i < 4) of h and of Wu; lane -> row g*8 + (lane >> 3), 16-byte chunk swz
+  const uint32_t swz = (uint32_t)((lane & 7) ^ (lane >> 3));
+  uint32_t hoff[4], woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = wave + 4 * i;
+    const int rl = g * 8 + (lane >> 3);  // LDS row
+    hoff[i] = (uint32_t)rl * hrow + swz * 16u;
+    // Wu LDS row rl: block B = rl / 16 (channel half B / 4, gb = B % 4), row 4j + s
+    const int B = rl >> 4, ii = rl & 15, j = ii >> 2, s = ii & 3;
+    const int c = c0 + (B >> 2) * 16 + 4 * j + (B & 3);
+    woff[i] = (uint32_t)(s * a.HS + c) * hrow + swz * 16u;
+  }
+  auto issue = [&](int stg, uint8_t* hbuf, uint8_t* wbuf) {
+    const uint32_t kb = (uint32_t)stg * 128u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = wave + 4 * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rH, (lds_void_t*)(hbuf + g * 1024), 16, hoff[i] + kb, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rWu, (lds_void_t*)(wbuf + g * 1024), 16, woff[i] + kb, 0, 0, 0);
+    }
+  };
+
+  f32x4_t acc[4][4];  // [gb][tb]
+#pragma unroll
+  for (int gb = 0; gb < 4; ++gb)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[gb][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // fragment addresses (LDS byte offsets): A block ch*4 + gb at +gb*2048, B token tile th*4 + tb at +tb*2048
+  const uint32_t slot0 = (uint32_t)(((lane >> 4) ^ (lane & 7)) * 16);
+  const uint32_t slot1 = (uint32_t)(((4 + (lane >> 4)) ^ (lane & 7)) * 16);
+  const uint32_t arow = (uint32_t)((ch * 64 + (lane & 15)) * 128), brow = (uint32_t)((th * 64 + (lane & 15)) * 128);
+  auto contract = [&](const uint8_t* hbuf, const uint8_t* wbuf, bool both) {
+    const uint32_t wa = (uint32_t)(uintptr_t)(lds_u8_t*)wbuf + arow, ha = (uint32_t)(uintptr_t)(lds_u8_t*)hbuf + brow;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks == 1 && !both) break;  // half stage (r % 64 == 32)
+      const uint32_t sl = ks ? slot1 : slot0;
+      u32x4_t af[4], bf[4];
+      asm volatile(
+          "ds_read_b128 %0, %8\n\t"
+          "ds_read_b128 %1, %8 offset:2048\n\t"
+          "ds_read_b128 %2, %8 offset:4096\n\t"
+          "ds_read_b128 %3, %8 offset:6144\n\t"
+          "ds_read_b128 %4, %9\n\t"
+          "ds_read_b128 %5, %9 offset:2048\n\t"
+          "ds_read_b128 %6, %9 offset:4096\n\t"
+          "ds_read_b128 %7, %9 offset:6144\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]),
+            "=&v"(bf[3])
+          : "v"(wa + sl), "v"(ha + sl)
+          : "memory");
+#pragma unroll
+      for (int gb = 0; gb < 4; ++gb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          acc[gb][tb] = mfma16(__builtin_bit_cast(uint4, af[gb]), __builtin_bit_cast(uint4, bf[tb]), acc[gb][tb]);
+    }
+  };
+
+  // epilogue operands of this lane: channels cl..cl+3, tokens th*64 + tb*16 + (lane & 15)
+  const int cl = c0 + ch * 16 + 4 * (lane >> 4);
+  uint2 r2v[4][4];  // [tb][s]
+  f32x4_t rrv[4];   // [tb]
+  auto load_epilogue = [&]() {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const uint32_t t = (uint32_t)(th * 64 + tb * 16 + (lane & 15));
+      rrv[tb] = __builtin_bit_cast(f32x4_t, bld16(rRr, t * 16u));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) r2v[tb][s] = bld8(rR2, t * rowb + (uint32_t)(s * a.HS + cl) * 2u);
+    }
+  };
+
+  // stages: loads of stage i+1 go out once stage i-1 has been consumed
+  issue(0, hb_0, wb_0);
+  if (nstage > 1) issue(1, hb_1, wb_1);
+  load_epilogue();
+  for (int stg = 0; stg < nstage; ++stg) {
+    // in flight on entry, in issue order: the stage's loads, then (stage 0:
+    // stage 1's 8 loads) the 20 epilogue loads (stages 0 and 1), then stage
+    // st's own loads for st >= 2, which follow the epilogue loads
+    if (stg == 0) {
+      if (nstage > 1) asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+    } else if (stg == 1) {
+      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    lds_sync();  // every wave's part of the stage has landed; stage stg-1 fully consumed
+    if (stg >= 1 && stg + 1 < nstage) {
+      if (stg & 1) issue(stg + 1, hb_0, wb_0);
+      else issue(stg + 1, hb_1, wb_1);
+    }
+    const bool both = 64 * stg + 64 <= a.r;
+    if (stg & 1) contract(hb_1, wb_1, both);
+    else contract(hb_0, wb_0, both);
+  }
+
+  // (G2) sigmoid and (MIX) over the lane's four stream accumulators
+  float onep[4][4];  // [s][gb]
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint2 w = *reinterpret_cast<const uint2*>(a.wn + (a.wn_len == a.HS ? 0 : s * a.HS) + cl);
+    onep[s][0] = 1.0f + bf_lo(w.x);
+    onep[s][1] = 1.0f + bf_hi(w.x);
+    onep[s][2] = 1.0f + bf_lo(w.y);
+    onep[s][3] = 1.0f + bf_hi(w.y);
+  }
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const uint32_t t = (uint32_t)(th * 64 + tb * 16 + (lane & 15));
+    float xo[4];
+#pragma unroll
+    for (int gb = 0; gb < 4; ++gb) {
+      float g[4], xn[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t w = gb < 2 ? r2v[tb][s].x : r2v[tb][s].y;
+        const float r2 = (gb & 1) ? bf_hi(w) : bf_lo(w);
+        g[s] = acc[gb][tb][s];
+        xn[s] = r2 * rrv[tb][s] * onep[s][gb];
+      }
+      xo[gb] = mix4(g, xn);
+    }
+    bst8(rX, (t * (uint32_t)a.HS + (uint32_t)cl) * 2u, make_uint2(pack_bf2(xo[0], xo[1]), pack_bf2(xo[2], xo[3])));
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <int TM, int RB, int KW, int KC>
 static void launch_kd(const DownArgs& d, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((hcgr_k1_dec<TM, RB, KW, KC>), grid, dim3(RB * KW * 64), 0, st, d);
@@ -1543,9 +1735,15 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   t.h = H; t.M = f.M; t.r = s.r; t.HS = s.hs; t.K = K;
   t.wu = f.wu; t.R2 = f.R2; t.rrms = f.rrms; t.wn = f.wnorm; t.wn_len = s.wn_full ? K : s.hs; t.x = f.x;
   const KTShape ts = kt_shape(p.kt);
-  dim3 g2((unsigned)(s.hs / ts.cb), (unsigned)cdiv(f.M, ts.tm));
-  switch (p.kt) {
-    default: launch_kt<64, 64>(t, g2, st); break;
+  if (p.kt == KT_S128) {
+    StageArgs sa;
+    sa.h = H; sa.M = f.M; sa.r = s.r; sa.HS = s.hs; sa.K = K; sa.wu = f.wu; sa.R2 = f.R2; sa.rrms = f.rrms;
+    sa.wn = f.wnorm; sa.wn_len = s.wn_full ? K : s.hs; sa.x = f.x; sa.npairs = s.hs / 64;
+    const int64_t pairs = cdiv(f.M, (int64_t)ts.tm) * sa.npairs;
+    hipLaunchKernelGGL(hcgr_k2_stage, dim3((unsigned)(cdiv(pairs, 8) * 16)), dim3(256), 0, st, sa);
+  } else {
+    dim3 g2((unsigned)(s.hs / ts.cb), (unsigned)cdiv(f.M, ts.tm));
+    launch_kt<64, 64>(t, g2, st);
   }
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return (int)e;
   return (int)hipSuccess;
