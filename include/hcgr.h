@@ -82,9 +82,11 @@ hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out);
 /* Frees a handle (NULL is allowed). Outstanding work on streams is unaffected. */
 void hcgr_destroy(hcgr_handle h);
 
-/* Bytes of device workspace hcgr_forward needs for M tokens (0 for M == 0).
- * The workspace holds the partial sums of the down/inject contraction (per K
- * chunk at decode sizes, per stream at mid sizes), the per-chunk sums of
+/* Bytes of device workspace that serve hcgr_forward for every token count
+ * from 1 to M (0 for M == 0); the value never decreases as M grows, so one
+ * workspace sized for the largest M serves all smaller calls. The workspace
+ * holds the partial sums of the down/inject contraction (per K chunk at
+ * decode sizes, per stream or stream segment at mid sizes), their sums of
  * squares and the SiLU output h handed to the up kernel. Its contents on
  * entry are ignored (no zero-fill needed); calls that may run concurrently
  * (different streams) need separate workspaces. */

@@ -169,7 +169,7 @@ hcgr_status hcgr_workspace_size_for(const hcgr_config* cfg, int64_t M, size_t* b
   if (st != HCGR_OK) return st;
   if (!bytes) return fail(HCGR_ERR_INVALID_ARGUMENT, "bytes is NULL");
   if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
-  *bytes = hcgr::make_plan(s, M).ws_bytes;
+  *bytes = hcgr::workspace_bound(s, M);
   return ok();
 }
 
@@ -203,10 +203,10 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
     } else if (p.kind == hcgr::PLAN_TILE) {
       hcgr::KTShape t = hcgr::kt_shape(p.kt);
       snprintf(buf, len,
-               "M=%lld plan=tile | k1_tile tm=%d waves=8 stage_k=64 streams/wg=%d row_splits=%d grid=%lld%s | "
+               "M=%lld plan=tile | k1_tile tm=%d waves=8 stage_k=64 streams/wg=%d row_splits=%d segments=%d grid=%lld%s | "
                "%s tm=%d channels=%d grid=%lld | workspace=%zu",
-               (long long)M, (int)hcgr::kTileTm, p.spw, p.nsplit,
-               (long long)(hcgr::cdiv(M, hcgr::kTileTm) * p.nsplit * (4 / p.spw)), p.spw == 1 ? " | k1_sum" : "",
+               (long long)M, (int)hcgr::kTileTm, p.spw, p.nsplit, p.nseg,
+               (long long)(hcgr::cdiv(M, hcgr::kTileTm) * p.nsplit * (4 / p.spw) * p.nseg), p.spw == 1 ? " | k1_sum" : "",
                k2_name(p.kt), t.tm, t.cb, k2_grid(s, p.kt, M), p.ws_bytes);
     } else {
       hcgr::KFShape f = hcgr::kf_shape(p.kf);

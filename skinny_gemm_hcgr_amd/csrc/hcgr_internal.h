@@ -116,6 +116,7 @@ struct Plan {
   int kf = 0, kt = 0;              // variants
   int spw = 4;                     // streams per down workgroup (4 or 1)
   int nsplit = 1;                  // row-block splits of the down rows
+  int nseg = 1;                    // column segments per stream (TILE, one stream per workgroup)
   int64_t mq = 0;                  // rows of the per-stream partials (STREAM)
   size_t off_p = 0, off_ss = 0, off_h = 0, off_q = 0, ws_bytes = 0;
 };
@@ -126,11 +127,13 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Largest M served by the SPLIT plan.
 constexpr int64_t kSplitMaxM = 64;
 // TILE plan: 64-token down kernel (hcgr_k1_tile) with at most 22 16-row
-// blocks per workgroup (4 row quarters of at most 6); taken with one stream per workgroup from kTileMinM
-// tokens, with all four once the token tiles alone fill the chip.
+// blocks per workgroup (4 row quarters of at most 6); taken from kTileMinM
+// tokens: one stream per workgroup (split into column segments while that
+// leaves the chip short of workgroups), all four once the token tiles alone
+// fill it.
 constexpr int64_t kTileTm = 64;
 constexpr int kTileMaxBlk = 22;
-constexpr int64_t kTileMinM = 4096;
+constexpr int64_t kTileMinM = 65;
 
 // SPLIT plan with down-kernel variant kd; false when the stream width does
 // not split into chunks of the variant (the caller then takes another plan).
@@ -174,10 +177,20 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   const int64_t target = 256;
   const int64_t tiles = cdiv(M, kTileTm);
   const int tsplit = (int)cdiv(s.nblk(), kTileMaxBlk);  // row splits of the tile down kernel
-  if (tiles * tsplit >= target || (M >= kTileMinM && tiles * 4 * tsplit >= target)) {
+  if (M >= kTileMinM) {
     p.kind = PLAN_TILE;
     p.spw = tiles * tsplit >= target ? 4 : 1;
     p.nsplit = tsplit;
+    // below one workgroup per CU, split each stream's columns into segments
+    // (an even number of 64-column stages each); hcgr_k1_sum then forms rrms
+    if (p.spw == 1) {
+      const int pairs = s.hs / 128;
+      for (int d = 1; d <= pairs; ++d)
+        if (pairs % d == 0) {
+          p.nseg = d;
+          if (tiles * 4 * tsplit * d >= target) break;
+        }
+    }
     p.kt = KT_S128;
     p.tm = kTileTm;
     const int tm2 = kt_shape(p.kt).tm;
@@ -186,7 +199,11 @@ inline Plan make_plan(const Shape& s, int64_t M) {
     p.off_h = 0;
     p.off_q = align256((size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
     p.ws_bytes = p.off_q;
-    if (p.spw == 1) p.ws_bytes = align256(p.off_q + (size_t)s.hc * (size_t)p.mq * np * sizeof(float));
+    if (p.spw == 1) {
+      const size_t parts = (size_t)s.hc * (size_t)p.nseg;
+      p.off_ss = align256(p.off_q + parts * (size_t)p.mq * np * sizeof(float));
+      p.ws_bytes = align256(p.off_ss + parts * (size_t)p.mq * sizeof(float));
+    }
     return p;
   }
   const KFShape f64 = kf_shape(KF_T64);
@@ -218,6 +235,22 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   p.ws_bytes = p.off_q;
   if (p.kind == PLAN_STREAM) p.ws_bytes = align256(p.off_q + (size_t)s.hc * (size_t)p.mq * np * sizeof(float));
   return p;
+}
+
+// Workspace that serves every token count up to M: the largest plan need
+// over M' <= M. Plans are piecewise: the split plan for M' <= kSplitMaxM, and
+// tile plans whose partial-sum storage depends on the token tile count
+// (every M' with the same tile count needs at most what its largest member
+// needs), so the maximum is taken over at most kSplitMaxM + 256 + 1 plans.
+inline size_t workspace_bound(const Shape& s, int64_t M) {
+  if (M <= 0) return 0;
+  size_t best = make_plan(s, M).ws_bytes;
+  for (int64_t m = 1; m <= M && m <= kSplitMaxM; ++m) best = best > make_plan(s, m).ws_bytes ? best : make_plan(s, m).ws_bytes;
+  for (int64_t t = 1; t * kTileTm <= M && t <= 256; ++t) {
+    const size_t b = make_plan(s, t * kTileTm).ws_bytes;
+    best = best > b ? best : b;
+  }
+  return best;
 }
 
 struct ForwardArgs {

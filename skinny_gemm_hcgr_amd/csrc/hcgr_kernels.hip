@@ -825,9 +825,11 @@ struct Tile1Args {
   uint16_t* h;  // [>= M, r]        (SPW = 4)
   uint16_t* inj_next;
   int64_t ld_inj_next;
-  float* Q;  // [HC][Mq][NP] rrms-scaled per-stream partials (SPW = 1)
+  float* Q;  // [HC*nseg][Mq][NP] per-stream partials (SPW = 1): rrms-scaled, or unscaled when nseg > 1
   int64_t Mq;
   int NP;
+  int nseg;    // column segments per stream (SPW = 1 only); > 1: rrms is formed by hcgr_k1_sum
+  float* SSp;  // [HC*nseg][Mq] per-segment sums of squares (nseg > 1)
 };
 
 template <int SPW>
@@ -849,9 +851,12 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rq = wave & 3, th = wave >> 2;
   constexpr int NG = 4 / SPW;
-  const int sg = (int)(blockIdx.x % NG);
-  const int split = (int)((blockIdx.x / NG) % a.nsplit);
-  const int64_t m0 = (int64_t)(blockIdx.x / (NG * a.nsplit)) * TM;
+  const int nseg = SPW == 1 ? a.nseg : 1;
+  const int seg = (int)(blockIdx.x % nseg);
+  const int bid = (int)(blockIdx.x / nseg);
+  const int sg = bid % NG;
+  const int split = (bid / NG) % a.nsplit;
+  const int64_t m0 = (int64_t)(bid / (NG * a.nsplit)) * TM;
   const int rows = (int)min((int64_t)TM, a.M - m0);
   const int s_first = sg * SPW;
   const int b0 = split * a.nblk / a.nsplit, b1 = (split + 1) * a.nblk / a.nsplit;
@@ -860,7 +865,8 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   const int wcnt = (rq + 1) * nbw / 4 - qb0;  // blocks of this wave (<= BPW)
   const bool lead = split == 0;
   const int HS = a.HS;
-  const int nst = SPW * (HS / 64);
+  const int c_begin = seg * (HS / nseg), c_end = c_begin + HS / nseg;  // this workgroup's columns of each stream
+  const int nst = SPW * (HS / nseg / 64);
   const uint32_t rowb = (uint32_t)a.K * 2u;
 
   const rsrc_t rR = make_rsrc(a.R + m0 * a.K, (uint32_t)rows * rowb);
@@ -972,7 +978,14 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
     v += __shfl_xor(v, 2, 64);
     v += __shfl_xor(v, 4, 64);
     ss = 0.0f;
-    if ((tid & 7) == 0) rrs[sl][tok] = 1.0f / sqrtf(v * a.inv_hs + a.eps);
+    if ((tid & 7) == 0) {
+      if (nseg == 1) {
+        rrs[sl][tok] = 1.0f / sqrtf(v * a.inv_hs + a.eps);
+      } else {  // a segment of the stream: its sum of squares goes out, the partial stays unscaled
+        rrs[sl][tok] = 1.0f;
+        if (lead && tok < rows) a.SSp[(int64_t)(s_first * nseg + seg) * a.Mq + m0 + tok] = v;
+      }
+    }
   };
 
   f32x4_t acc_s[BPW][NTB];
@@ -1037,10 +1050,10 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   // stage they stay on it: those loads refill free buffers and are not used).
   const int s_last = s_first + SPW - 1;
   auto advance = [&](int& s, int& c) {
-    if (c + 64 < HS) c += 64;
-    else if (s < s_last) { c = 0; ++s; }
+    if (c + 64 < c_end) c += 64;
+    else if (s < s_last) { c = c_begin; ++s; }
   };
-  int s1 = s_first, c1 = 0, s2, c2, s3, c3;
+  int s1 = s_first, c1 = c_begin, s2, c2, s3, c3;
   advance(s1, c1);
   s2 = s1; c2 = c1; advance(s2, c2);
   s3 = s2; c3 = c2; advance(s3, c3);
@@ -1060,23 +1073,23 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
     issue_w(s1, c1, wnx);
     issue_ry(s3, c3, (st + 3) & (NRY - 1));
     if (st + 1 < nst) {
-      if (c1 == 0) {  // stage st+1 opens stream s1
+      if (c1 == c_begin) {  // stage st+1 opens stream s1
         ih = iwh[s1 - s_first][tok];
         il = iwl[s1 - s_first][tok];
       }
       combine(s1, c1, (st + 1) & (NRY - 1));
-      if (c1 + 64 == HS) stream_rrms(s1 - s_first);  // stage st+1 closes stream s1
+      if (c1 + 64 == c_end) stream_rrms(s1 - s_first);  // stage st+1 closes stream s1
     }
     contract(wc, b);
-    if (c0 + 64 == HS) fold(s - s_first);  // stage st closed stream s (its rrms is visible since the barrier)
+    if (c0 + 64 == c_end) fold(s - s_first);  // stage st closed stream s (its rrms is visible since the barrier)
     s1 = s2; c1 = c2;
     s2 = s3; c2 = c3;
     advance(s3, c3);
   };
 
   // prologue: weights of stage 0, R/y of stages 0-2; COMBINE of stage 0
-  issue_w(s_first, 0, w_0);
-  issue_ry(s_first, 0, 0);
+  issue_w(s_first, c_begin, w_0);
+  issue_ry(s_first, c_begin, 0);
   issue_ry(s1, c1, 1);
   issue_ry(s2, c2, 2);
   if (!wloader) {
@@ -1086,9 +1099,9 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   lds_sync();  // R/y of stage 0 and the iw table
   ih = iwh[0][tok];
   il = iwl[0][tok];
-  combine(s_first, 0, 0);
-  // iterations in pairs: weights alternate w_0, w_1 (nst is even)
-  int s = s_first, c0 = 0;
+  combine(s_first, c_begin, 0);
+  // iterations in pairs: weights alternate w_0, w_1 (a segment holds an even number of stages)
+  int s = s_first, c0 = c_begin;
   for (int st = 0; st < nst; st += 2) {
     iteration(st, s, c0, w_0, w_1);
     advance(s, c0);
@@ -1099,7 +1112,7 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  if (lead)
+  if (lead && nseg == 1)
     for (int i = tid; i < SPW * TM; i += NT) {
       const int sl = i / TM, t = i % TM;
       if (t < rows) a.rrms[(m0 + t) * 4 + s_first + sl] = rrs[sl][t];
@@ -1134,7 +1147,7 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
           f32x4_t v = acc_s[i][tb];
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] *= rr;
-          *reinterpret_cast<f32x4_t*>(a.Q + ((int64_t)s_first * a.Mq + m) * a.NP + n0) = v;
+          *reinterpret_cast<f32x4_t*>(a.Q + ((int64_t)(s_first * nseg + seg) * a.Mq + m) * a.NP + n0) = v;
         }
       }
     }
@@ -1142,41 +1155,83 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// hcgr_k1_sum (STREAM plan): v = sum_s rrms_s P_s for each token and row;
-// down rows -> h = SiLU(v/HC) (bf16), inject rows -> inj_next. One thread per
-// (token, 8 consecutive rows).
+// hcgr_k1_sum (STREAM plan, and TILE with one stream per workgroup):
+// v = sum_s rrms_s P_s for each token and row; down rows -> h = SiLU(v/HC)
+// (bf16), inject rows -> inj_next. P_s arrives rrms-scaled, or as unscaled
+// column-segment partials with their sums of squares, from which rrms is
+// formed here (and written). One lane per (token, 8 consecutive rows,
+// stream); the four stream lanes are adjacent and combine by shuffles.
 // ---------------------------------------------------------------------------
 struct SumArgs {
-  const float* Q;
+  const float* Q;  // [HC*nseg][Mq][NP]
   int64_t Mq, M;
   int NP, r, n_rows;
   float inv_hc;
   uint16_t* h;
   uint16_t* inj_next;
   int64_t ld_inj_next;
+  int nseg;          // > 1: Q holds unscaled segment partials and SSp their sums of squares
+  const float* SSp;  // [HC*nseg][Mq]
+  float* rrms;       // written when nseg > 1
+  float eps, inv_hs;
 };
 
 __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
+  // lane = (token m, chunk c of 8 rows, stream s); s is the fastest index, so
+  // the four streams of a (token, chunk) sit in adjacent lanes
   const int nch = a.r / 8 + 1;  // r/8 chunks of h, then the chunk holding the inject rows
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t m = idx / nch;
-  const int c = (int)(idx % nch);
-  if (m >= a.M) return;
+  const int s = (int)(idx & 3);
+  const int64_t mc = idx >> 2;
+  const int64_t m = min(mc / nch, a.M - 1);  // lanes past M recompute the last token and store nothing
+  const int c = (int)(mc % nch);
+  const bool live = mc / nch < a.M;
   const int n = c * 8;
-  float v[8];
+  float rr = 1.0f;  // partials arrive rrms-scaled unless the streams were split into segments
+  if (a.nseg > 1) {  // (N) rrms of stream s from its segments' sums of squares
+    float sq = 0.0f;
+    for (int g = 0; g < a.nseg; ++g) sq += a.SSp[(int64_t)(s * a.nseg + g) * a.Mq + m];
+    rr = 1.0f / sqrtf(sq * a.inv_hs + a.eps);
+    if (live && c == 0) a.rrms[m * 4 + s] = rr;
+  }
+  float u[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+  for (int e = 0; e < 8; ++e) u[e] = 0.0f;
+  const float* p = a.Q + ((int64_t)s * a.nseg * a.Mq + m) * a.NP + n;
+  const int64_t gstride = a.Mq * a.NP;
+  int g = 0;
+  for (; g + 4 <= a.nseg; g += 4) {  // four segments' loads in flight at once
+    f32x4_t lo[4], hi[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const float* p = a.Q + ((int64_t)s * a.Mq + m) * a.NP + n;
-    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(p);
-    const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(p + 4);
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = *reinterpret_cast<const f32x4_t*>(p + (g + j) * gstride);
+      hi[j] = *reinterpret_cast<const f32x4_t*>(p + (g + j) * gstride + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u[e] += lo[j][e];
+        u[e + 4] += hi[j][e];
+      }
+  }
+  for (; g < a.nseg; ++g) {
+    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(p + g * gstride);
+    const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(p + g * gstride + 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      v[e] += lo[e];
-      v[e + 4] += hi[e];
+      u[e] += lo[e];
+      u[e + 4] += hi[e];
     }
   }
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {  // sum over the four stream lanes
+    v[e] = rr * u[e];
+    v[e] += __shfl_xor(v[e], 1, 64);
+    v[e] += __shfl_xor(v[e], 2, 64);
+  }
+  if (!live || s != 0) return;
   if (n < a.r) {
     uint32_t o[4];
 #pragma unroll
@@ -1399,19 +1454,18 @@ __global__ __launch_bounds__(256) void hcgr_k2_tile(TileArgs a) {
 // hcgr_k2_stage: (G2) + (MIX) for a tile of 128 tokens x 32 channels (x 4
 // streams = 128 gate columns), 4 waves; wave (ch, th) owns channels ch*16..
 // and tokens th*64.. as 4 x 4 MFMA tiles (A = Wu rows, B = h rows). h and Wu
-// stream through LDS in stages of 64 k (one 128-byte line per row) by direct
-// global->LDS loads, double buffered (64 KB per workgroup, so two workgroups
-// share a CU and one's waits overlap the other's work). Fragment reads are
+// pass through one 32 KB LDS stage buffer in stages of 64 k (one 128-byte
+// line per row) by direct global->LDS loads; four workgroups share a CU, so
+// one's load waits are covered by the others' work. Fragment reads are
 // batched asm blocks (every LDS read they make is covered by the stage
 // wait). Inside a 16-row MFMA block, row 4j+s is stream s of channel 4j+gb
 // of the wave's block gb, so lane l ends with the 4 streams of channels
 // 4*(l/16)+gb, gb = 0..3, of token l%16: the MIX sum over streams is
 // lane-local and each lane moves 8 contiguous bytes of R2 and x per stream
-// and token. R2 and rrms go to registers once the first two stages are in
-// flight. Workgroups b and b+8 (the same XCD) take the two 32-channel halves
-// of a 64-channel group, so the second half of every 128-byte R2 line is an
-// L2 hit, and each XCD sees a fixed subset of channel groups (their Wu
-// slices stay in its L2).
+// and token. Workgroups b and b+8 (the same XCD) take the two 32-channel
+// halves of a 64-channel group, so the second half of every 128-byte R2
+// line is an L2 hit, and each XCD sees a fixed subset of channel groups
+// (their Wu slices stay in its L2).
 // ---------------------------------------------------------------------------
 struct StageArgs {
   const uint16_t* h;  // [>= M, r]
@@ -1426,12 +1480,10 @@ struct StageArgs {
   int npairs;  // 64-channel groups (HS / 64)
 };
 
-__global__ __launch_bounds__(256, 2) void hcgr_k2_stage(StageArgs a) {
+__global__ __launch_bounds__(256, 4) void hcgr_k2_stage(StageArgs a) {
   constexpr int TM = 128, CG = 32, SB = 16384;  // tokens, channels per workgroup, bytes per h (or Wu) stage
-  __shared__ __attribute__((aligned(1024))) uint8_t hb_0[SB];
-  __shared__ __attribute__((aligned(1024))) uint8_t hb_1[SB];
-  __shared__ __attribute__((aligned(1024))) uint8_t wb_0[SB];
-  __shared__ __attribute__((aligned(1024))) uint8_t wb_1[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t hb[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t wb[SB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1531,31 +1583,16 @@ __global__ __launch_bounds__(256, 2) void hcgr_k2_stage(StageArgs a) {
     }
   };
 
-  // stages: loads of stage i+1 go out once stage i-1 has been consumed
-  issue(0, hb_0, wb_0);
-  if (nstage > 1) issue(1, hb_1, wb_1);
-  load_epilogue();
+  // One stage buffer of 32 KB: four workgroups share a CU (128 VGPRs each),
+  // and the others' work covers each workgroup's load waits.
   for (int stg = 0; stg < nstage; ++stg) {
-    // in flight on entry, in issue order: the stage's loads, then (stage 0:
-    // stage 1's 8 loads) the 20 epilogue loads (stages 0 and 1), then stage
-    // st's own loads for st >= 2, which follow the epilogue loads
-    if (stg == 0) {
-      if (nstage > 1) asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-    } else if (stg == 1) {
-      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    lds_sync();  // every wave's part of the stage has landed; stage stg-1 fully consumed
-    if (stg >= 1 && stg + 1 < nstage) {
-      if (stg & 1) issue(stg + 1, hb_0, wb_0);
-      else issue(stg + 1, hb_1, wb_1);
-    }
-    const bool both = 64 * stg + 64 <= a.r;
-    if (stg & 1) contract(hb_1, wb_1, both);
-    else contract(hb_0, wb_0, both);
+    issue(stg, hb, wb);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_sync();                               // every wave's part of the stage has landed
+    contract(hb, wb, 64 * stg + 64 <= a.r);   // a half stage when r % 64 == 32
+    lds_sync();                               // every wave is done with the buffer before it is refilled
   }
+  load_epilogue();
 
   // (G2) sigmoid and (MIX) over the lane's four stream accumulators
   float onep[4][4];  // [s][gb]
@@ -1700,7 +1737,8 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     a.eps = s.eps; a.inv_hc = 1.0f / (float)s.hc; a.inv_hs = 1.0f / (float)s.hs;
     a.R2 = f.R2; a.rrms = f.rrms; a.h = H; a.inj_next = f.inj_next; a.ld_inj_next = f.ld_inj_next;
     a.Q = Q; a.Mq = p.mq; a.NP = s.np();
-    const dim3 g1((unsigned)(cdiv(f.M, kTileTm) * p.nsplit * (4 / p.spw)));
+    a.nseg = p.nseg; a.SSp = reinterpret_cast<float*>(ws + p.off_ss);
+    const dim3 g1((unsigned)(cdiv(f.M, kTileTm) * p.nsplit * (4 / p.spw) * p.nseg));
     if (p.spw == 4) hipLaunchKernelGGL(hcgr_k1_tile<4>, g1, dim3(512), 0, st, a);
     else hipLaunchKernelGGL(hcgr_k1_tile<1>, g1, dim3(512), 0, st, a);
   } else {
@@ -1725,7 +1763,9 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     SumArgs sa;
     sa.Q = Q; sa.Mq = p.mq; sa.M = f.M; sa.NP = s.np(); sa.r = s.r; sa.n_rows = s.n_rows();
     sa.inv_hc = 1.0f / (float)s.hc; sa.h = H; sa.inj_next = f.inj_next; sa.ld_inj_next = f.ld_inj_next;
-    const int64_t threads = f.M * (s.r / 8 + 1);
+    sa.nseg = p.kind == PLAN_TILE ? p.nseg : 1; sa.SSp = reinterpret_cast<const float*>(ws + p.off_ss);
+    sa.rrms = f.rrms; sa.eps = s.eps; sa.inv_hs = 1.0f / (float)s.hs;
+    const int64_t threads = f.M * (s.r / 8 + 1) * 4;
     hipLaunchKernelGGL(hcgr_k1_sum, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st, sa);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }

@@ -165,12 +165,24 @@ def test_full_width_wnorm_and_other_shapes_accepted(lib):
 
 
 def test_plan_description_and_workspace_size(lib):
-    for M in (1, 16, 17, 32, 64, 65, 128, 129, 1024, 1025, 8192, 65536):
+    prev = 0
+    for M in (1, 16, 17, 32, 64, 65, 128, 129, 300, 1024, 1025, 2048, 4096, 8192, 16384, 65536):
         n = H.hcgr_workspace_size_for(CFG, M)
-        assert n > 0 and n % 256 == 0  # not monotonic: the K split count changes between plans
+        assert n > 0 and n % 256 == 0
+        assert n >= prev  # one workspace sized for the largest M serves every smaller call
+        prev = n
         d = H.hcgr_describe_plan(CFG, M)
         assert d.startswith(f"M={M} plan=")
     assert H.hcgr_describe_plan(CFG, 0) == "M=0: no launch"
+
+
+def test_workspace_size_monotone_every_m(lib):
+    for cfg in (CFG, H.Config(hs=640, r=64), H.Config(hs=1024, r=512)):
+        prev = 0
+        for M in range(1, 1200):
+            n = H.hcgr_workspace_size_for(cfg, M)
+            assert n >= prev, (cfg, M)
+            prev = n
 
 
 def test_create_without_gfx950_fails_cleanly(lib):

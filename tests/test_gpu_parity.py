@@ -145,12 +145,13 @@ def test_strided_injection_and_layer_chaining(op, weights):
     check_all(out2, run_oracle(inp2))
 
 
-@pytest.mark.parametrize("hs,r,M", [(1024, 512, 16384), (640, 64, 8192), (2560, 320, 16420)])
+@pytest.mark.parametrize("hs,r,M", [(1024, 512, 16384), (640, 64, 8192), (2560, 320, 16420), (640, 64, 200), (1024, 512, 1000)])
 def test_tile_plan_shapes(H, hs, r, M):
-    """Large-M down kernel on other shapes: r = 512 (33 row blocks, two row
-    splits per token tile), a short stream (HS = 640: 10 stages, a partial
-    trip of the 6-stage loop) with one stream per workgroup, and a token count
-    whose last tile is partial."""
+    """Tile down kernel on other shapes: r = 512 (33 row blocks, two row
+    splits per token tile), a short stream (HS = 640: 10 stages) with one
+    stream per workgroup, a token count whose last tile is partial, and mid
+    token counts whose streams are split into column segments (HS = 640: 5
+    segments of 2 stages; r = 512: row splits and segments together)."""
     shape = synth.Shape(hs=hs, r=r)
     o = H.HCGR(H.Config(hs=hs, r=r), 0)
     plan = H.hcgr_describe_plan(o.cfg, M)
