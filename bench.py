@@ -15,8 +15,8 @@ bf16, separate Wd/Wi). Timing:
     rotating over enough sets to exceed the 256 MB Infinity Cache, so the
     weights come from HBM as they would when other layers run in between;
     "warm" re-reads one set.
-  * per-kernel durations come from HIP events recorded by hcgr_forward_timed
-    between the kernels, on the same stream.
+  * per-kernel durations come from the start/end HIP events that
+    hcgr_forward_timed takes around each kernel on the same stream.
 Inputs are seeded synthetic data (synth/) with the study's distributions.
 Prints ONE JSON line on stdout; --json-out also writes it (and the sweep) to a file.
 """
@@ -161,11 +161,12 @@ def time_calls(H, op, sets, steps, warmup, stream):
 
 def time_kernels(H, op, sets, steps, stream, host_us):
     """Average duration (µs) of each of the three kernels over `steps` calls,
-    from HIP events that hcgr_forward_timed records on the launch stream."""
+    from the start/end HIP events hcgr_forward_timed takes around each kernel
+    on the launch stream (kernel execution only, no dispatch gaps)."""
     import torch
     evs = []
     for _ in range(steps):
-        row = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         for e in row:
             e.record()  # materialise the hipEvent_t
         evs.append(row)
@@ -176,8 +177,8 @@ def time_kernels(H, op, sets, steps, stream, host_us):
     torch.cuda.synchronize()
     sums = [0.0, 0.0, 0.0]
     for row in evs:
-        for j in range(3):
-            sums[j] += row[j].elapsed_time(row[j + 1]) * 1e3
+        for j in range(3):  # start and end of stage j's kernel
+            sums[j] += row[2 * j].elapsed_time(row[2 * j + 1]) * 1e3
     names = stage_names(H.hcgr_describe_plan(op.cfg, sets.M))
     return {names[j]: sums[j] / steps for j in range(3) if names[j]}
 
@@ -211,12 +212,45 @@ def time_graph(H, op, sets, replays, stream):
     return us
 
 
-def roofline_entry(name, M, us, merged, plan):
+def kernel_source_digest():
+    """Digest of the kernel sources; a counter summary taken on other sources no longer applies."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "skinny_gemm_hcgr_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from a committed rocprofv3
+    counter summary (profiles/*_traffic.md: FETCH_SIZE and WRITE_SIZE scaled
+    by a copy kernel of known size), or None when there is none or the kernel
+    sources have changed since the counters were taken."""
+    import glob
+    import re
+    digest = kernel_source_digest()
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
+        with open(f) as fh:
+            text = fh.read()
+        for block in re.findall(r"```json\n(.*?)\n```", text, re.S):
+            try:
+                d = json.loads(block)
+            except ValueError:
+                continue
+            if d.get("workload") == workload and d.get("kernel") == kernel and d.get("source_digest") == digest:
+                return d.get("traffic_bytes_per_launch")
+    return None
+
+
+def roofline_entry(name, M, us, merged, plan, workload):
     b = kernel_bytes(name, M, merged, plan)
     gbs = b / (us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": name, "avg_us": round(us, 3),
-            "alg_bytes_per_launch": b, "flops_per_launch": kernel_flops(name, M)}
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, workload), "kernel": name,
+            "avg_us": round(us, 3), "alg_bytes_per_launch": b, "flops_per_launch": kernel_flops(name, M),
+            "source_digest": kernel_source_digest()}
 
 
 def run_workload(H, op_sep, op_merged, name, M, merged, scale0, steps, warmup, cold, stream):
@@ -285,6 +319,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--warm", action="store_true", help="headline on one re-read buffer set")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run 5 device-to-device copies of BYTES (HBM counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the op is token-parallel and this build has no multi-GPU "
@@ -295,6 +331,15 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 5}))
+        return
     H.load_library()
     op = H.HCGR(H.Config(), 0)
     opm = H.HCGR(H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336), 0)
@@ -323,7 +368,7 @@ def main():
             torch.cuda.empty_cache()
 
     dom = max(head["kernels_us"], key=lambda k: head["kernels_us"][k])
-    roof = roofline_entry(dom, M, head["kernels_us"][dom], merged, head["plan"])
+    roof = roofline_entry(dom, M, head["kernels_us"][dom], merged, head["plan"], args.workload)
     line = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["us_per_call"] / 1e3, 6),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

@@ -131,13 +131,15 @@ hcgr_status hcgr_forward(hcgr_handle h,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* hcgr_forward with per-stage timing marks, for measurement: `events` points
- * to 4 hipEvent_t handles owned by the caller (created with timing enabled).
- * events[0] is recorded on `stream` before the first kernel; events[1] after
- * the down/inject kernel; events[2] after the reduction kernel when the plan
- * has one (otherwise right after events[1]); events[3] after the up/mix
- * kernel. Same arguments, checks and results as hcgr_forward otherwise; NULL
- * events -> HCGR_ERR_INVALID_ARGUMENT. */
+/* hcgr_forward with per-kernel timing, for measurement: `events` points to 6
+ * hipEvent_t handles owned by the caller (created with timing enabled).
+ * events[2i] and events[2i+1] take the start and end times of stage i's
+ * kernel itself (the launches go through hipExtLaunchKernelGGL, so the gaps
+ * between kernels are not counted): stage 0 is the down/inject kernel, stage
+ * 1 the reduction kernel when the plan has one (otherwise both events are
+ * recorded right after stage 0, an empty interval), stage 2 the up/mix
+ * kernel. Same arguments, checks and results as hcgr_forward otherwise; a
+ * NULL events array or handle -> HCGR_ERR_INVALID_ARGUMENT. */
 hcgr_status hcgr_forward_timed(hcgr_handle h,
                                const uint16_t* R, const uint16_t* y,
                                const uint16_t* inj, int64_t ld_inj,

@@ -176,11 +176,14 @@ def hcgr_forward(handle, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_
 
 def hcgr_forward_timed(handle, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x,
                        workspace, workspace_bytes, stream, events) -> int:
-    """``hcgr_forward`` plus 4 caller-owned hipEvent_t marks (raw handles, ints)
-    recorded before the first kernel and after each of the three kernels."""
+    """``hcgr_forward`` plus 6 caller-owned hipEvent_t handles (ints): events
+    2i and 2i+1 take the start and end of stage i's kernel (down/inject,
+    reduction, up/mix)."""
     if not isinstance(stream, int):
         stream = stream.cuda_stream
-    ev = (ctypes.c_void_p * 4)(*events)
+    if len(events) != 6:
+        raise ValueError("hcgr_forward_timed takes 6 events")
+    ev = (ctypes.c_void_p * 6)(*events)
     st = load_library().hcgr_forward_timed(handle, _p(R), _p(y), _p(inj), int(ld_inj), _p(wnorm), _p(wd), _p(wi),
                                            _p(wu), int(M), _p(R2), _p(rrms), _p(inj_next), int(ld_inj_next), _p(x),
                                            _p(workspace), int(workspace_bytes), stream, ev)

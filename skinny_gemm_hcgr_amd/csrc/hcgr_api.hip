@@ -330,7 +330,7 @@ hcgr_status hcgr_forward_timed(hcgr_handle h, const uint16_t* R, const uint16_t*
                                int64_t ld_inj_next, uint16_t* x, void* workspace, size_t workspace_bytes,
                                void* stream, void* const* events) {
   if (!events) return fail(HCGR_ERR_INVALID_ARGUMENT, "events is NULL");
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 6; ++i)
     if (!events[i]) return fail(HCGR_ERR_INVALID_ARGUMENT, "events[%d] is NULL", i);
   return forward_impl(h, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x, workspace,
                       workspace_bytes, stream, events);

@@ -265,9 +265,9 @@ struct ForwardArgs {
 int configure_kernels();
 
 // Enqueues the plan's kernels on `stream`; returns the hipError_t of the
-// launches. With `events` (4 hipEvent_t) it records events[0] before the
-// first kernel and events[i] after the i-th stage (a plan with two kernels
-// records events[2] and events[3] back to back).
+// launches. With `events` (6 hipEvent_t) events[2i] and events[2i+1] mark the
+// start and end of stage i's kernel (a plan without a middle kernel records
+// events[2] and events[3] back to back after the first kernel).
 int launch_forward(const Shape& s, const Plan& p, const ForwardArgs& a, void* stream, void* const* events);
 
 }  // namespace hcgr

@@ -9,6 +9,7 @@
 // A and B use the same k order, so any internal k permutation of the
 // instruction cancels; only the row/column assignment matters.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include <functional>
@@ -1625,44 +1626,52 @@ __global__ __launch_bounds__(256, 4) void hcgr_k2_stage(StageArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int TM, int RB, int KW, int KC>
-static void launch_kd(const DownArgs& d, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((hcgr_k1_dec<TM, RB, KW, KC>), grid, dim3(RB * KW * 64), 0, st, d);
+// Every launch goes through hipExtLaunchKernelGGL: with a pair of timing
+// events (start, stop) the runtime stamps them at the kernel's own start and
+// end, so per-kernel durations exclude the dispatch gaps between kernels.
+template <typename F, typename... Args>
+static void klaunch(F k, dim3 grid, dim3 block, size_t lds, hipStream_t st, const hipEvent_t* ev, Args... args) {
+  hipExtLaunchKernelGGL(k, grid, block, (uint32_t)lds, st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0u, args...);
 }
-static void launch_kd_variant(int v, const DownArgs& d, dim3 grid, hipStream_t st) {
+
+template <int TM, int RB, int KW, int KC>
+static void launch_kd(const DownArgs& d, dim3 grid, hipStream_t st, const hipEvent_t* ev) {
+  klaunch(hcgr_k1_dec<TM, RB, KW, KC>, grid, dim3(RB * KW * 64), 0, st, ev, d);
+}
+static void launch_kd_variant(int v, const DownArgs& d, dim3 grid, hipStream_t st, const hipEvent_t* ev = nullptr) {
   switch (v) {
-    case KD_T16_R7_K1_C128: launch_kd<16, 7, 1, 128>(d, grid, st); break;
-    case KD_T16_R1_K4_C512: launch_kd<16, 1, 4, 512>(d, grid, st); break;
-    case KD_T16_R3_K1_C256: launch_kd<16, 3, 1, 256>(d, grid, st); break;
-    case KD_T16_R3_K2_C512: launch_kd<16, 3, 2, 512>(d, grid, st); break;
-    case KD_T32_R7_K1_C128: launch_kd<32, 7, 1, 128>(d, grid, st); break;
-    case KD_T32_R1_K4_C512: launch_kd<32, 1, 4, 512>(d, grid, st); break;
-    case KD_T32_R3_K1_C256: launch_kd<32, 3, 1, 256>(d, grid, st); break;
-    case KD_T32_R3_K2_C512: launch_kd<32, 3, 2, 512>(d, grid, st); break;
-    case KD_T64_R7_K1_C128: launch_kd<64, 7, 1, 128>(d, grid, st); break;
-    default: launch_kd<64, 3, 1, 256>(d, grid, st); break;
+    case KD_T16_R7_K1_C128: launch_kd<16, 7, 1, 128>(d, grid, st, ev); break;
+    case KD_T16_R1_K4_C512: launch_kd<16, 1, 4, 512>(d, grid, st, ev); break;
+    case KD_T16_R3_K1_C256: launch_kd<16, 3, 1, 256>(d, grid, st, ev); break;
+    case KD_T16_R3_K2_C512: launch_kd<16, 3, 2, 512>(d, grid, st, ev); break;
+    case KD_T32_R7_K1_C128: launch_kd<32, 7, 1, 128>(d, grid, st, ev); break;
+    case KD_T32_R1_K4_C512: launch_kd<32, 1, 4, 512>(d, grid, st, ev); break;
+    case KD_T32_R3_K1_C256: launch_kd<32, 3, 1, 256>(d, grid, st, ev); break;
+    case KD_T32_R3_K2_C512: launch_kd<32, 3, 2, 512>(d, grid, st, ev); break;
+    case KD_T64_R7_K1_C128: launch_kd<64, 7, 1, 128>(d, grid, st, ev); break;
+    default: launch_kd<64, 3, 1, 256>(d, grid, st, ev); break;
   }
 }
-static void launch_reduce(int cpl, const ReduceArgs& r, dim3 grid, hipStream_t st) {
+static void launch_reduce(int cpl, const ReduceArgs& r, dim3 grid, hipStream_t st, const hipEvent_t* ev = nullptr) {
   switch (cpl) {
-    case 1: hipLaunchKernelGGL(hcgr_k1_reduce<1>, grid, dim3(256), 0, st, r); break;
-    case 2: hipLaunchKernelGGL(hcgr_k1_reduce<2>, grid, dim3(256), 0, st, r); break;
-    case 3: hipLaunchKernelGGL(hcgr_k1_reduce<3>, grid, dim3(256), 0, st, r); break;
-    case 5: hipLaunchKernelGGL(hcgr_k1_reduce<5>, grid, dim3(256), 0, st, r); break;
-    default: hipLaunchKernelGGL(hcgr_k1_reduce<8>, grid, dim3(256), 0, st, r); break;
+    case 1: klaunch(hcgr_k1_reduce<1>, grid, dim3(256), 0, st, ev, r); break;
+    case 2: klaunch(hcgr_k1_reduce<2>, grid, dim3(256), 0, st, ev, r); break;
+    case 3: klaunch(hcgr_k1_reduce<3>, grid, dim3(256), 0, st, ev, r); break;
+    case 5: klaunch(hcgr_k1_reduce<5>, grid, dim3(256), 0, st, ev, r); break;
+    default: klaunch(hcgr_k1_reduce<8>, grid, dim3(256), 0, st, ev, r); break;
   }
 }
 template <int TM, int NW, int RBW>
-static void launch_k2(const UpArgs& u, dim3 grid, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((hcgr_k2_up_mix<TM, NW, RBW>), grid, dim3(NW * 64), lds, st, u);
+static void launch_k2(const UpArgs& u, dim3 grid, size_t lds, hipStream_t st, const hipEvent_t* ev = nullptr) {
+  klaunch(hcgr_k2_up_mix<TM, NW, RBW>, grid, dim3(NW * 64), lds, st, ev, u);
 }
 template <int TM, int NW, int BPW, int KS>
-static void launch_kf(const FullArgs& f, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((hcgr_k1_full<TM, NW, BPW, KS>), grid, dim3(NW * 64), 0, st, f);
+static void launch_kf(const FullArgs& f, dim3 grid, hipStream_t st, const hipEvent_t* ev) {
+  klaunch(hcgr_k1_full<TM, NW, BPW, KS>, grid, dim3(NW * 64), 0, st, ev, f);
 }
 template <int TM, int CB>
-static void launch_kt(const TileArgs& t, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((hcgr_k2_tile<TM, CB>), grid, dim3(256), 0, st, t);
+static void launch_kt(const TileArgs& t, dim3 grid, hipStream_t st, const hipEvent_t* ev) {
+  klaunch(hcgr_k2_tile<TM, CB>, grid, dim3(256), 0, st, ev, t);
 }
 
 int configure_kernels() {
@@ -1674,8 +1683,19 @@ int configure_kernels() {
   return (int)hipSuccess;
 }
 
-static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hipStream_t st,
-                        const std::function<hipError_t(int)>& mark) {
+// Per-stage timing: events[2i] and events[2i+1] bracket stage i's kernel (null: untimed).
+struct Timing {
+  const hipEvent_t* ev;
+  const hipEvent_t* stage(int i) const { return ev ? ev + 2 * i : nullptr; }
+  // a stage the plan does not have: an empty interval right after the previous stage
+  hipError_t skip(int i, hipStream_t st) const {
+    hipError_t e = hipSuccess;
+    if (ev && (e = hipEventRecord(ev[2 * i], st)) == hipSuccess) e = hipEventRecord(ev[2 * i + 1], st);
+    return e;
+  }
+};
+
+static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hipStream_t st, const Timing& tm) {
   hipError_t e;
   char* ws = static_cast<char*>(f.ws);
   float* P = reinterpret_cast<float*>(ws + p.off_p);
@@ -1692,17 +1712,16 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   d.inv_hc = 1.0f / (float)s.hc;
   d.R2 = f.R2; d.P = P; d.SS = SS;
   dim3 g1((unsigned)(p.ntiles_n * p.nkc), (unsigned)(p.mpad / p.tm));
-  launch_kd_variant(p.k1, d, g1, st);
-  if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return (int)e;
+  launch_kd_variant(p.k1, d, g1, st, tm.stage(0));
+  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   ReduceArgs r;
   r.P = P; r.SS = SS; r.Mpad = p.mpad; r.M = f.M;
   r.NP = s.np(); r.kcps = p.kcps; r.HS = s.hs; r.HC = s.hc; r.r = s.r; r.n_rows = s.n_rows();
   r.eps = s.eps; r.inv_hc = 1.0f / (float)s.hc; r.inv_hs = 1.0f / (float)s.hs;
   r.rrms = f.rrms; r.h = H; r.inj_next = f.inj_next; r.ld_inj_next = f.ld_inj_next;
   const int64_t waves = (int64_t)s.n_rows() * (p.mpad / 16);
-  launch_reduce(red_cpl(p.kcps), r, dim3((unsigned)((waves + 3) / 4)), st);
+  launch_reduce(red_cpl(p.kcps), r, dim3((unsigned)((waves + 3) / 4)), st, tm.stage(1));
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  if ((e = mark(2)) != hipSuccess) return (int)e;
 
   UpArgs u;
   u.h = H; u.Mpad = p.mpad; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = K;
@@ -1711,16 +1730,14 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   const size_t lds = (size_t)p.tm * (s.r + 8) * sizeof(uint16_t);
   dim3 g2((unsigned)(s.hs / p.cb), (unsigned)(p.mpad / p.tm));
   switch (p.k2) {
-    case K2_T16: launch_k2<16, 4, 1>(u, g2, lds, st); break;
-    case K2_T32: launch_k2<32, 4, 1>(u, g2, lds, st); break;
-    default: launch_k2<64, 4, 1>(u, g2, lds, st); break;
+    case K2_T16: launch_k2<16, 4, 1>(u, g2, lds, st, tm.stage(2)); break;
+    case K2_T32: launch_k2<32, 4, 1>(u, g2, lds, st, tm.stage(2)); break;
+    default: launch_k2<64, 4, 1>(u, g2, lds, st, tm.stage(2)); break;
   }
-  if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return (int)e;
-  return (int)hipSuccess;
+  return (int)hipGetLastError();
 }
 
-static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hipStream_t st,
-                        const std::function<hipError_t(int)>& mark) {
+static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hipStream_t st, const Timing& tm) {
   hipError_t e;
   char* ws = static_cast<char*>(f.ws);
   uint16_t* H = reinterpret_cast<uint16_t*>(ws + p.off_h);
@@ -1739,8 +1756,8 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     a.Q = Q; a.Mq = p.mq; a.NP = s.np();
     a.nseg = p.nseg; a.SSp = reinterpret_cast<float*>(ws + p.off_ss);
     const dim3 g1((unsigned)(cdiv(f.M, kTileTm) * p.nsplit * (4 / p.spw) * p.nseg));
-    if (p.spw == 4) hipLaunchKernelGGL(hcgr_k1_tile<4>, g1, dim3(512), 0, st, a);
-    else hipLaunchKernelGGL(hcgr_k1_tile<1>, g1, dim3(512), 0, st, a);
+    if (p.spw == 4) klaunch(hcgr_k1_tile<4>, g1, dim3(512), 0, st, tm.stage(0), a);
+    else klaunch(hcgr_k1_tile<1>, g1, dim3(512), 0, st, tm.stage(0), a);
   } else {
   FullArgs a;
   a.R = f.R; a.y = f.y; a.inj = f.inj; a.ld_inj = f.ld_inj;
@@ -1753,11 +1770,11 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   a.Q = Q; a.Mq = p.mq; a.NP = s.np();
   dim3 g1((unsigned)cdiv(f.M, fs.tm), (unsigned)(p.nsplit * (4 / p.spw)));
   switch (p.kf) {
-    case KF_T32: launch_kf<32, 8, 3, 128>(a, g1, st); break;
-    default: launch_kf<64, 8, 3, 64>(a, g1, st); break;
+    case KF_T32: launch_kf<32, 8, 3, 128>(a, g1, st, tm.stage(0)); break;
+    default: launch_kf<64, 8, 3, 64>(a, g1, st, tm.stage(0)); break;
   }
   }
-  if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return (int)e;
+  if ((e = hipGetLastError()) != hipSuccess) return (int)e;
 
   if (p.kind == PLAN_STREAM || (p.kind == PLAN_TILE && p.spw == 1)) {
     SumArgs sa;
@@ -1766,10 +1783,11 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     sa.nseg = p.kind == PLAN_TILE ? p.nseg : 1; sa.SSp = reinterpret_cast<const float*>(ws + p.off_ss);
     sa.rrms = f.rrms; sa.eps = s.eps; sa.inv_hs = 1.0f / (float)s.hs;
     const int64_t threads = f.M * (s.r / 8 + 1) * 4;
-    hipLaunchKernelGGL(hcgr_k1_sum, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st, sa);
+    klaunch(hcgr_k1_sum, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st, tm.stage(1), sa);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  } else if ((e = tm.skip(1, st)) != hipSuccess) {
+    return (int)e;
   }
-  if ((e = mark(2)) != hipSuccess) return (int)e;
 
   TileArgs t;
   t.h = H; t.M = f.M; t.r = s.r; t.HS = s.hs; t.K = K;
@@ -1780,24 +1798,19 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     sa.h = H; sa.M = f.M; sa.r = s.r; sa.HS = s.hs; sa.K = K; sa.wu = f.wu; sa.R2 = f.R2; sa.rrms = f.rrms;
     sa.wn = f.wnorm; sa.wn_len = s.wn_full ? K : s.hs; sa.x = f.x; sa.npairs = s.hs / 64;
     const int64_t pairs = cdiv(f.M, (int64_t)ts.tm) * sa.npairs;
-    hipLaunchKernelGGL(hcgr_k2_stage, dim3((unsigned)(cdiv(pairs, 8) * 16)), dim3(256), 0, st, sa);
+    klaunch(hcgr_k2_stage, dim3((unsigned)(cdiv(pairs, 8) * 16)), dim3(256), 0, st, tm.stage(2), sa);
   } else {
     dim3 g2((unsigned)(s.hs / ts.cb), (unsigned)cdiv(f.M, ts.tm));
-    launch_kt<64, 64>(t, g2, st);
+    launch_kt<64, 64>(t, g2, st, tm.stage(2));
   }
-  if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return (int)e;
-  return (int)hipSuccess;
+  return (int)hipGetLastError();
 }
 
 int launch_forward(const Shape& s, const Plan& p, const ForwardArgs& f, void* stream, void* const* events) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  std::function<hipError_t(int)> mark = [&](int i) -> hipError_t {
-    return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), st) : hipSuccess;
-  };
-  hipError_t e;
-  if ((e = mark(0)) != hipSuccess) return (int)e;
-  if (p.kind == PLAN_SPLIT) return launch_split(s, p, f, st, mark);
-  return launch_tiled(s, p, f, st, mark);
+  const Timing tm{reinterpret_cast<const hipEvent_t*>(events)};
+  if (p.kind == PLAN_SPLIT) return launch_split(s, p, f, st, tm);
+  return launch_tiled(s, p, f, st, tm);
 }
 
 }  // namespace hcgr

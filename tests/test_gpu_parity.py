@@ -293,6 +293,35 @@ def test_decode_interleaved_stress(H, op, weights):
         check_all(outs[M], run_oracle(inps[M]))
 
 
+@pytest.mark.parametrize("M", [32, 1024, 16384])
+def test_forward_timed_matches_forward(H, op, weights, M):
+    """The timed entry point gives the same bits as hcgr_forward and a start/end
+    event pair per stage (an empty middle interval when the plan has no
+    reduction kernel)."""
+    inp = synth.make_inputs(M, SHAPE, seed=3, device="cuda", weights=weights)
+    ref = gpu_forward(op, inp)
+    out = op.alloc_outputs(M)
+    ws = torch.empty(H.hcgr_workspace_size(op.handle, M), dtype=torch.uint8, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    H.hcgr_forward_timed(op.handle, inp["R"], inp["y"], inp["inj"], inp["inj"].stride(0), inp["wnorm"], inp["wd"],
+                         inp["wi"], inp["wu"], M, out["R2"], out["rrms"], out["inj_next"], out["ld_inj_next"], out["x"],
+                         ws, ws.numel(), torch.cuda.current_stream().cuda_stream, [e.cuda_event for e in ev])
+    torch.cuda.synchronize()
+    for k in ("R2", "rrms", "inj_next", "x"):
+        assert torch.equal(ref[k], out[k]), k
+    d = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(3)]
+    assert d[0] > 0 and d[2] > 0 and d[1] >= 0, d
+    assert all(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) >= 0 for i in range(2))  # stages in order
+    with pytest.raises(H.HcgrError):
+        H.hcgr_forward_timed(op.handle, inp["R"], inp["y"], inp["inj"], inp["inj"].stride(0), inp["wnorm"], inp["wd"],
+                             inp["wi"], inp["wu"], M, out["R2"], out["rrms"], out["inj_next"], out["ld_inj_next"],
+                             out["x"], ws, ws.numel(), torch.cuda.current_stream().cuda_stream,
+                             [e.cuda_event for e in ev[:5]] + [0])
+
+
 def test_graph_capture_replays(op, weights):
     """hcgr_forward captured into a HIP graph: several replays with new input
     values written between them, each checked against an eager call."""
