@@ -195,7 +195,7 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
       hcgr::K2Shape b = hcgr::k2_shape(p.k2);
       snprintf(buf, len,
                "M=%lld plan=split mpad=%lld | k1_dec tm=%d row_blocks=%d k_waves=%d k_chunk=%d chunks=%d n_tiles=%d "
-               "grid=%dx%lld | k1_reduce waves=%lld | k2_up_mix tm=%d waves=%d channels=%d grid=%dx%lld | "
+               "grid=%dx%lld | k1_reduce waves=%lld | k2_dec tm=%d waves=%d channels=%d grid=%dx%lld | "
                "workspace=%zu",
                (long long)M, (long long)p.mpad, a.tm, a.rb, a.kw, p.kc, p.nkc, p.ntiles_n, p.ntiles_n * p.nkc,
                (long long)(p.mpad / p.tm), (long long)(s.n_rows() * (p.mpad / 16)), b.tm, b.nw, p.cb,

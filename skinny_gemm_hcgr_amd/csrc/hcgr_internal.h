@@ -13,8 +13,9 @@
 //                         (token tile, K chunk inside one stream, row tile)
 //     K1r hcgr_k1_reduce  sums the chunk partials per stream, forms rrms,
 //                         scales, SiLU(./HC) -> h (workspace), inj_next
-//     K2  hcgr_k2_up_mix  up contraction on MFMA tiles whose 16 rows are
-//                         4 channels x 4 streams; sigmoid + MIX in registers
+//     K2  hcgr_k2_dec     up contraction on MFMA tiles whose 16 rows are
+//                         4 channels x 4 streams, Wu rows and h staged in LDS by
+//                         direct global->LDS loads; sigmoid + MIX in registers
 //   TILE (large sizes). Activation streaming with LDS-staged weights:
 //     K1  hcgr_k1_tile    a workgroup owns 64 tokens and every down/inject
 //                         row (or a row split); weights, R and y arrive in
@@ -58,11 +59,13 @@ inline KDShape kd_shape(int v) {
                                      {64, 7, 1, 128}, {64, 3, 1, 256}};
   return t[v];
 }
-// SPLIT-plan up kernel variants (token tile; 4 waves of 4 channels x 4 streams).
+// SPLIT-plan up kernel variants: token tile; kDecUpWaves waves of 4
+// channels x 4 streams each per workgroup.
+constexpr int kDecUpWaves = 4;
 enum K2Variant { K2_T16 = 0, K2_T32 = 1, K2_T64S = 2, K2_NVAR };
 struct K2Shape { int tm, nw, rbw; };
 inline K2Shape k2_shape(int v) {
-  static const K2Shape t[K2_NVAR] = {{16, 4, 1}, {32, 4, 1}, {64, 4, 1}};
+  static const K2Shape t[K2_NVAR] = {{16, kDecUpWaves, 1}, {32, kDecUpWaves, 1}, {64, kDecUpWaves, 1}};
   return t[v];
 }
 // The reduction kernel gives each of a wave's 4 lane groups up to kRedMaxCpl

@@ -344,11 +344,17 @@ __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K2: (G2) gate = h . Wu^T, G = sigmoid(gate), (MIX) x[c] = 1/4 sum_s G xn.
-// Workgroup = TM tokens x CB = NW*RBW*4 channels. A operand rows: 16 rows =
-// 4 channels x 4 streams (row i -> channel i/4, stream i%4, i.e. Wu row
-// (i%4)*HS + c), so accumulator q of a lane is stream q of one channel and
-// the sum over streams stays in registers. B operand = h tile staged in LDS.
+// hcgr_k2_dec (SPLIT plan, decode sizes): (G2) gate = h . Wu^T, G =
+// sigmoid(gate), (MIX) x[c] = 1/4 sum_s G xn, for a token tile of TM tokens
+// and 16 channels x 4 streams, 4 waves. The workgroup's 64 Wu rows (r values
+// each) and its h tile arrive in LDS by direct global->LDS loads (wide 1 KB
+// instructions instead of per-lane fragment loads); inside a row the 16-byte
+// chunk c sits in slot (c & ~3) | ((c ^ row) & 3), which spreads the 16-row
+// fragment reads over the banks. R2, rrms and Wnorm of the epilogue are
+// loaded into registers meanwhile. Wave w owns channels 4w..4w+3: MFMA row
+// 4*c + s is stream s of channel c (Wu row s*HS + c), so lane l ends with the
+// four streams of channel w*4 + l/16 for token l%16 and the MIX sum is
+// lane-local.
 // ---------------------------------------------------------------------------
 struct UpArgs {
   const uint16_t* h;
@@ -362,142 +368,92 @@ struct UpArgs {
   uint16_t* x;
 };
 
-template <int TM, int NW, int RBW>
-__global__ __launch_bounds__(NW * 64) void hcgr_k2_up_mix(UpArgs a) {
-  constexpr int NT = NW * 64;
+template <int TM, int NW>
+__global__ __launch_bounds__(NW * 64) void hcgr_k2_dec(UpArgs a) {
   constexpr int NTB = TM / 16;
-  constexpr int JMAX = 16;  // r <= 512
-  extern __shared__ __attribute__((aligned(16))) uint16_t hl[];
-  const int ldh = a.r + 8;
+  constexpr int WR = NW * 16;  // Wu rows of the workgroup (NW * 4 channels x 4 streams)
+  extern __shared__ __attribute__((aligned(1024))) uint8_t dl[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t m0 = (int64_t)blockIdx.y * TM;
-  const int cbase = blockIdx.x * (NW * RBW * 4);
-  const int koff = 8 * (lane >> 4);
+  const int rows = (int)min((int64_t)TM, a.M - m0);
+  const int cbase = blockIdx.x * (NW * 4);
+  const int cpr = a.r / 8;  // 16-byte chunks per row (a multiple of 4)
+  const uint32_t rowb = (uint32_t)a.r * 2u;
+  uint8_t* wl = dl;              // [WR][r]: row 4*cl + s = stream s of channel cbase + cl
+  uint8_t* hl = dl + WR * rowb;  // [TM][r]
+  const rsrc_t rWu = make_rsrc(a.wu, (uint32_t)a.K * rowb);
+  const rsrc_t rH = make_rsrc(a.h + m0 * a.r, (uint32_t)rows * rowb);  // rows past M read as zero
+
+  // global -> LDS: instruction i fills LDS chunks [64 i, 64 i + 64) of a
+  // block; WR*cpr and TM*cpr are multiples of 64
+  for (int i = wave; i * 64 < WR * cpr; i += NW) {
+    const int q = i * 64 + lane, row = q / cpr, sl = q % cpr;
+    const int c = (sl & ~3) | ((sl ^ row) & 3);  // the chunk this slot holds
+    const uint32_t off = (uint32_t)((row & 3) * a.HS + cbase + (row >> 2)) * rowb + (uint32_t)c * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWu, (lds_void_t*)(wl + i * 1024), 16, off, 0, 0, 0);
+  }
+  for (int i = wave; i * 64 < TM * cpr; i += NW) {
+    const int q = i * 64 + lane, row = q / cpr, sl = q % cpr;
+    const int c = (sl & ~3) | ((sl ^ row) & 3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rH, (lds_void_t*)(hl + i * 1024), 16, (uint32_t)row * rowb + (uint32_t)c * 16u,
+                                             0, 0, 0);
+  }
+  // epilogue operands: lane holds streams q = 0..3 of channel c for token m
+  const int c = cbase + wave * 4 + (lane >> 4);
+  float pr2[NTB][4], prr[NTB][4], pone[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pone[q] = 1.0f + bf1(a.wn[a.wn_full ? q * a.HS + c : c]);
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    const int64_t m = m0 + tb * 16 + (lane & 15);
+    const int64_t mc = m < a.M ? m : a.M - 1;  // clamped: no branch around the load
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pr2[tb][q] = bf1(a.R2[mc * a.K + q * a.HS + c]);
+      prr[tb][q] = a.rrms[mc * 4 + q];
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_sync();  // every wave's global->LDS loads have landed
+
+  f32x4_t acc[NTB];
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) acc[tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int arow = wave * 16 + (lane & 15);
   const int nj = a.r / 32;
-
-  const uint16_t* wrow[RBW];
-#pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) {
-    const int c = cbase + (wave * RBW + rb) * 4 + ((lane & 15) >> 2);
-    const int s = lane & 3;
-    wrow[rb] = a.wu + ((int64_t)s * a.HS + c) * a.r;
-  }
-
-  // decode-sized tiles: issue every global load of the wave (weights and the
-  // epilogue's R2, rrms and Wnorm) before the first wait
-  uint4 wall[RBW == 1 ? JMAX : 1];
-  float pr2[RBW == 1 ? NTB : 1][4], prr[RBW == 1 ? NTB : 1][4], pone[4];
-  if constexpr (RBW == 1) {
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j)
-      if (j < nj) wall[j] = ld16(wrow[0] + j * 32 + koff);
-    const int c = cbase + wave * 4 + (lane >> 4);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) pone[q] = 1.0f + bf1(a.wn[a.wn_full ? q * a.HS + c : c]);
+  auto kstep = [&](int j, uint4& af, uint4 (&bf)[NTB]) {  // fragments of k step j
+    af = *reinterpret_cast<const uint4*>(wl + arow * rowb + (uint32_t)(j * 4 + (((lane >> 4) ^ arow) & 3)) * 16u);
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
-      const int64_t m = m0 + tb * 16 + (lane & 15);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t mc = m < a.M ? m : a.M - 1;  // clamped: no branch around the load
-        pr2[tb][q] = bf1(a.R2[mc * a.K + q * a.HS + c]);
-        prr[tb][q] = a.rrms[mc * 4 + q];
-      }
+      const int t = tb * 16 + (lane & 15);
+      bf[tb] = *reinterpret_cast<const uint4*>(hl + t * rowb + (uint32_t)(j * 4 + (((lane >> 4) ^ t) & 3)) * 16u);
     }
+  };
+  int j = 0;
+  for (; j + 2 <= nj; j += 2) {  // two k steps' fragments in flight per round trip
+    uint4 a0, a1, b0[NTB], b1[NTB];
+    kstep(j, a0, b0);
+    kstep(j + 1, a1, b1);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) acc[tb] = mfma16(a1, b1[tb], mfma16(a0, b0[tb], acc[tb]));
+  }
+  if (j < nj) {
+    uint4 a0, b0[NTB];
+    kstep(j, a0, b0);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) acc[tb] = mfma16(a0, b0[tb], acc[tb]);
   }
 
-  // h tile -> LDS: every load is issued before the first LDS store (a
-  // compile-time count for r <= 512, clamped past the tile: no branch around
-  // a load), so staging costs one memory round trip
-  const int cpr = a.r / 8;
-  constexpr int HPT = TM * 64 / NT;
-  uint4 hv[HPT];
 #pragma unroll
-  for (int j = 0; j < HPT; ++j) {
-    const int q = min(tid + j * NT, TM * cpr - 1);
-    hv[j] = ld16(a.h + (m0 + q / cpr) * a.r + (q % cpr) * 8);
-  }
+  for (int tb = 0; tb < NTB; ++tb) {
+    const int64_t m = m0 + tb * 16 + (lane & 15);
+    if (m < a.M) {
+      float sum = 0.0f;
 #pragma unroll
-  for (int j = 0; j < HPT; ++j) {
-    const int q = tid + j * NT;
-    if (q < TM * cpr) st16(&hl[(q / cpr) * ldh + (q % cpr) * 8], hv[j]);
-  }
-  __syncthreads();
-
-  f32x4_t acc[RBW][NTB];
-#pragma unroll
-  for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) acc[rb][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  if constexpr (RBW == 1) {
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j) {
-      if (j < nj) {
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-          const uint4 b = *reinterpret_cast<const uint4*>(&hl[(tb * 16 + (lane & 15)) * ldh + j * 32 + koff]);
-          acc[0][tb] = mfma16(wall[j], b, acc[0][tb]);
-        }
-      }
-    }
-  } else {
-    uint4 wn_[RBW];
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) wn_[rb] = ld16(wrow[rb] + koff);
-    for (int j = 0; j < nj; ++j) {
-      uint4 wc[RBW];
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) wc[rb] = wn_[rb];
-      if (j + 1 < nj) {
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) wn_[rb] = ld16(wrow[rb] + (j + 1) * 32 + koff);
-      }
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        const uint4 b = *reinterpret_cast<const uint4*>(&hl[(tb * 16 + (lane & 15)) * ldh + j * 32 + koff]);
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) acc[rb][tb] = mfma16(wc[rb], b, acc[rb][tb]);
-      }
-    }
-  }
-
-  // epilogue: lane holds streams q = 0..3 of channel c for token m
-  if constexpr (RBW == 1) {
-    const int c = cbase + wave * 4 + (lane >> 4);
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) {
-      const int64_t m = m0 + tb * 16 + (lane & 15);
-      if (m < a.M) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sum = fmaf(sigmoid_f(acc[0][tb][q]), pr2[tb][q] * prr[tb][q] * pone[q], sum);
-        a.x[m * a.HS + c] = to_bf(sum * 0.25f);
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int rb = 0; rb < RBW; ++rb) {
-    const int c = cbase + (wave * RBW + rb) * 4 + (lane >> 4);
-    float onep[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) onep[q] = 1.0f + bf1(a.wn[a.wn_full ? q * a.HS + c : c]);
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) {
-      const int64_t m = m0 + tb * 16 + (lane & 15);
-      if (m < a.M) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float g = sigmoid_f(acc[rb][tb][q]);
-          const float xn = bf1(a.R2[m * a.K + q * a.HS + c]) * a.rrms[m * 4 + q] * onep[q];
-          sum = fmaf(g, xn, sum);
-        }
-        a.x[m * a.HS + c] = to_bf(sum * 0.25f);
-      }
+      for (int q = 0; q < 4; ++q) sum = fmaf(sigmoid_f(acc[tb][q]), pr2[tb][q] * prr[tb][q] * pone[q], sum);
+      a.x[m * a.HS + c] = to_bf(sum * 0.25f);
     }
   }
 }
@@ -1661,10 +1617,6 @@ static void launch_reduce(int cpl, const ReduceArgs& r, dim3 grid, hipStream_t s
     default: klaunch(hcgr_k1_reduce<8>, grid, dim3(256), 0, st, ev, r); break;
   }
 }
-template <int TM, int NW, int RBW>
-static void launch_k2(const UpArgs& u, dim3 grid, size_t lds, hipStream_t st, const hipEvent_t* ev = nullptr) {
-  klaunch(hcgr_k2_up_mix<TM, NW, RBW>, grid, dim3(NW * 64), lds, st, ev, u);
-}
 template <int TM, int NW, int BPW, int KS>
 static void launch_kf(const FullArgs& f, dim3 grid, hipStream_t st, const hipEvent_t* ev) {
   klaunch(hcgr_k1_full<TM, NW, BPW, KS>, grid, dim3(NW * 64), 0, st, ev, f);
@@ -1675,11 +1627,11 @@ static void launch_kt(const TileArgs& t, dim3 grid, hipStream_t st, const hipEve
 }
 
 int configure_kernels() {
-  const int lim = 96 * 1024;
+  const int lim = 128 * 1024;  // (64 + 64) rows of r <= 512 values
   hipError_t e;
-  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_up_mix<16, 4, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
-  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_up_mix<32, 4, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
-  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_up_mix<64, 4, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
+  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<16, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
+  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<32, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
+  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<64, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
   return (int)hipSuccess;
 }
 
@@ -1727,12 +1679,13 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   u.h = H; u.Mpad = p.mpad; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = K;
   u.wu = f.wu; u.R2 = f.R2; u.rrms = f.rrms; u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0;
   u.x = f.x;
-  const size_t lds = (size_t)p.tm * (s.r + 8) * sizeof(uint16_t);
-  dim3 g2((unsigned)(s.hs / p.cb), (unsigned)(p.mpad / p.tm));
+  const size_t lds = (size_t)(kDecUpWaves * 16 + p.tm) * (size_t)s.r * sizeof(uint16_t);
+  const dim3 g2((unsigned)(s.hs / p.cb), (unsigned)(p.mpad / p.tm));
+  const dim3 b2(kDecUpWaves * 64);
   switch (p.k2) {
-    case K2_T16: launch_k2<16, 4, 1>(u, g2, lds, st, tm.stage(2)); break;
-    case K2_T32: launch_k2<32, 4, 1>(u, g2, lds, st, tm.stage(2)); break;
-    default: launch_k2<64, 4, 1>(u, g2, lds, st, tm.stage(2)); break;
+    case K2_T16: klaunch(hcgr_k2_dec<16, kDecUpWaves>, g2, b2, lds, st, tm.stage(2), u); break;
+    case K2_T32: klaunch(hcgr_k2_dec<32, kDecUpWaves>, g2, b2, lds, st, tm.stage(2), u); break;
+    default: klaunch(hcgr_k2_dec<64, kDecUpWaves>, g2, b2, lds, st, tm.stage(2), u); break;
   }
   return (int)hipGetLastError();
 }
