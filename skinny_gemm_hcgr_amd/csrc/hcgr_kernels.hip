@@ -739,30 +739,30 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_full(FullArgs a) {
 
 // ---------------------------------------------------------------------------
 // hcgr_k1_tile (large token counts): COMBINE + N + down/inject contraction
-// for a tile of TM = 64 tokens, with every operand staged through LDS by
-// direct global->LDS loads (buffer_load ... lds, 8 rows x 128 bytes per wave
-// instruction).
+// for a tile of TM = 64 tokens.
 // Workgroup = (token tile) x (row split: 16-row blocks [b0, b1), at most 22)
-// x (stream group: SPW = 4 streams, or SPW = 1 stream whose rrms-scaled
-// partial goes to the workspace). Eight waves, two per SIMD: wave (rq, th)
-// owns row quarter rq of the blocks (at most 6) and token half th (two MFMA
-// column blocks of 16 tokens).
-// A stage is 64 columns of k, one 128-byte line per matrix row. The loop is
-// software pipelined with one barrier per iteration: iteration i contracts
-// stage i (weights and activation from LDS into v_mfma_f32_16x16x32_bf16)
-// while it combines stage i+1 (R and y from LDS -> R2 to HBM, bf16
-// activation R2*(1+Wnorm) written over R in place), so the VALU work of one
-// may overlap the matrix and LDS work of the other. Weights are double
-// buffered (stage i+1 loads during iteration i) and R/y/Wnorm use a ring of
-// four (stage i+3 loads during iteration i). Waves 0-3 issue only R/y
-// loads and waves 4-7 only weight loads: a wave's loads complete in issue
-// order, so a weight wait never queues behind HBM misses, and each wave
-// issues a fixed count per stage, so the wait at the top of an iteration
-// names an exact count. Inside each 128-byte LDS row the 16-byte chunk c of
-// row t sits in slot c ^ (t & 7), which spreads MFMA fragment reads (16
-// rows, one chunk) over the banks. At each stream end the stream's sum of
-// squares gives rrms and, with SPW = 4, the stream accumulator is folded
-// into the rrms-scaled total (two accumulator sets).
+// x (stream group: SPW = 4 streams, or SPW = 1 stream whose partial goes to
+// the workspace) x (column segment of that stream, SPW = 1 only). Eight
+// waves, two per SIMD: wave (rq, th) owns row quarter rq of the blocks (at
+// most 6) and token half th (two MFMA column blocks of 16 tokens).
+// A stage is 64 columns of k. Iteration i contracts stage i (weights and the
+// bf16 activation from LDS into v_mfma_f32_16x16x32_bf16) and combines stage
+// i+1 (R, y and Wnorm from registers -> R2 to HBM, activation R2*(1+Wnorm)
+// to LDS), with one barrier per iteration. Thread t owns one 16-byte chunk
+// (token t/8) of every stage and prefetches its R, y and Wnorm chunks D = 4
+// stages ahead into a ring of registers, so the workgroup keeps several
+// stages of HBM reads in flight without LDS space for them. Weights (read
+// from L2) and the activation are double buffered in LDS; the weights arrive
+// by direct global->LDS loads, 8 rows x 128 bytes per wave instruction,
+// six per wave. Every thread issues the same loads in the same order in
+// every iteration (prefetches past the last stage use an offset outside the
+// buffer range: they return zeros without touching memory), so the wait at
+// the top of an iteration names an exact count of later loads. Inside each
+// 128-byte LDS row the 16-byte chunk c of row t sits in slot c ^ (t & 7),
+// which spreads MFMA fragment reads (16 rows, one chunk) over the banks. At
+// each stream end the stream's sum of squares gives rrms and, with SPW = 4,
+// the stream accumulator is folded into the rrms-scaled total (two
+// accumulator sets).
 // ---------------------------------------------------------------------------
 struct Tile1Args {
   const uint16_t* R;
@@ -789,18 +789,22 @@ struct Tile1Args {
   float* SSp;  // [HC*nseg][Mq] per-segment sums of squares (nseg > 1)
 };
 
+template <int N>
+using ic = std::integral_constant<int, N>;
+
 template <int SPW>
 __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
-  constexpr int TM = (int)kTileTm, NT = 512, BPW = 6, NTB = 2, NRY = 4;
-  constexpr int WGRP = kTileMaxBlk * 2 / 4;  // 8-row weight groups per loading wave per stage
-  // R/y stage buffer: R rows, y rows, then the stage's 64 Wnorm values (1 KB slot)
-  constexpr int WBYTES = kTileMaxBlk * 16 * 128, ABYTES = TM * 128, RYB = 2 * ABYTES + 1024;
+  constexpr int TM = (int)kTileTm, NT = 512, BPW = 6, NTB = 2, D = 4;
+  constexpr int WGRP = 6;  // 8-row weight groups per wave per stage
+  constexpr int WBYTES = 8 * WGRP * 1024, ABYTES = TM * 128;
   constexpr int NSET = SPW == 4 ? 1 : 0;  // rrms-scaled total kept in registers
-  static_assert(TM == 64 && WGRP * 4 == 2 * kTileMaxBlk && (kTileMaxBlk * 3) / 4 + BPW <= kTileMaxBlk + 1,
+  constexpr uint32_t kOut = 0x80000000u;  // offset past every buffer range
+  static_assert(TM == 64 && 8 * WGRP >= 2 * kTileMaxBlk && (kTileMaxBlk * 3) / 4 + BPW <= 8 * WGRP / 2,
                 "tile shape: every wave's blocks (read or not) lie inside the weight buffer");
   __shared__ __attribute__((aligned(1024))) uint8_t w_0[WBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t w_1[WBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t ry[NRY * RYB];
+  __shared__ __attribute__((aligned(1024))) uint8_t act_0[ABYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t act_1[ABYTES];
   __shared__ float iwh[SPW][TM], iwl[SPW][TM], rrs[SPW][TM];
 
   const int tid = threadIdx.x;
@@ -833,100 +837,73 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   const rsrc_t rW0 = make_rsrc(a.w0, (uint32_t)a.r * rowb);
   const rsrc_t rW1 = make_rsrc(a.w1, (uint32_t)a.HC * rowb);  // rows past HC read as zero
 
-  // (COMBINE) iw = 2*sigmoid(inj/HC) in fp64, kept as fp32 hi + lo
-  for (int i = tid; i < SPW * TM; i += NT) {
-    const int sl = i / TM, t = i % TM;
-    double v = 0.0;
-    if (t < rows) v = 2.0 / (1.0 + exp(-(double)bf1(a.inj[(m0 + t) * a.ld_inj + s_first + sl]) / (double)a.HC));
-    const float hi = (float)v;
-    iwh[sl][t] = hi;
-    iwl[sl][t] = (float)(v - (double)hi);
-  }
+  // injection logit of table entry tid (loaded before the prefetches below,
+  // which then stay in flight while iw is formed)
+  const int it = tid % TM, isl = (tid / TM) % SPW;
+  const uint16_t injb = a.inj[(m0 + min(it, rows - 1)) * a.ld_inj + s_first + isl];
 
   // chunk this lane moves inside its 128-byte row (rows t with t & 7 == lane >> 3)
   const uint32_t swz = (uint32_t)((lane & 7) ^ (lane >> 3));
   const uint32_t grow = (uint32_t)(lane >> 3);  // row inside an 8-row group
-  // waves 0-3 load R, y (8-token groups lw and lw + 4 of each) and, wave 0,
-  // Wnorm; waves 4-7 load weights (8-row groups g = lw + 4 j)
-  const bool wloader = wave >= 4;
-  const int lw = wave & 3;
+  // weight groups of this wave: 8-row group g = wave + 8 j of the split's rows
   uint32_t woff[WGRP];
   uint32_t winj = 0;  // bit j: group j holds inject rows
 #pragma unroll
   for (int j = 0; j < WGRP; ++j) {
-    const int g = lw + 4 * j;
+    const int g = wave + 8 * j;
     const int n = b0 * 16 + g * 8;  // r is a multiple of 8, so a group never straddles r
     const bool down = n < a.r;
-    woff[j] = g < 2 * nbw ? (uint32_t)((down ? n : n - a.r) + (int)grow) * rowb + swz * 16u : 0x80000000u;
+    woff[j] = g < 2 * nbw ? (uint32_t)((down ? n : n - a.r) + (int)grow) * rowb + swz * 16u : kOut;
     if (!down) winj |= 1u << j;
   }
   winj = __builtin_amdgcn_readfirstlane(winj);
-  const uint32_t tR = (uint32_t)(lw * 8) + grow;  // token row this lane loads (groups lw and lw + 4)
-  const uint32_t offR = tR * rowb + swz * 16u, offY = tR * (uint32_t)HS * 2u + swz * 16u;
+  // this thread's chunk of every stage: token tok, LDS slot tid & 7 (chunk swz)
+  const int tok = tid >> 3;
+  const uint32_t offR = (uint32_t)tok * rowb + swz * 16u;
+  const uint32_t offY = (uint32_t)tok * (uint32_t)HS * 2u + swz * 16u;
   const uint32_t wnc = a.folded ? 0u : (a.wn_len == HS ? 0u : 1u);  // Wnorm indexed by k
-  const uint32_t wn_lane = lane < 8 ? (uint32_t)lane * 16u : 0x80000000u;  // 8 lanes x 16 bytes = 64 values
+  const uint32_t la_off = (uint32_t)(tok * 128 + (tid & 7) * 16);
 
-  auto issue_w = [&](int s, int c0, uint8_t* wbuf) {
+  auto issue_w = [&](bool valid, int s, int c0, uint8_t* wbuf) {
     const uint32_t kb = (uint32_t)(s * HS + c0) * 2u;
-    if (!wloader) return;
 #pragma unroll
     for (int j = 0; j < WGRP; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds((winj >> j) & 1u ? rW1 : rW0,
-                                               (lds_void_t*)(wbuf + (lw + 4 * j) * 1024), 16, woff[j] + kb, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((winj >> j) & 1u ? rW1 : rW0, (lds_void_t*)(wbuf + (wave + 8 * j) * 1024),
+                                               16, valid ? woff[j] + kb : kOut, 0, 0, 0);
   };
-  auto issue_ry = [&](int s, int c0, int b) {
-    if (wloader) return;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint8_t* base = ry + b * RYB + (lw + 4 * j) * 1024;
-      const uint32_t tb = (uint32_t)(32 * j);  // + 4 groups of 8 tokens
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rR, (lds_void_t*)base, 16, offR + tb * rowb + (uint32_t)(s * HS + c0) * 2u,
-                                               0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rY, (lds_void_t*)(base + ABYTES), 16,
-                                               offY + tb * (uint32_t)HS * 2u + (uint32_t)c0 * 2u, 0, 0, 0);
-    }
-    if (lw == 0)  // the stage's Wnorm values (folded weights: a zero-length range, so 0 and a factor of 1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rWn, (lds_void_t*)(ry + b * RYB + 2 * ABYTES), 16,
-                                               wn_lane + ((wnc ? (uint32_t)(s * HS) : 0u) + (uint32_t)c0) * 2u, 0, 0, 0);
+  u32x4_t rv[D], yv[D], wv[D];  // prefetch ring: stage j in slot j % D
+  auto load_ry = [&](auto SL, bool valid, int s, int c0) {
+    constexpr int k = decltype(SL)::value;
+    const uint32_t col = (uint32_t)c0 * 2u;
+    const uint32_t oR = valid ? offR + (uint32_t)(s * HS) * 2u + col : kOut;
+    const uint32_t oY = valid ? offY + col : kOut;
+    const uint32_t oW = valid ? (wnc ? (uint32_t)(s * HS) * 2u : 0u) + col + swz * 16u : kOut;
+    rv[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rR, (int)oR, 0, 0));
+    yv[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rY, (int)oY, 0, 0));
+    wv[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rWn, (int)oW, 0, 0));
   };
 
-  // COMBINE chunk of this thread: token tid >> 3, LDS slot tid & 7
-  const int tok = tid >> 3;
-  const uint32_t la_off = (uint32_t)(tok * 128 + (tid & 7) * 16);
-  const uint32_t ry_lds = (uint32_t)(uintptr_t)(lds_u8_t*)ry;
   float ss = 0.0f, ih = 0.0f, il = 0.0f;
-  auto combine = [&](int s, int c0, int b) {
-    // R, y and Wnorm chunks in one block of LDS reads. The iteration wait
-    // already covers their global->LDS loads; reading them in asm keeps the
-    // compiler from adding a wait for the loads of later stages into the
-    // other buffers.
-    const uint32_t la = ry_lds + (uint32_t)(b * RYB) + la_off;
-    const uint32_t lwn = ry_lds + (uint32_t)(b * RYB + 2 * ABYTES) + swz * 16u;
-    u32x4_t rq4, yq4, wq4;
-    asm volatile(
-        "ds_read_b128 %0, %3\n\t"
-        "ds_read_b128 %1, %3 offset:8192\n\t"
-        "ds_read_b128 %2, %4\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(rq4), "=&v"(yq4), "=&v"(wq4)  // early clobber: results return while later reads still need la
-        : "v"(la), "v"(lwn)
-        : "memory");
-    static_assert(ABYTES == 8192, "offset above");
+  // stages past the last one combine the zeros their prefetch returned and
+  // store nothing (out-of-range R2 offset); running them keeps every ring
+  // slot consumed on every path
+  auto combine = [&](auto SL, bool valid, int s, int c0, uint8_t* abuf) {
+    constexpr int k = decltype(SL)::value;
     uint32_t o2[4], ou[4];
     float acc = ss;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float r0 = fmaf(bf_lo(yq4[e]), il, fmaf(bf_lo(yq4[e]), ih, bf_lo(rq4[e])));
-      const float r1 = fmaf(bf_hi(yq4[e]), il, fmaf(bf_hi(yq4[e]), ih, bf_hi(rq4[e])));
+      const uint32_t rw = rv[k][e], yw = yv[k][e], ww = wv[k][e];
+      const float r0 = fmaf(bf_lo(yw), il, fmaf(bf_lo(yw), ih, bf_lo(rw)));
+      const float r1 = fmaf(bf_hi(yw), il, fmaf(bf_hi(yw), ih, bf_hi(rw)));
       acc = fmaf(r0, r0, acc);
       acc = fmaf(r1, r1, acc);
       o2[e] = pack_bf2(r0, r1);
-      ou[e] = pack_bf2(r0 * (1.0f + bf_lo(wq4[e])), r1 * (1.0f + bf_hi(wq4[e])));
+      ou[e] = pack_bf2(r0 * (1.0f + bf_lo(ww)), r1 * (1.0f + bf_hi(ww)));
     }
     ss = acc;
-    bst16(rR2, (uint32_t)tok * rowb + (uint32_t)(s * HS + c0) * 2u + swz * 16u, make_uint4(o2[0], o2[1], o2[2], o2[3]));
-    const u32x4_t ov = {ou[0], ou[1], ou[2], ou[3]};
-    asm volatile("ds_write_b128 %0, %1" : : "v"(la), "v"(ov) : "memory");  // activation over R in place
+    bst16(rR2, valid ? offR + (uint32_t)(s * HS + c0) * 2u : kOut, make_uint4(o2[0], o2[1], o2[2], o2[3]));
+    *reinterpret_cast<u32x4_t*>(abuf + la_off) = u32x4_t{ou[0], ou[1], ou[2], ou[3]};
   };
   // (N) the stream's sum of squares -> rrms of this thread's token
   auto stream_rrms = [&](int sl) {
@@ -960,33 +937,40 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
 
   // (G1, INJ) contraction of one stage: A = weight rows, B = activation
   const uint32_t bfr_off = (uint32_t)((th * (TM / 2) + (lane & 15)) * 128);
-  auto contract = [&](const uint8_t* wbuf, int b) {
-    // activation fragments of both k halves in one block of LDS reads (asm,
-    // for the reason given in COMBINE)
+  auto contract = [&](const uint8_t* wbuf, const uint8_t* abuf) {
     u32x4_t bq[2][NTB];
-    const uint32_t ba = ry_lds + (uint32_t)(b * RYB) + bfr_off;
-    const uint32_t b0a = ba + (uint32_t)((((lane >> 4)) ^ (lane & 7)) * 16);
-    const uint32_t b1a = ba + (uint32_t)(((4 + (lane >> 4)) ^ (lane & 7)) * 16);
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %4 offset:2048\n\t"
-        "ds_read_b128 %2, %5\n\t"
-        "ds_read_b128 %3, %5 offset:2048\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(bq[0][0]), "=&v"(bq[0][1]), "=&v"(bq[1][0]), "=&v"(bq[1][1])  // early clobber, as in COMBINE
-        : "v"(b0a), "v"(b1a)
-        : "memory");
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int slot = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) {  // blocks past wcnt compute unused values (inside the buffer)
-        const uint4 af = *reinterpret_cast<const uint4*>(wbuf + ((qb0 + i) * 16 + (lane & 15)) * 128 + slot);
+      for (int tb = 0; tb < NTB; ++tb)
+        bq[ks][tb] = *reinterpret_cast<const u32x4_t*>(abuf + bfr_off + tb * 2048 +
+                                                       (((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16));
+    // A fragments of k half 0 up front; each is replaced by its k half 1
+    // fragment as soon as its two products have issued
+    const uint8_t* wrow = wbuf + (qb0 * 16 + (lane & 15)) * 128;
+    const int slot0 = (((lane >> 4)) ^ (lane & 7)) * 16, slot1 = ((4 + (lane >> 4)) ^ (lane & 7)) * 16;
+    uint4 af[BPW];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)  // blocks past wcnt compute unused values (inside the buffer)
+      af[i] = *reinterpret_cast<const uint4*>(wrow + i * 2048 + slot0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
-          acc_s[i][tb] = mfma16(af, __builtin_bit_cast(uint4, bq[ks][tb]), acc_s[i][tb]);
+          acc_s[i][tb] = mfma16(af[i], __builtin_bit_cast(uint4, bq[ks][tb]), acc_s[i][tb]);
+        if (ks == 0) af[i] = *reinterpret_cast<const uint4*>(wrow + i * 2048 + slot1);
       }
+    // schedule: the ten first reads, then each pair of products followed by
+    // the read that replaces its A fragment, then the last twelve products
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NTB + BPW, 0);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NTB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, NTB * BPW, 0);
   };
   auto fold = [&](int sl) {  // stream end: total += rrms_s * stream accumulator
     if constexpr (NSET) {
@@ -1003,67 +987,83 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
     }
   };
 
-  // Stage parameters (stream, column) of stages i+1 and i+3 (past the last
-  // stage they stay on it: those loads refill free buffers and are not used).
+  // stage pointers (stream, first column): stage i, i+1 and i+D; past the
+  // last stage they stay on it (the loads they drive are then out of range)
   const int s_last = s_first + SPW - 1;
   auto advance = [&](int& s, int& c) {
     if (c + 64 < c_end) c += 64;
     else if (s < s_last) { c = c_begin; ++s; }
   };
-  int s1 = s_first, c1 = c_begin, s2, c2, s3, c3;
+  int s0 = s_first, c0 = c_begin;
+  int s1 = s0, c1 = c0;
   advance(s1, c1);
-  s2 = s1; c2 = c1; advance(s2, c2);
-  s3 = s2; c3 = c2; advance(s3, c3);
+  int sD = s0, cD = c0;
 
-  // Iteration st. On entry a weight wave may have in flight the weights of
-  // stage st and R2 stores; an R/y wave the R/y (wave 0: and Wnorm) loads of
-  // stages st+1 and st+2, in issue order, and R2 stores. Loads complete in
-  // issue order but a store may complete before earlier loads, so a wait
-  // counts loads only: weight waves wait for everything, R/y waves for all
-  // but the loads of stage st+2 (4; wave 0: 5).
-  auto iteration = [&](int st, int s, int c0, uint8_t* wc, uint8_t* wnx) {
-    if (wloader) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (lw == 0) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    lds_sync();  // loads of stage st (weights) and st+1 (R/y) landed; iteration st-1 fully done
-    const int b = st & (NRY - 1);
-    issue_w(s1, c1, wnx);
-    issue_ry(s3, c3, (st + 3) & (NRY - 1));
-    if (st + 1 < nst) {
-      if (c1 == c_begin) {  // stage st+1 opens stream s1
-        ih = iwh[s1 - s_first][tok];
-        il = iwl[s1 - s_first][tok];
-      }
-      combine(s1, c1, (st + 1) & (NRY - 1));
-      if (c1 + 64 == c_end) stream_rrms(s1 - s_first);  // stage st+1 closes stream s1
-    }
-    contract(wc, b);
-    if (c0 + 64 == c_end) fold(s - s_first);  // stage st closed stream s (its rrms is visible since the barrier)
-    s1 = s2; c1 = c2;
-    s2 = s3; c2 = c3;
-    advance(s3, c3);
-  };
-
-  // prologue: weights of stage 0, R/y of stages 0-2; COMBINE of stage 0
-  issue_w(s_first, c_begin, w_0);
-  issue_ry(s_first, c_begin, 0);
-  issue_ry(s1, c1, 1);
-  issue_ry(s2, c2, 2);
-  if (!wloader) {
-    if (lw == 0) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  // prologue: weights of stage 0, R/y/Wnorm of stages 0 .. D-1
+  issue_w(true, s0, c0, w_0);
+  load_ry(ic<0>{}, true, sD, cD);
+  advance(sD, cD);
+  load_ry(ic<1>{}, 1 < nst, sD, cD);
+  advance(sD, cD);
+  load_ry(ic<2>{}, 2 < nst, sD, cD);
+  advance(sD, cD);
+  load_ry(ic<3>{}, 3 < nst, sD, cD);
+  advance(sD, cD);
+  static_assert(D == 4, "prologue and loop body above are written for a ring of four");
+  // (COMBINE) iw = 2*sigmoid(inj/HC) in fp64, kept as fp32 hi + lo
+  if (tid < SPW * TM) {
+    const double v = it < rows ? 2.0 / (1.0 + exp(-(double)bf1(injb) / (double)a.HC)) : 0.0;
+    const float hi = (float)v;
+    iwh[isl][it] = hi;
+    iwl[isl][it] = (float)(v - (double)hi);
   }
-  lds_sync();  // R/y of stage 0 and the iw table
+  lds_sync();
   ih = iwh[0][tok];
   il = iwl[0][tok];
-  combine(s_first, c_begin, 0);
-  // iterations in pairs: weights alternate w_0, w_1 (a segment holds an even number of stages)
-  int s = s_first, c0 = c_begin;
-  for (int st = 0; st < nst; st += 2) {
-    iteration(st, s, c0, w_0, w_1);
-    advance(s, c0);
-    iteration(st + 1, s, c0, w_1, w_0);
-    advance(s, c0);
+  asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // weights and R/y of stage 0
+  combine(ic<0>{}, true, s0, c0, act_0);
+  if (c0 + 64 == c_end) stream_rrms(0);
+
+  // Iteration st (slot k = st % D). On entry the newest memory operations of
+  // this thread are, in issue order: the weights of stage st, the R2 store
+  // (and, closing a column segment, a sum-of-squares store), then the
+  // R/y/Wnorm loads of stage st+D-1. The vector memory counter covers loads
+  // and stores; with the stores issued before the prefetch, vmcnt(3) leaves
+  // exactly those three prefetch loads in flight whether or not a store may
+  // complete ahead of earlier loads. Everything it waits for includes
+  // R/y/Wnorm of stage st+1 (issued D-1 iterations back).
+  auto iteration = [&](auto K, int st) {
+    constexpr int k = decltype(K)::value;
+    asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    lds_sync();  // weights of stage st landed for every wave; iteration st-1 fully done
+    uint8_t* wcur = (k & 1) ? w_1 : w_0;
+    uint8_t* wnxt = (k & 1) ? w_0 : w_1;
+    uint8_t* acur = (k & 1) ? act_1 : act_0;
+    uint8_t* anxt = (k & 1) ? act_0 : act_1;
+    const bool v1 = st + 1 < nst;
+    issue_w(v1, s1, c1, wnxt);
+    if (v1 && c1 == c_begin) {  // stage st+1 opens stream s1
+      ih = iwh[s1 - s_first][tok];
+      il = iwl[s1 - s_first][tok];
+    }
+    combine(ic<(k + 1) % D>{}, v1, s1, c1, anxt);
+    if (v1 && c1 + 64 == c_end) stream_rrms(s1 - s_first);  // stage st+1 closes stream s1
+    load_ry(K, st + D < nst, sD, cD);  // slot k held stage st, combined in iteration st-1
+    if (st < nst) {
+      contract(wcur, acur);
+      if (c0 + 64 == c_end) fold(s0 - s_first);  // stage st closed stream s0 (its rrms is visible since the barrier)
+    }
+    s0 = s1; c0 = c1;
+    advance(s1, c1);
+    advance(sD, cD);
+  };
+  // groups of four iterations (slots and buffers by position in the group);
+  // iterations past the last stage only keep the ring in step
+  for (int st = 0; st < nst; st += D) {
+    iteration(ic<0>{}, st);
+    iteration(ic<1>{}, st + 1);
+    iteration(ic<2>{}, st + 2);
+    iteration(ic<3>{}, st + 3);
   }
   // the loads issued past the last stage must land before the LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
