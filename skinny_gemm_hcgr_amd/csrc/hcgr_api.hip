@@ -173,10 +173,13 @@ hcgr_status hcgr_workspace_size_for(const hcgr_config* cfg, int64_t M, size_t* b
   return ok();
 }
 
-static const char* k2_name(int kt) { return kt == hcgr::KT_S128 ? "k2_stage" : "k2_tile"; }
-static long long k2_grid(const hcgr::Shape& s, int kt, int64_t M) {
-  const hcgr::KTShape t = hcgr::kt_shape(kt);
-  if (kt == hcgr::KT_S128) return (long long)(hcgr::cdiv(hcgr::cdiv(M, t.tm) * (s.hs / 64), 8) * 16);
+static const char* k2_name(int kt) {
+  return kt == hcgr::KT_SWEEP ? "k2_sweep" : kt == hcgr::KT_S128 ? "k2_stage" : "k2_tile";
+}
+static long long k2_grid(const hcgr::Shape& s, const hcgr::Plan& p, int64_t M) {
+  const hcgr::KTShape t = hcgr::kt_shape(p.kt);
+  if (p.kt == hcgr::KT_SWEEP) return (long long)(hcgr::cdiv(M, t.tm) * p.nranges);
+  if (p.kt == hcgr::KT_S128) return (long long)(hcgr::cdiv(hcgr::cdiv(M, t.tm) * (s.hs / 64), 8) * 16);
   return (long long)(s.hs / t.cb) * hcgr::cdiv(M, t.tm);
 }
 
@@ -204,19 +207,19 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
       hcgr::KTShape t = hcgr::kt_shape(p.kt);
       snprintf(buf, len,
                "M=%lld plan=tile | k1_tile tm=%d waves=8 stage_k=64 streams/wg=%d row_splits=%d segments=%d grid=%lld%s | "
-               "%s tm=%d channels=%d grid=%lld | workspace=%zu",
+               "%s tm=%d channels=%d ranges=%d grid=%lld | workspace=%zu",
                (long long)M, (int)hcgr::kTileTm, p.spw, p.nsplit, p.nseg,
                (long long)(hcgr::cdiv(M, hcgr::kTileTm) * p.nsplit * (4 / p.spw) * p.nseg), p.spw == 1 ? " | k1_sum" : "",
-               k2_name(p.kt), t.tm, t.cb, k2_grid(s, p.kt, M), p.ws_bytes);
+               k2_name(p.kt), t.tm, t.cb, p.nranges, k2_grid(s, p, M), p.ws_bytes);
     } else {
       hcgr::KFShape f = hcgr::kf_shape(p.kf);
       hcgr::KTShape t = hcgr::kt_shape(p.kt);
       snprintf(buf, len,
                "M=%lld plan=%s | k1_full tm=%d waves=%d stage_k=%d streams/wg=%d row_splits=%d grid=%lldx%d%s | "
-               "%s tm=%d channels=%d grid=%lld | workspace=%zu",
+               "%s tm=%d channels=%d ranges=%d grid=%lld | workspace=%zu",
                (long long)M, p.kind == hcgr::PLAN_FULL ? "full" : "stream", f.tm, f.nw, f.ks, p.spw, p.nsplit,
                (long long)hcgr::cdiv(M, f.tm), p.nsplit * (4 / p.spw), p.kind == hcgr::PLAN_STREAM ? " | k1_sum" : "",
-               k2_name(p.kt), t.tm, t.cb, k2_grid(s, p.kt, M), p.ws_bytes);
+               k2_name(p.kt), t.tm, t.cb, p.nranges, k2_grid(s, p, M), p.ws_bytes);
     }
   }
   return ok();

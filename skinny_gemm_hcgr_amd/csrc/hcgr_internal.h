@@ -86,13 +86,21 @@ inline KFShape kf_shape(int v) {
 }
 // Tiled up kernel variants: token tile, channel tile (x 4 streams).
 // KT_T64: hcgr_k2_tile (register-staged operands); KT_S128: hcgr_k2_stage
-// (operands staged by direct global->LDS loads).
-enum KTVariant { KT_T64 = 0, KT_S128 = 1, KT_NVAR };
+// (operands staged by direct global->LDS loads); KT_SWEEP: hcgr_k2_sweep
+// (h of a 128-token tile held in registers while the workgroup sweeps a
+// range of 32-channel groups).
+enum KTVariant { KT_T64 = 0, KT_S128 = 1, KT_SWEEP = 2, KT_NVAR };
 struct KTShape { int tm, cb; };
 inline KTShape kt_shape(int v) {
-  static const KTShape t[KT_NVAR] = {{64, 64}, {128, 32}};
+  static const KTShape t[KT_NVAR] = {{64, 64}, {128, 32}, {128, 32}};
   return t[v];
 }
+// hcgr_k2_sweep serves 96 <= r <= 320 (2 to 5 k stages of 64) from
+// kSweepMinM tokens, with enough channel ranges per token tile to give
+// every CU a workgroup.
+constexpr int64_t kSweepMinM = 4096;
+inline int sweep_nks(int r) { return (r + 63) / 64; }
+inline bool sweep_fits(int r) { return r >= 96 && r <= 320; }
 
 struct Shape {
   int hc, hs, r;
@@ -121,6 +129,7 @@ struct Plan {
   int nsplit = 1;                  // row-block splits of the down rows
   int nseg = 1;                    // column segments per stream (TILE, one stream per workgroup)
   int64_t mq = 0;                  // rows of the per-stream partials (STREAM)
+  int nranges = 1;                 // channel-group ranges per token tile (hcgr_k2_sweep)
   size_t off_p = 0, off_ss = 0, off_h = 0, off_q = 0, ws_bytes = 0;
 };
 
@@ -195,6 +204,12 @@ inline Plan make_plan(const Shape& s, int64_t M) {
         }
     }
     p.kt = KT_S128;
+    if (M >= kSweepMinM && sweep_fits(s.r)) {
+      p.kt = KT_SWEEP;
+      const int64_t t2 = cdiv(M, kt_shape(KT_SWEEP).tm);
+      const int ng = hs / kt_shape(KT_SWEEP).cb;
+      p.nranges = (int)(t2 >= target ? 1 : cdiv(target, t2) < ng ? cdiv(target, t2) : ng);
+    }
     p.tm = kTileTm;
     const int tm2 = kt_shape(p.kt).tm;
     p.mpad = cdiv(M, tm2) * tm2;

@@ -1582,6 +1582,329 @@ __global__ __launch_bounds__(256, 4) void hcgr_k2_stage(StageArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// hcgr_k2_sweep (large token counts): (G2) + (MIX) for a tile of 128 tokens
+// over a range of 32-channel groups (x 4 streams = 128 gate rows per group).
+// The tile's h is loaded once into registers as MFMA B fragments (NKS
+// stages of 64 k). A group's Wu rows pass through an LDS ring of NKS stages
+// (one per k stage; stage q+NKS-1 loads while stage q contracts) and its R2
+// rows and Wnorm through a double-buffered LDS area, all by direct
+// global->LDS loads. Waves 0-3 issue only Wu loads and waves 4-7 only R2
+// loads, so a wave's loads complete in issue order without one kind waiting
+// behind the other. Eight waves, two per SIMD: wave (rq, tq) owns 16
+// channels of the group (4 MFMA row blocks; row 4j+s of block gb is stream
+// s of channel 4j+gb, so lane l ends with the four streams of channels
+// 4*(l/16)+gb, gb = 0..3, and the MIX sum is lane-local) and tokens 32tq..
+// (two column blocks). A group's sigmoid + MIX epilogue runs at the next
+// group's first stage beside that stage's products.
+// ---------------------------------------------------------------------------
+struct SweepArgs {
+  const uint16_t* h;  // [>= M, r]
+  int64_t M;
+  int r, HS, K;
+  const uint16_t* wu;  // [K, r]
+  const uint16_t* R2;  // [M, K]
+  const float* rrms;   // [M, 4]
+  const uint16_t* wn;
+  int wn_len;
+  uint16_t* x;   // [M, HS]
+  int ngroups;   // HS / 32
+  int nranges;   // channel-group ranges per token tile
+};
+
+constexpr int kSweepTm = 128, kSweepCg = 32;
+constexpr int kSweepWsb = 4 * kSweepCg * 128;                    // one Wu stage: 128 rows x 64 k
+constexpr int kSweepR2b = 4 * kSweepTm * kSweepCg * 2 + 4 * 1024;  // a group's R2 (4 streams x 128 tokens x 64 B) + 4 Wnorm slots
+inline constexpr size_t sweep_lds_bytes(int nks) { return (size_t)nks * kSweepWsb + 2 * (size_t)kSweepR2b; }
+
+template <int NKS>
+__global__ __launch_bounds__(512) void hcgr_k2_sweep(SweepArgs a) {
+  constexpr int TM = kSweepTm, CG = kSweepCg, NTB = 2, WSB = kSweepWsb, R2B = kSweepR2b;
+  constexpr int R2S = TM * CG * 2;  // one stream of a group's R2 (8 KB)
+  constexpr uint32_t kOut = 0x80000000u;
+  static_assert(NKS >= 2 && NKS <= 5, "ring of 2..5 k stages");
+  static_assert(sweep_lds_bytes(5) <= 160 * 1024, "LDS of one CU");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t dl[];
+  uint8_t* wring = dl;              // [NKS][128 rows][128 B]
+  uint8_t* r2buf = dl + NKS * WSB;  // [2]{[4 streams][TM tokens][64 B], [4][1 KB Wnorm slot]}
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rq = wave & 1, tq = wave >> 1;
+  const int64_t tiles = (a.M + TM - 1) / TM;
+  const int64_t tile = (int64_t)blockIdx.x % tiles;
+  const int range = (int)((int64_t)blockIdx.x / tiles);
+  const int g_begin = range * a.ngroups / a.nranges, g_end = (range + 1) * a.ngroups / a.nranges;
+  const int64_t m0 = tile * TM;
+  const int rows = (int)min((int64_t)TM, a.M - m0);
+  const uint32_t rowb = (uint32_t)a.K * 2u, hrow = (uint32_t)a.r * 2u;
+
+  const rsrc_t rH = make_rsrc(a.h + m0 * a.r, (uint32_t)rows * hrow);
+  const rsrc_t rWu = make_rsrc(a.wu, (uint32_t)a.K * hrow);
+  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, (uint32_t)rows * rowb);
+  const rsrc_t rRr = make_rsrc(a.rrms + m0 * 4, (uint32_t)rows * 16u);
+  const rsrc_t rWn = make_rsrc(a.wn, (uint32_t)a.wn_len * 2u);
+  const rsrc_t rX = make_rsrc(a.x + m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
+
+  // h of the lane's tokens as B fragments (past r: zeros), and their rrms
+  u32x4_t hf[NKS][2][NTB];
+  f32x4_t rrv[NTB];
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    const uint32_t t = (uint32_t)(tq * 32 + tb * 16 + (lane & 15));
+#pragma unroll
+    for (int j = 0; j < NKS; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int k = j * 64 + ks * 32 + 8 * (lane >> 4);
+        hf[j][ks][tb] = __builtin_bit_cast(u32x4_t, bld16(rH, k < a.r ? t * hrow + (uint32_t)k * 2u : kOut));
+      }
+    rrv[tb] = __builtin_bit_cast(f32x4_t, bld16(rRr, t * 16u));
+  }
+
+  // Wu loads (waves 0-3): 8-row groups G = wave + 4 i (i < 4) of the 128
+  // stage rows; LDS row rl = 16 blk + 4 jj + s holds stream s of channel
+  // 16 (blk / 4) + 4 jj + (blk % 4) of the group, its 16-byte chunk c in slot
+  // c ^ (rl & 7); k past r reads zeros
+  const uint32_t swz = (uint32_t)((lane & 7) ^ (lane >> 3));
+  uint32_t woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = ((wave & 3) + 4 * i) * 8 + (lane >> 3);
+    const int blk = rl >> 4, jj = (rl >> 2) & 3, s = rl & 3;
+    woff[i] = (uint32_t)(s * a.HS + 16 * (blk >> 2) + 4 * jj + (blk & 3)) * hrow + swz * 16u;
+  }
+  auto issue_wu = [&](bool valid, int g, int j) {  // !valid: past the sweep, reads zeros
+    uint8_t* buf = wring + j * WSB;
+    const uint32_t base = (uint32_t)(g * CG) * hrow + (uint32_t)j * 128u;
+    const bool inr = valid && j * 64 + (int)swz * 8 < a.r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rWu, (lds_void_t*)(buf + ((wave & 3) + 4 * i) * 1024), 16,
+                                               inr ? woff[i] + base : kOut, 0, 0, 0);
+  };
+  // R2 loads (waves 4-7): instruction n = wave - 4 + 4 i (i < 8) moves stream
+  // n / 8, tokens 16 (n % 8) .. +15, 64 bytes each (lane: token lane / 4,
+  // chunk lane % 4); then one Wnorm load per wave into its 1 KB slot (wave 4:
+  // the group's values, the others: zeros)
+  auto issue_r2 = [&](bool valid, int g, int b) {  // !valid: past the sweep, reads zeros
+    uint8_t* buf = r2buf + b * R2B;
+    const int c0 = g * CG;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = (wave - 4) + 4 * i, s = n >> 3;
+      const uint32_t t = (uint32_t)((n & 7) * 16 + (lane >> 2));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rR2, (lds_void_t*)(buf + s * R2S + (n & 7) * 1024), 16,
+          valid ? t * rowb + (uint32_t)(s * a.HS + c0) * 2u + (uint32_t)(lane & 3) * 16u : kOut, 0, 0, 0);
+    }
+    const bool full = a.wn_len != a.HS;
+    const bool live = valid && wave == 4 && lane < (full ? 16 : 4);
+    const uint32_t wo = (uint32_t)((full ? (lane >> 2) * a.HS : 0) + c0 + (full ? (lane & 3) : lane) * 8) * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWn, (lds_void_t*)(buf + 4 * R2S + (wave - 4) * 1024), 16,
+                                             live ? wo : kOut, 0, 0, 0);
+  };
+
+  f32x4_t acc[4][NTB];
+#pragma unroll
+  for (int gb = 0; gb < 4; ++gb)
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) acc[gb][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // (G2) one k stage: A = the wave's 64 Wu rows, B = h fragments. Past r (a
+  // half last stage) both operands are zeros, so the second k step of that
+  // stage adds nothing and runs unconditionally.
+  const uint32_t wbase = (uint32_t)(uintptr_t)(lds_u8_t*)wring + (uint32_t)((rq * 64 + (lane & 15)) * 128);
+  const uint32_t slot0 = (uint32_t)(((lane >> 4) ^ (lane & 7)) * 16);
+  const uint32_t slot1 = (uint32_t)(((4 + (lane >> 4)) ^ (lane & 7)) * 16);
+  typedef u32x4_t afrag_t[2][4];
+  auto load_a = [&](auto J, afrag_t& af) {
+    constexpr int j = decltype(J)::value;
+    const uint32_t wa = wbase + (uint32_t)(j * WSB);
+    const uint32_t a0 = wa + slot0, a1 = wa + slot1;
+    // every LDS read here is covered by the stage wait; one asm block with its
+    // wait inside, so the outputs are complete when it ends and the compiler
+    // adds no wait for the ring's later loads
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:2048\n\t"
+        "ds_read_b128 %2, %8 offset:4096\n\t"
+        "ds_read_b128 %3, %8 offset:6144\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "ds_read_b128 %5, %9 offset:2048\n\t"
+        "ds_read_b128 %6, %9 offset:4096\n\t"
+        "ds_read_b128 %7, %9 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0][0]), "=&v"(af[0][1]), "=&v"(af[0][2]), "=&v"(af[0][3]), "=&v"(af[1][0]), "=&v"(af[1][1]),
+          "=&v"(af[1][2]), "=&v"(af[1][3])
+        : "v"(a0), "v"(a1)
+        : "memory");
+  };
+  auto products = [&](auto J, const afrag_t& af) {
+    constexpr int j = decltype(J)::value;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int gb = 0; gb < 4; ++gb)
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+          acc[gb][tb] = mfma16(__builtin_bit_cast(uint4, af[ks][gb]), __builtin_bit_cast(uint4, hf[j][ks][tb]),
+                               acc[gb][tb]);
+  };
+
+  // (G2) sigmoid + (MIX) of a finished group: x of the lane's 4 channels for
+  // each column block. The LDS reads (R2 and Wnorm of the group) come first,
+  // apart from the arithmetic, so that the arithmetic can interleave with a
+  // stage's products.
+  const uint32_t r2lane = (uint32_t)(uintptr_t)(lds_u8_t*)r2buf + (uint32_t)(rq * 32 + 8 * (lane >> 4));
+  const uint32_t wstep = a.wn_len != a.HS ? 64u : 0u;  // Wnorm indexed by k: one 64-byte row per stream
+  struct EpiIn { u32x2_t wv[4], rv[NTB][4]; };
+  auto epi_load = [&](int b, EpiIn& e) {
+    const uint32_t rb = r2lane + (uint32_t)(b * R2B);
+    const uint32_t wa = rb + (uint32_t)(4 * R2S);
+    const uint32_t t0 = rb + (uint32_t)(tq * 32 + (lane & 15)) * 64u;  // column block 0; block 1 is 16 tokens on
+    static_assert(NTB == 2 && R2S == 8192, "offsets below");
+    asm volatile(
+        "ds_read_b64 %0, %12\n\t"
+        "ds_read_b64 %1, %13\n\t"
+        "ds_read_b64 %2, %14\n\t"
+        "ds_read_b64 %3, %15\n\t"
+        "ds_read_b64 %4, %16\n\t"
+        "ds_read_b64 %5, %16 offset:8192\n\t"
+        "ds_read_b64 %6, %16 offset:16384\n\t"
+        "ds_read_b64 %7, %16 offset:24576\n\t"
+        "ds_read_b64 %8, %16 offset:1024\n\t"
+        "ds_read_b64 %9, %16 offset:9216\n\t"
+        "ds_read_b64 %10, %16 offset:17408\n\t"
+        "ds_read_b64 %11, %16 offset:25600\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(e.wv[0]), "=&v"(e.wv[1]), "=&v"(e.wv[2]), "=&v"(e.wv[3]), "=&v"(e.rv[0][0]), "=&v"(e.rv[0][1]),
+          "=&v"(e.rv[0][2]), "=&v"(e.rv[0][3]), "=&v"(e.rv[1][0]), "=&v"(e.rv[1][1]), "=&v"(e.rv[1][2]),
+          "=&v"(e.rv[1][3])
+        : "v"(wa), "v"(wa + wstep), "v"(wa + 2u * wstep), "v"(wa + 3u * wstep), "v"(t0)
+        : "memory");
+  };
+  // live = false: the x stores go out of range (dropped)
+  auto epi_math = [&](const EpiIn& e, bool live, int g, const f32x4_t (&ac)[4][NTB]) {
+    float onep[4][4];  // [s][gb]
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      onep[s][0] = 1.0f + bf_lo(e.wv[s][0]);
+      onep[s][1] = 1.0f + bf_hi(e.wv[s][0]);
+      onep[s][2] = 1.0f + bf_lo(e.wv[s][1]);
+      onep[s][3] = 1.0f + bf_hi(e.wv[s][1]);
+    }
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      float xq[4];
+#pragma unroll
+      for (int gb = 0; gb < 4; ++gb) {
+        float gs[4], xn[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t w = gb < 2 ? e.rv[tb][s][0] : e.rv[tb][s][1];
+          const float r2 = (gb & 1) ? bf_hi(w) : bf_lo(w);
+          gs[s] = ac[gb][tb][s];
+          xn[s] = r2 * rrv[tb][s] * onep[s][gb];
+        }
+        xq[gb] = mix4(gs, xn);
+      }
+      const uint32_t t = (uint32_t)(tq * 32 + tb * 16 + (lane & 15));
+      bst8(rX, live ? (t * (uint32_t)a.HS + (uint32_t)(g * CG + rq * 16 + 4 * (lane >> 4))) * 2u : kOut,
+           make_uint2(pack_bf2(xq[0], xq[1]), pack_bf2(xq[2], xq[3])));
+    }
+  };
+
+  // prologue: Wu of stages 0 .. NKS-2 of the first group (waves 0-3), R2 of
+  // the first group (waves 4-7); h and rrms above
+  if (wave < 4) {
+#pragma unroll
+    for (int j = 0; j < NKS - 1; ++j) issue_wu(true, g_begin, j);
+  } else {
+    issue_r2(true, g_begin, 0);
+  }
+  // vmcnt(0) through the builtin (0x0f70: expcnt and lgkmcnt left open), so the
+  // compiler also knows the h and rrms registers have landed
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  lds_sync();
+
+  // Stage (g, j). At its top a Wu wave has issued the Wu of every stage up to
+  // (g, j) + NKS - 2, 4 loads per stage (stages past the sweep included, as
+  // out-of-range loads, so the count never changes); vmcnt(4 (NKS - 2))
+  // counts later loads only (a store may complete ahead of earlier loads) and
+  // leaves the NKS - 2 newer stages in flight. Stage (g, j) loads the Wu of
+  // stage (g, j) + NKS - 1 into ring slot j - 1 (read by the previous stage).
+  // The epilogue of group g runs at stage (g + 1, 0), beside that stage's
+  // products, from the accumulators set aside at the end of group g; so
+  // R2(g) must stay until then, and R2(g + 1) loads at stage (g, 1) into the
+  // other buffer (free once the epilogue of g - 1 is done). At stage
+  // (g + 1, 0) an R2 wave waits for R2(g) with the 9 loads of R2(g + 1) left
+  // in flight.
+  f32x4_t accp[4][NTB];  // group g - 1, waiting for its epilogue
+#pragma unroll
+  for (int gb = 0; gb < 4; ++gb)
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) accp[gb][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int g = g_begin; g < g_end; ++g) {
+    const int b = (g - g_begin) & 1;
+    auto stage = [&](auto J) {
+      constexpr int j = decltype(J)::value;
+      if (g != g_begin || j != 0) {
+        if (wave < 4) {
+          if constexpr (NKS == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          else if constexpr (NKS == 3) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+          else if constexpr (NKS == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+          else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+        } else if (j == 0) {
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        }
+        lds_sync();
+      }
+      if (wave < 4) {
+        constexpr int q2 = j + NKS - 1;  // stage (g, q2), or (g + 1, q2 - NKS)
+        const int gn = q2 >= NKS ? g + 1 : g;
+        issue_wu(gn < g_end, gn, q2 >= NKS ? q2 - NKS : q2);
+      } else if (j == 1) {
+        issue_r2(g + 1 < g_end, g + 1, b ^ 1);
+      }
+      afrag_t af;
+      load_a(J, af);
+      if constexpr (j == 0) {  // the previous group's epilogue beside this stage's products
+        EpiIn e;
+        epi_load(b ^ 1, e);
+        products(J, af);
+        epi_math(e, g != g_begin, g - 1, accp);
+      } else {
+        products(J, af);
+      }
+      if constexpr (j == NKS - 1) {
+#pragma unroll
+        for (int gb = 0; gb < 4; ++gb)
+#pragma unroll
+          for (int tb = 0; tb < NTB; ++tb) {
+            accp[gb][tb] = acc[gb][tb];
+            acc[gb][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+      }
+    };
+    stage(ic<0>{});
+    stage(ic<1>{});
+    if constexpr (NKS > 2) stage(ic<2>{});
+    if constexpr (NKS > 3) stage(ic<3>{});
+    if constexpr (NKS > 4) stage(ic<4>{});
+  }
+  // the last group's epilogue
+  if (wave >= 4) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_sync();
+  {
+    EpiIn e;
+    epi_load((g_end - 1 - g_begin) & 1, e);
+    epi_math(e, true, g_end - 1, accp);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // Every launch goes through hipExtLaunchKernelGGL: with a pair of timing
 // events (start, stop) the runtime stamps them at the kernel's own start and
 // end, so per-kernel durations exclude the dispatch gaps between kernels.
@@ -1632,6 +1955,10 @@ int configure_kernels() {
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<16, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<32, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<64, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
+  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(2))) != hipSuccess) return (int)e;
+  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<3>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(3))) != hipSuccess) return (int)e;
+  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(4))) != hipSuccess) return (int)e;
+  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<5>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(5))) != hipSuccess) return (int)e;
   return (int)hipSuccess;
 }
 
@@ -1746,7 +2073,20 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   t.h = H; t.M = f.M; t.r = s.r; t.HS = s.hs; t.K = K;
   t.wu = f.wu; t.R2 = f.R2; t.rrms = f.rrms; t.wn = f.wnorm; t.wn_len = s.wn_full ? K : s.hs; t.x = f.x;
   const KTShape ts = kt_shape(p.kt);
-  if (p.kt == KT_S128) {
+  if (p.kt == KT_SWEEP) {
+    SweepArgs wa;
+    wa.h = H; wa.M = f.M; wa.r = s.r; wa.HS = s.hs; wa.K = K; wa.wu = f.wu; wa.R2 = f.R2; wa.rrms = f.rrms;
+    wa.wn = f.wnorm; wa.wn_len = s.wn_full ? K : s.hs; wa.x = f.x; wa.ngroups = s.hs / kSweepCg; wa.nranges = p.nranges;
+    const dim3 g2((unsigned)(cdiv(f.M, (int64_t)kSweepTm) * p.nranges));
+    const int nks = sweep_nks(s.r);
+    switch (nks) {
+      case 2: klaunch(hcgr_k2_sweep<2>, g2, dim3(512), sweep_lds_bytes(2), st, tm.stage(2), wa); break;
+      case 3: klaunch(hcgr_k2_sweep<3>, g2, dim3(512), sweep_lds_bytes(3), st, tm.stage(2), wa); break;
+      case 4: klaunch(hcgr_k2_sweep<4>, g2, dim3(512), sweep_lds_bytes(4), st, tm.stage(2), wa); break;
+      case 5: klaunch(hcgr_k2_sweep<5>, g2, dim3(512), sweep_lds_bytes(5), st, tm.stage(2), wa); break;
+      default: return (int)hipErrorInvalidValue;  // make_plan takes this kernel for 2..5 k stages only
+    }
+  } else if (p.kt == KT_S128) {
     StageArgs sa;
     sa.h = H; sa.M = f.M; sa.r = s.r; sa.HS = s.hs; sa.K = K; sa.wu = f.wu; sa.R2 = f.R2; sa.rrms = f.rrms;
     sa.wn = f.wnorm; sa.wn_len = s.wn_full ? K : s.hs; sa.x = f.x; sa.npairs = s.hs / 64;

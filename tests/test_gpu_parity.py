@@ -168,6 +168,29 @@ def test_tile_plan_shapes(H, hs, r, M):
     o.close()
 
 
+@pytest.mark.parametrize("hs,r,M", [(256, 96, 4200), (512, 160, 4096), (384, 224, 4225), (256, 256, 4096),
+                                    (512, 288, 5000), (2560, 320, 4096)])
+def test_sweep_up_kernel_shapes(H, hs, r, M):
+    """The up kernel that sweeps 32-channel groups with h held in registers,
+    at every ring depth (2 to 5 k stages of 64), with half last stages
+    (r % 64 == 32), one to five groups per channel range, uneven ranges and
+    a last token tile of one token (M = 4225)."""
+    shape = synth.Shape(hs=hs, r=r)
+    o = H.HCGR(H.Config(hs=hs, r=r), 0)
+    plan = H.hcgr_describe_plan(o.cfg, M)
+    _say(f"[parity] sweep up kernel hs={hs} r={r} M={M}: {plan}")
+    assert "k2_sweep" in plan
+    inp = synth.make_inputs(M, shape, seed=13, device="cuda")
+    out = gpu_forward(o, inp)
+    rows = sample_rows(M, 64)
+    cfg = oracle.OracleConfig(hs=hs, r=r)
+    idx = torch.as_tensor(rows, device="cuda")
+    ref = oracle.forward(cfg, inp["R"][idx].cpu(), inp["y"][idx].cpu(), inp["inj"][idx].cpu(), inp["wnorm"].cpu(),
+                         inp["wd"].cpu(), inp["wi"].cpu(), inp["wu"].cpu())
+    check_all(out, ref, rows)
+    o.close()
+
+
 def test_full_width_wnorm_large(H):
     """Wnorm indexed by k (length HC*HS) on the large-M path."""
     o = H.HCGR(H.Config(wnorm_len=SHAPE.k), 0)
