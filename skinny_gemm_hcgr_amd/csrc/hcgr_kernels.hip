@@ -350,8 +350,10 @@ __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
 // each) and its h tile arrive in LDS by direct global->LDS loads (wide 1 KB
 // instructions instead of per-lane fragment loads); inside a row the 16-byte
 // chunk c sits in slot (c & ~3) | ((c ^ row) & 3), which spreads the 16-row
-// fragment reads over the banks. R2, rrms and Wnorm of the epilogue are
-// loaded into registers meanwhile. Wave w owns channels 4w..4w+3: MFMA row
+// fragment reads over the banks. The epilogue's R2 rows, rrms and Wnorm
+// arrive the same way (a few wide loads instead of many 2- and 4-byte ones),
+// and the channel groups that share a 128-byte line of R2 or x run on one
+// XCD. Wave w owns channels 4w..4w+3: MFMA row
 // 4*c + s is stream s of channel c (Wu row s*HS + c), so lane l ends with the
 // four streams of channel w*4 + l/16 for token l%16 and the MIX sum is
 // lane-local.
@@ -378,13 +380,25 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k2_dec(UpArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t m0 = (int64_t)blockIdx.y * TM;
   const int rows = (int)min((int64_t)TM, a.M - m0);
-  const int cbase = blockIdx.x * (NW * 4);
+  // channel groups of NW*4 channels; workgroup x goes to XCD x % 8 (the
+  // dispatcher's round robin), so XCD k takes a contiguous run of groups and
+  // the groups that share a 128-byte line of R2 or x share that XCD's L2
+  const int ncg = (int)gridDim.x;  // a multiple of 8
+  const int cbase = ((blockIdx.x & 7) * (ncg >> 3) + (blockIdx.x >> 3)) * (NW * 4);
   const int cpr = a.r / 8;  // 16-byte chunks per row (a multiple of 4)
   const uint32_t rowb = (uint32_t)a.r * 2u;
+  constexpr int CW = NW * 4;              // channels of the workgroup
+  constexpr int RRB = (TM > 64 ? TM : 64) * 16;  // rrms slot: one 16-byte lane per token, 64 lanes at least
   uint8_t* wl = dl;              // [WR][r]: row 4*cl + s = stream s of channel cbase + cl
   uint8_t* hl = dl + WR * rowb;  // [TM][r]
+  uint8_t* r2l = hl + TM * rowb;  // [TM][4 streams][CW channels] bf16
+  uint8_t* rrl = r2l + TM * 4 * CW * 2;  // [TM][4] float
+  uint8_t* wnl = rrl + RRB;              // [4 streams or 1][CW] bf16 (1 KB slot)
   const rsrc_t rWu = make_rsrc(a.wu, (uint32_t)a.K * rowb);
   const rsrc_t rH = make_rsrc(a.h + m0 * a.r, (uint32_t)rows * rowb);  // rows past M read as zero
+  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, (uint32_t)rows * (uint32_t)a.K * 2u);
+  const rsrc_t rRr = make_rsrc(a.rrms + m0 * 4, (uint32_t)rows * 16u);
+  const rsrc_t rWn = make_rsrc(a.wn, (uint32_t)(a.wn_full ? a.K : a.HS) * 2u);
 
   // global -> LDS: instruction i fills LDS chunks [64 i, 64 i + 64) of a
   // block; WR*cpr and TM*cpr are multiples of 64
@@ -400,23 +414,43 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k2_dec(UpArgs a) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rH, (lds_void_t*)(hl + i * 1024), 16, (uint32_t)row * rowb + (uint32_t)c * 16u,
                                              0, 0, 0);
   }
-  // epilogue operands: lane holds streams q = 0..3 of channel c for token m
-  const int c = cbase + wave * 4 + (lane >> 4);
-  float pr2[NTB][4], prr[NTB][4], pone[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) pone[q] = 1.0f + bf1(a.wn[a.wn_full ? q * a.HS + c : c]);
-#pragma unroll
-  for (int tb = 0; tb < NTB; ++tb) {
-    const int64_t m = m0 + tb * 16 + (lane & 15);
-    const int64_t mc = m < a.M ? m : a.M - 1;  // clamped: no branch around the load
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      pr2[tb][q] = bf1(a.R2[mc * a.K + q * a.HS + c]);
-      prr[tb][q] = a.rrms[mc * 4 + q];
-    }
+  // epilogue operands, also global -> LDS: the tile's R2 rows of the
+  // workgroup's channels (lane: token q / 8, stream (q / 2) % 4, half q % 2),
+  // its rrms rows and the channels' Wnorm
+  static_assert(TM % 8 == 0 && CW == 16, "R2 slots: 8 per token, 64 per instruction");
+  for (int i = wave; i < TM / 8; i += NW) {
+    const int q = i * 64 + lane, t = q >> 3, sq = (q >> 1) & 3;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rR2, (lds_void_t*)(r2l + i * 1024), 16,
+        (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)(sq * a.HS + cbase + (q & 1) * 8) * 2u, 0, 0, 0);
+  }
+  if (wave == 0) {
+    for (int i = 0; i * 64 < TM; ++i)  // lanes past the tile read zeros into the slot
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rRr, (lds_void_t*)(rrl + i * 1024), 16,
+                                               (uint32_t)(i * 64 + lane) * 16u, 0, 0, 0);
+    const bool live = lane < (a.wn_full ? 8 : 2);
+    const uint32_t wo = (uint32_t)((a.wn_full ? (lane >> 1) * a.HS : 0) + cbase + (lane & 1) * 8) * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWn, (lds_void_t*)wnl, 16, live ? wo : 0x80000000u, 0, 0, 0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_sync();  // every wave's global->LDS loads have landed
+
+  // lane holds streams q = 0..3 of channel c for token m
+  const int cl = wave * 4 + (lane >> 4), c = cbase + cl;
+  float pr2[NTB][4], prr[NTB][4], pone[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    pone[q] = 1.0f + bf1(*reinterpret_cast<const uint16_t*>(wnl + ((a.wn_full ? q * CW : 0) + cl) * 2));
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    const int t = tb * 16 + (lane & 15);
+    const f32x4_t rr = *reinterpret_cast<const f32x4_t*>(rrl + t * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pr2[tb][q] = bf1(*reinterpret_cast<const uint16_t*>(r2l + (t * 4 + q) * (CW * 2) + cl * 2));
+      prr[tb][q] = rr[q];
+    }
+  }
 
   f32x4_t acc[NTB];
 #pragma unroll
@@ -1950,7 +1984,7 @@ static void launch_kt(const TileArgs& t, dim3 grid, hipStream_t st, const hipEve
 }
 
 int configure_kernels() {
-  const int lim = 128 * 1024;  // (64 + 64) rows of r <= 512 values
+  const int lim = 160 * 1024;  // (64 + 64) rows of r <= 512 values, plus the epilogue operands
   hipError_t e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<16, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<32, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
@@ -2006,7 +2040,9 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   u.h = H; u.Mpad = p.mpad; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = K;
   u.wu = f.wu; u.R2 = f.R2; u.rrms = f.rrms; u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0;
   u.x = f.x;
-  const size_t lds = (size_t)(kDecUpWaves * 16 + p.tm) * (size_t)s.r * sizeof(uint16_t);
+  const size_t lds = (size_t)(kDecUpWaves * 16 + p.tm) * (size_t)s.r * sizeof(uint16_t)  // Wu rows, h tile
+                    + (size_t)p.tm * 4 * (kDecUpWaves * 4) * sizeof(uint16_t)             // R2 rows
+                    + (size_t)(p.tm > 64 ? p.tm : 64) * 16 + 1024;                          // rrms, Wnorm
   const dim3 g2((unsigned)(s.hs / p.cb), (unsigned)(p.mpad / p.tm));
   const dim3 b2(kDecUpWaves * 64);
   switch (p.k2) {
