@@ -194,14 +194,25 @@ inline Plan make_plan(const Shape& s, int64_t M) {
     p.spw = tiles * tsplit >= target ? 4 : 1;
     p.nsplit = tsplit;
     // below one workgroup per CU, split each stream's columns into segments
-    // (an even number of 64-column stages each); hcgr_k1_sum then forms rrms
+    // (an even number of 64-column stages each); hcgr_k1_sum then forms rrms.
+    // The count minimises a cost fitted to measurements on MI355X (HS = 2560,
+    // r = 320), in microseconds: per round of workgroups on the CUs, a fixed
+    // 8.5 plus 1.3 per stage (the down kernel runs stages in groups of four),
+    // and per segment 0.4 + 0.0004 per token for writing and summing the
+    // partials. It depends on M only through the token tile count, so every M
+    // with the same tile count gets the same plan (the workspace bound below
+    // relies on that).
     if (p.spw == 1) {
       const int pairs = s.hs / 128;
-      for (int d = 1; d <= pairs; ++d)
-        if (pairs % d == 0) {
-          p.nseg = d;
-          if (tiles * 4 * tsplit * d >= target) break;
-        }
+      const double mt = (double)(tiles * kTileTm);
+      double best = 1e300;
+      for (int d = 1; d <= pairs; ++d) {
+        if (pairs % d != 0) continue;
+        const int64_t rounds = cdiv(tiles * 4 * tsplit * d, target);
+        const int64_t nst = cdiv(2 * pairs / d, 4) * 4;
+        const double cost = (double)rounds * (8.5 + 1.3 * (double)nst) + (double)d * (0.4 + 0.0004 * mt);
+        if (cost < best) { best = cost; p.nseg = d; }
+      }
     }
     p.kt = KT_S128;
     if (M >= kSweepMinM && sweep_fits(s.r)) {
