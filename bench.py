@@ -68,7 +68,7 @@ def kernel_bytes(name, M, merged=False, plan=""):
         return wdown + M * (act_in + out)
     if name == "hcgr_k1_sum":
         return M * HC * 2                       # inj_next out
-    if name in ("hcgr_k2_dec", "hcgr_k2_tile", "hcgr_k2_stage", "hcgr_k2_sweep"):
+    if name in ("hcgr_k2_dec", "hcgr_k2_stage", "hcgr_k2_sweep"):
         return K * R_LOW * 2 + HS * 2 + M * (K * 2 + HC * 4 + HS * 2)  # Wu, Wnorm; R2, rrms in; x out
     raise KeyError(name)
 
@@ -76,7 +76,7 @@ def kernel_bytes(name, M, merged=False, plan=""):
 def kernel_flops(name, M):
     if name in ("hcgr_k1_dec", "hcgr_k1_full", "hcgr_k1_tile"):
         return M * 2 * (R_LOW + HC) * K
-    if name in ("hcgr_k2_dec", "hcgr_k2_tile", "hcgr_k2_stage", "hcgr_k2_sweep"):
+    if name in ("hcgr_k2_dec", "hcgr_k2_stage", "hcgr_k2_sweep"):
         return M * 2 * R_LOW * K
     return 0
 
@@ -86,7 +86,7 @@ def stage_names(plan: str):
     a plan has no kernel between two marks)."""
     if "plan=split" in plan:
         return ("hcgr_k1_dec", "hcgr_k1_reduce", "hcgr_k2_dec")
-    up = "hcgr_k2_sweep" if "k2_sweep" in plan else "hcgr_k2_stage" if "k2_stage" in plan else "hcgr_k2_tile"
+    up = "hcgr_k2_sweep" if "k2_sweep" in plan else "hcgr_k2_stage"
     if "plan=tile" in plan:
         return ("hcgr_k1_tile", "hcgr_k1_sum" if "streams/wg=1" in plan else None, up)
     if "plan=stream" in plan:

@@ -173,14 +173,11 @@ hcgr_status hcgr_workspace_size_for(const hcgr_config* cfg, int64_t M, size_t* b
   return ok();
 }
 
-static const char* k2_name(int kt) {
-  return kt == hcgr::KT_SWEEP ? "k2_sweep" : kt == hcgr::KT_S128 ? "k2_stage" : "k2_tile";
-}
+static const char* k2_name(int kt) { return kt == hcgr::KT_SWEEP ? "k2_sweep" : "k2_stage"; }
 static long long k2_grid(const hcgr::Shape& s, const hcgr::Plan& p, int64_t M) {
   const hcgr::KTShape t = hcgr::kt_shape(p.kt);
   if (p.kt == hcgr::KT_SWEEP) return (long long)(hcgr::cdiv(M, t.tm) * p.nranges);
-  if (p.kt == hcgr::KT_S128) return (long long)(hcgr::cdiv(hcgr::cdiv(M, t.tm) * (s.hs / 64), 8) * 16);
-  return (long long)(s.hs / t.cb) * hcgr::cdiv(M, t.tm);
+  return (long long)(hcgr::cdiv(hcgr::cdiv(M, t.tm) * (s.hs / 64), 8) * 16);
 }
 
 hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, size_t len) {

@@ -85,14 +85,13 @@ inline KFShape kf_shape(int v) {
   return t[v];
 }
 // Tiled up kernel variants: token tile, channel tile (x 4 streams).
-// KT_T64: hcgr_k2_tile (register-staged operands); KT_S128: hcgr_k2_stage
-// (operands staged by direct global->LDS loads); KT_SWEEP: hcgr_k2_sweep
-// (h of a 128-token tile held in registers while the workgroup sweeps a
-// range of 32-channel groups).
-enum KTVariant { KT_T64 = 0, KT_S128 = 1, KT_SWEEP = 2, KT_NVAR };
+// KT_S128: hcgr_k2_stage (operands staged by direct global->LDS loads);
+// KT_SWEEP: hcgr_k2_sweep (h of a 128-token tile held in registers while the
+// workgroup sweeps a range of 32-channel groups).
+enum KTVariant { KT_S128 = 0, KT_SWEEP = 1, KT_NVAR };
 struct KTShape { int tm, cb; };
 inline KTShape kt_shape(int v) {
-  static const KTShape t[KT_NVAR] = {{64, 64}, {128, 32}, {128, 32}};
+  static const KTShape t[KT_NVAR] = {{128, 32}, {128, 32}};
   return t[v];
 }
 // hcgr_k2_sweep serves 96 <= r <= 320 (2 to 5 k stages of 64) from

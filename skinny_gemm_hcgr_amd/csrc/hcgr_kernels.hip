@@ -1238,32 +1238,6 @@ __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// hcgr_k2_tile: (G2) + (MIX) for a tile of 64 tokens x 64 channels (x 4
-// streams), 4 waves; wave (wt, wc) owns tokens wt*32.. and channels wc*32..
-// for all 4 streams. MFMA: A = Wu rows (channels), B = h^T (tokens), both
-// staged per 32-wide k step through double-buffered LDS (50 KB per
-// workgroup, so three workgroups share a CU and one's epilogue overlaps
-// another's contraction). Lane l ends with channels 4*(l/16)..+3 of token
-// l%16 of each (token block, channel block, stream), so the MIX sum over
-// streams is lane-local and each lane moves 8 contiguous bytes of R2 and x.
-// R2 and rrms of the lane are loaded into registers two k steps before the
-// end. All global accesses are unconditional buffer accesses whose
-// descriptors end at row M (loads past it read 0, stores past it are
-// dropped).
-// ---------------------------------------------------------------------------
-struct TileArgs {
-  const uint16_t* h;
-  int64_t M;
-  int r, HS, K;
-  const uint16_t* wu;
-  const uint16_t* R2;
-  const float* rrms;
-  const uint16_t* wn;
-  int wn_len;
-  uint16_t* x;
-};
-
 // x = 1/4 sum_s xn_s sigmoid(g_s) with one reciprocal: d_s = 1 + e^(-g_s),
 // sum_s xn_s / d_s = N / D, D = d0 d1 d2 d3, N = (xn0 d1 + xn1 d0) d2 d3 +
 // (xn2 d3 + xn3 d2) d0 d1. g is clamped below at -20 so that D stays finite
@@ -1276,169 +1250,6 @@ __device__ __forceinline__ float mix4(const float g[4], const float xn[4]) {
   const float n01 = fmaf(xn[0], d[1], xn[1] * d[0]);
   const float n23 = fmaf(xn[2], d[3], xn[3] * d[2]);
   return 0.25f * fmaf(n01, d23, n23 * d01) * __builtin_amdgcn_rcpf(d01 * d23);
-}
-
-template <int TM, int CB>
-struct TileLds {
-  static constexpr int LDK = 40;                // padded k row (32 + 8), bf16 elements
-  static constexpr int H_ELEMS = TM * LDK;      // one h stage
-  static constexpr int W_ELEMS = 4 * CB * LDK;  // one Wu stage
-};
-
-template <int TM, int CB>
-__global__ __launch_bounds__(256) void hcgr_k2_tile(TileArgs a) {
-  using L = TileLds<TM, CB>;
-  constexpr int LDK = L::LDK;
-  constexpr int NT = TM / 32;   // token blocks per wave
-  constexpr int NJ = CB / 32;   // channel blocks per wave
-  constexpr int HPT = TM * 4 / 256, WPT = 4 * CB * 4 / 256;
-  static_assert(HPT >= 1 && (TM * 4) % 256 == 0 && (4 * CB * 4) % 256 == 0, "whole chunks per thread");
-
-  __shared__ __attribute__((aligned(16))) uint16_t hs[2][L::H_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][L::W_ELEMS];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wt = wave & 1, wc = wave >> 1;
-  const int c0 = blockIdx.x * CB;
-  const int64_t m0 = (int64_t)blockIdx.y * TM;
-  const int rows = (int)min((int64_t)TM, a.M - m0);
-  const int koff = 8 * (lane >> 4);
-  const int nk = a.r / 32;
-  const uint32_t rowb = (uint32_t)a.K * 2u;
-  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, (uint32_t)rows * rowb);
-  const rsrc_t rX = make_rsrc(a.x + m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
-  const rsrc_t rRr = make_rsrc(a.rrms + m0 * 4, (uint32_t)rows * 16u);
-
-  // lane coordinates: channel cl..cl+3 of block j, token tl of block tb
-  const int tl = wt * (TM / 2) + (lane & 15);             // + tb*16
-  const int cl = wc * (CB / 2) + 4 * (lane >> 4);         // + j*16
-  // (1 + Wnorm) of the lane's channels
-  float onep[NJ][4][4];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint2 w = *reinterpret_cast<const uint2*>(a.wn + (a.wn_len == a.HS ? 0 : s * a.HS) + c0 + cl + j * 16);
-      onep[j][s][0] = 1.0f + bf_lo(w.x);
-      onep[j][s][1] = 1.0f + bf_hi(w.x);
-      onep[j][s][2] = 1.0f + bf_lo(w.y);
-      onep[j][s][3] = 1.0f + bf_hi(w.y);
-    }
-
-  uint4 hv[HPT], wv[WPT];
-  auto load_stage = [&](int kk) {
-    const int k0 = kk * 32;
-#pragma unroll
-    for (int j = 0; j < HPT; ++j) {
-      const int q = tid + j * 256;
-      hv[j] = ld16(a.h + (m0 + (q >> 2)) * a.r + k0 + (q & 3) * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      const int q = tid + j * 256;
-      const int row = q >> 2;  // s*CB + channel
-      wv[j] = ld16(a.wu + ((int64_t)(row / CB) * a.HS + c0 + row % CB) * a.r + k0 + (q & 3) * 8);
-    }
-  };
-  auto store_stage = [&](int b) {
-#pragma unroll
-    for (int j = 0; j < HPT; ++j) {
-      const int q = tid + j * 256;
-      st16(&hs[b][(q >> 2) * LDK + (q & 3) * 8], hv[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      const int q = tid + j * 256;
-      st16(&ws[b][(q >> 2) * LDK + (q & 3) * 8], wv[j]);
-    }
-  };
-
-  f32x4_t acc[NT][NJ][4];
-#pragma unroll
-  for (int tb = 0; tb < NT; ++tb)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc[tb][j][s] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  auto compute = [&](int b) {
-    uint4 bfr[NT];
-#pragma unroll
-    for (int tb = 0; tb < NT; ++tb)
-      bfr[tb] = *reinterpret_cast<const uint4*>(&hs[b][(tl + tb * 16) * LDK + koff]);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 af = *reinterpret_cast<const uint4*>(
-            &ws[b][(s * CB + wc * (CB / 2) + j * 16 + (lane & 15)) * LDK + koff]);
-#pragma unroll
-        for (int tb = 0; tb < NT; ++tb) acc[tb][j][s] = mfma16(af, bfr[tb], acc[tb][j][s]);
-      }
-  };
-
-  // epilogue operands, loaded two k steps before the end
-  uint2 r2v[NT][NJ][4];
-  f32x4_t rrv[NT];
-  auto load_epilogue = [&]() {
-#pragma unroll
-    for (int tb = 0; tb < NT; ++tb) {
-      const uint32_t t = tl + tb * 16;
-      rrv[tb] = __builtin_bit_cast(f32x4_t, bld16(rRr, t * 16u));
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          r2v[tb][j][s] = bld8(rR2, t * rowb + (uint32_t)(s * a.HS + c0 + cl + j * 16) * 2u);
-    }
-  };
-
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  int kk = 0;
-  for (; kk + 2 < nk; ++kk) {  // every step but the last two: prefetch, contract, stage
-    load_stage(kk + 1);
-    compute(kk & 1);
-    store_stage((kk + 1) & 1);
-    __syncthreads();
-  }
-  if (kk + 1 < nk) {  // second to last step: stage the last k step, then the epilogue loads
-    load_stage(kk + 1);
-    load_epilogue();
-    compute(kk & 1);
-    store_stage((kk + 1) & 1);
-    __syncthreads();
-    ++kk;
-  } else {
-    load_epilogue();
-  }
-  compute(kk & 1);  // last step: no load
-
-  // epilogue: (G2) sigmoid and (MIX) over the lane's four stream accumulators
-#pragma unroll
-  for (int tb = 0; tb < NT; ++tb) {
-    const uint32_t t = tl + tb * 16;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      float xo[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float g[4], xn[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint32_t w = (q < 2) ? r2v[tb][j][s].x : r2v[tb][j][s].y;
-          const float r2 = (q & 1) ? bf_hi(w) : bf_lo(w);
-          g[s] = acc[tb][j][s][q];
-          xn[s] = r2 * rrv[tb][s] * onep[j][s][q];
-        }
-        xo[q] = mix4(g, xn);
-      }
-      bst8(rX, (t * (uint32_t)a.HS + c0 + cl + j * 16) * 2u, make_uint2(pack_bf2(xo[0], xo[1]), pack_bf2(xo[2], xo[3])));
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1978,11 +1789,6 @@ template <int TM, int NW, int BPW, int KS>
 static void launch_kf(const FullArgs& f, dim3 grid, hipStream_t st, const hipEvent_t* ev) {
   klaunch(hcgr_k1_full<TM, NW, BPW, KS>, grid, dim3(NW * 64), 0, st, ev, f);
 }
-template <int TM, int CB>
-static void launch_kt(const TileArgs& t, dim3 grid, hipStream_t st, const hipEvent_t* ev) {
-  klaunch(hcgr_k2_tile<TM, CB>, grid, dim3(256), 0, st, ev, t);
-}
-
 int configure_kernels() {
   const int lim = 160 * 1024;  // (64 + 64) rows of r <= 512 values, plus the epilogue operands
   hipError_t e;
@@ -2105,9 +1911,6 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     return (int)e;
   }
 
-  TileArgs t;
-  t.h = H; t.M = f.M; t.r = s.r; t.HS = s.hs; t.K = K;
-  t.wu = f.wu; t.R2 = f.R2; t.rrms = f.rrms; t.wn = f.wnorm; t.wn_len = s.wn_full ? K : s.hs; t.x = f.x;
   const KTShape ts = kt_shape(p.kt);
   if (p.kt == KT_SWEEP) {
     SweepArgs wa;
@@ -2122,15 +1925,12 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
       case 5: klaunch(hcgr_k2_sweep<5>, g2, dim3(512), sweep_lds_bytes(5), st, tm.stage(2), wa); break;
       default: return (int)hipErrorInvalidValue;  // make_plan takes this kernel for 2..5 k stages only
     }
-  } else if (p.kt == KT_S128) {
+  } else {
     StageArgs sa;
     sa.h = H; sa.M = f.M; sa.r = s.r; sa.HS = s.hs; sa.K = K; sa.wu = f.wu; sa.R2 = f.R2; sa.rrms = f.rrms;
     sa.wn = f.wnorm; sa.wn_len = s.wn_full ? K : s.hs; sa.x = f.x; sa.npairs = s.hs / 64;
     const int64_t pairs = cdiv(f.M, (int64_t)ts.tm) * sa.npairs;
     klaunch(hcgr_k2_stage, dim3((unsigned)(cdiv(pairs, 8) * 16)), dim3(256), 0, st, tm.stage(2), sa);
-  } else {
-    dim3 g2((unsigned)(s.hs / ts.cb), (unsigned)cdiv(f.M, ts.tm));
-    launch_kt<64, 64>(t, g2, st, tm.stage(2));
   }
   return (int)hipGetLastError();
 }

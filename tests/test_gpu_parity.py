@@ -191,6 +191,28 @@ def test_sweep_up_kernel_shapes(H, hs, r, M):
     o.close()
 
 
+@pytest.mark.parametrize("hs,r,M,kind", [(4352, 64, 1, "stream"), (4352, 64, 20, "stream"), (4224, 64, 8, "full"),
+                                         (4224, 64, 64, "full")])
+def test_fallback_plans_small_m(H, hs, r, M, kind):
+    """Decode token counts whose stream width no decode K chunk divides (HS =
+    34*128: 34 chunks of 128 are too many for the reduction, 512 does not
+    divide it; HS = 33*128 likewise, with an odd stage count): the one-stream
+    (partials summed by hcgr_k1_sum) and four-stream forms of hcgr_k1_full,
+    then the staged up kernel."""
+    shape = synth.Shape(hs=hs, r=r)
+    o = H.HCGR(H.Config(hs=hs, r=r), 0)
+    plan = H.hcgr_describe_plan(o.cfg, M)
+    _say(f"[parity] fallback plan hs={hs} r={r} M={M}: {plan}")
+    assert f"plan={kind}" in plan
+    inp = synth.make_inputs(M, shape, seed=17, device="cuda")
+    out = gpu_forward(o, inp)
+    cfg = oracle.OracleConfig(hs=hs, r=r)
+    ref = oracle.forward(cfg, inp["R"].cpu(), inp["y"].cpu(), inp["inj"].cpu(), inp["wnorm"].cpu(), inp["wd"].cpu(),
+                         inp["wi"].cpu(), inp["wu"].cpu())
+    check_all(out, ref)
+    o.close()
+
+
 def test_full_width_wnorm_large(H):
     """Wnorm indexed by k (length HC*HS) on the large-M path."""
     o = H.HCGR(H.Config(wnorm_len=SHAPE.k), 0)
@@ -345,10 +367,13 @@ def test_forward_timed_matches_forward(H, op, weights, M):
                              [e.cuda_event for e in ev[:5]] + [0])
 
 
-def test_graph_capture_replays(op, weights):
+@pytest.mark.parametrize("M", [48, 4160])
+def test_graph_capture_replays(op, weights, M):
     """hcgr_forward captured into a HIP graph: several replays with new input
-    values written between them, each checked against an eager call."""
-    M = 48
+    values written between them, each checked against an eager call (bitwise)
+    and the first against the oracle. M = 48 is the decode plan; M = 4160 the
+    tile plan with column segments, the segment sum and the sweeping up
+    kernel (oracle on sampled rows)."""
     inp = synth.make_inputs(M, SHAPE, seed=11, device="cuda", weights=weights)
     out = op.alloc_outputs(M)
     ws = op.workspace(M)
@@ -373,7 +398,11 @@ def test_graph_capture_replays(op, weights):
         for k in ("R2", "rrms", "inj_next", "x"):
             assert torch.equal(out[k], eager[k]), (rep, k)
         if rep == 0:
-            check_all(out, run_oracle(fresh))
+            if M <= 64:
+                check_all(out, run_oracle(fresh))
+            else:
+                rows = sample_rows(M, 48)
+                check_all(out, run_oracle(fresh, rows), rows)
 
 
 def test_m0_and_errors_on_device(H, op, weights):
