@@ -136,7 +136,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest M served by the SPLIT plan.
-constexpr int64_t kSplitMaxM = 64;
+constexpr int64_t kSplitMaxM = 128;
 // TILE plan: 64-token down kernel (hcgr_k1_tile) with at most 22 16-row
 // blocks per workgroup (4 row quarters of at most 6); taken from kTileMinM
 // tokens: one stream per workgroup (split into column segments while that
@@ -180,7 +180,7 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   const int hs = s.hs;
   const size_t np = (size_t)s.np();
   if (M <= kSplitMaxM) {
-    const int kd = M <= 16 ? KD_T16_R7_K1_C128 : M <= 32 ? KD_T32_R7_K1_C128 : KD_T64_R7_K1_C128;
+    const int kd = M <= 16 ? KD_T16_R7_K1_C128 : M <= 32 ? KD_T32_R7_K1_C128 : M <= 64 ? KD_T64_R7_K1_C128 : KD_T64_R3_K1_C256;
     const int kd_wide = M <= 16 ? KD_T16_R3_K2_C512 : M <= 32 ? KD_T32_R3_K2_C512 : KD_T64_R3_K1_C256;
     if (make_split(s, M, kd, &p) || make_split(s, M, kd_wide, &p)) return p;
   }

@@ -383,8 +383,9 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k2_dec(UpArgs a) {
   // channel groups of NW*4 channels; workgroup x goes to XCD x % 8 (the
   // dispatcher's round robin), so XCD k takes a contiguous run of groups and
   // the groups that share a 128-byte line of R2 or x share that XCD's L2
-  const int ncg = (int)gridDim.x;  // a multiple of 8
-  const int cbase = ((blockIdx.x & 7) * (ncg >> 3) + (blockIdx.x >> 3)) * (NW * 4);
+  const int ncg = (int)gridDim.x;  // HS / 16: a multiple of 8 for every accepted HS
+  const int cg = (ncg & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (ncg >> 3) + (blockIdx.x >> 3));
+  const int cbase = cg * (NW * 4);
   const int cpr = a.r / 8;  // 16-byte chunks per row (a multiple of 4)
   const uint32_t rowb = (uint32_t)a.r * 2u;
   constexpr int CW = NW * 4;              // channels of the workgroup
