@@ -213,6 +213,33 @@ def test_fallback_plans_small_m(H, hs, r, M, kind):
     o.close()
 
 
+GRID_SHAPES = [(128, 32), (384, 96), (640, 160), (1152, 224), (256, 512), (1408, 288)]
+GRID_M = [1, 17, 65, 130, 700, 4100]
+
+
+@pytest.mark.parametrize("hs,r,M", [(hs, r, M) for hs, r in GRID_SHAPES for M in GRID_M] +
+                         [(128, 32, 16400), (640, 160, 16400)])
+def test_shape_grid(H, hs, r, M):
+    """Every plan and kernel variant across shapes: decode chunks that do or
+    do not divide the stream (hs = 128 with M = 65 falls through to the tile
+    plan), 1 to 11 column segments (some with a stage count that is not a
+    multiple of four), row splits (r = 512), half last k stages in the up
+    kernels (r % 64 == 32), both tiled up kernels, and four streams per down
+    workgroup at M = 16400. Oracle on sampled rows."""
+    shape = synth.Shape(hs=hs, r=r)
+    o = H.HCGR(H.Config(hs=hs, r=r), 0)
+    _say(f"[parity] grid hs={hs} r={r} M={M}: {H.hcgr_describe_plan(o.cfg, M)}")
+    inp = synth.make_inputs(M, shape, seed=hs + r + M, device="cuda")
+    out = gpu_forward(o, inp)
+    rows = sample_rows(M, 24)
+    cfg = oracle.OracleConfig(hs=hs, r=r)
+    idx = torch.as_tensor(rows, device="cuda")
+    ref = oracle.forward(cfg, inp["R"][idx].cpu(), inp["y"][idx].cpu(), inp["inj"][idx].cpu(), inp["wnorm"].cpu(),
+                         inp["wd"].cpu(), inp["wi"].cpu(), inp["wu"].cpu())
+    check_all(out, ref, rows)
+    o.close()
+
+
 def test_full_width_wnorm_large(H):
     """Wnorm indexed by k (length HC*HS) on the large-M path."""
     o = H.HCGR(H.Config(wnorm_len=SHAPE.k), 0)
