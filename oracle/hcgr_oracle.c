@@ -26,6 +26,13 @@
  * Every bf16 input is widened exactly to double; every step runs in double
  * in the order the page lists, one token at a time.
  *
+ * Besides the whole op, the same pull request's "PR Self-Review" section lists
+ * a combine-only entry point and a mix entry point. Reading taken here (the
+ * page names them without formulas): combine = (COMBINE) alone, giving R2;
+ * mix = every other step applied to a residual that needs no injection, that
+ * is R2 = R, giving rrms, inj_next and x. Both run through the loop below
+ * with the other part switched off.
+ *
  * Parity pins for each step live in the test-suite (closed forms, invariants
  * and one-hot special cases); none of them calls this file's arithmetic twice.
  */
@@ -67,34 +74,39 @@ static double* widen_all(const uint16_t* src, int64_t n)
 
 static double logistic(double v) { return 1.0 / (1.0 + exp(-v)); }
 
-/* Returns 0 on success, -1 on a bad argument, -2 on allocation failure.
- * Outputs (double, row-major): R2 [M,K], rrms [M,HC], inj_next [M,HC],
- * x [M,HS]. Optional intermediates (pass NULL to skip): xn [M,K],
- * lora [M,r], h [M,r], gate [M,K], G [M,K]. */
-int hcgr_oracle_forward(const hcgr_oracle_cfg* cfg, int64_t M,
-                        const uint16_t* R, const uint16_t* y,
-                        const uint16_t* inj, int64_t ld_inj,
-                        const uint16_t* wnorm, const uint16_t* wd,
-                        const uint16_t* wi, const uint16_t* wu,
-                        double* R2_out, double* rrms_out, double* inj_next_out,
-                        double* x_out, double* xn_dbg, double* lora_dbg,
-                        double* h_dbg, double* gate_dbg, double* G_dbg,
-                        int nthreads)
+/* Which parts of the op run_tokens computes. */
+enum { PART_COMBINE = 1, PART_MIX = 2 };
+
+/* The op, or one of its two parts, for M tokens. With PART_COMBINE the
+ * residual is R2 = R + y*iw; without it R2 = R (y and inj are not read).
+ * With PART_MIX the steps N, G1, INJ, G2 and MIX follow; without it only R2
+ * is produced (the weights are not read). */
+static int run_tokens(const hcgr_oracle_cfg* cfg, int64_t M, int parts,
+                      const uint16_t* R, const uint16_t* y,
+                      const uint16_t* inj, int64_t ld_inj,
+                      const uint16_t* wnorm, const uint16_t* wd,
+                      const uint16_t* wi, const uint16_t* wu,
+                      double* R2_out, double* rrms_out, double* inj_next_out,
+                      double* x_out, double* xn_dbg, double* lora_dbg,
+                      double* h_dbg, double* gate_dbg, double* G_dbg,
+                      int nthreads)
 {
-    if (!cfg || M < 0 || cfg->hc < 1 || cfg->hs < 1 || cfg->r < 1 || ld_inj < cfg->hc)
+    if (!cfg || M < 0 || cfg->hc < 1 || cfg->hs < 1 || cfg->r < 1)
         return -1;
-    if (cfg->merged && cfg->n_pad < cfg->r + cfg->hc) return -1;
+    if ((parts & PART_COMBINE) && ld_inj < cfg->hc) return -1;
+    if ((parts & PART_MIX) && cfg->merged && cfg->n_pad < cfg->r + cfg->hc) return -1;
     if (M == 0) return 0;
     const int HC = cfg->hc, HS = cfg->hs, RR = cfg->r;
     const int64_t K = (int64_t)HC * HS;
     const int64_t wlen = cfg->wnorm_full ? K : HS;
     const int64_t down_rows = cfg->merged ? cfg->n_pad : RR;
+    const int mix = (parts & PART_MIX) != 0;
 
-    double* Wn = widen_all(wnorm, wlen);
-    double* Wd = widen_all(wd, down_rows * K);         /* Wd [r,K] or Wm [n_pad,K] */
-    double* Wi = cfg->merged ? NULL : widen_all(wi, (int64_t)HC * K);
-    double* Wu = widen_all(wu, K * RR);                /* Wu [K,r]                 */
-    if (!Wn || !Wd || !Wu || (!cfg->merged && !Wi)) {
+    double* Wn = mix ? widen_all(wnorm, wlen) : NULL;
+    double* Wd = mix ? widen_all(wd, down_rows * K) : NULL;          /* Wd [r,K] or Wm [n_pad,K] */
+    double* Wi = (mix && !cfg->merged) ? widen_all(wi, (int64_t)HC * K) : NULL;
+    double* Wu = mix ? widen_all(wu, K * RR) : NULL;                 /* Wu [K,r]                 */
+    if (mix && (!Wn || !Wd || !Wu || (!cfg->merged && !Wi))) {
         free(Wn); free(Wd); free(Wi); free(Wu);
         return -2;
     }
@@ -126,16 +138,24 @@ int hcgr_oracle_forward(const hcgr_oracle_cfg* cfg, int64_t M,
         for (int64_t m = 0; m < M; ++m) {
             if (!ok) continue;
             const uint16_t* Rm = R + m * K;
-            const uint16_t* ym = y + m * HS;
-            const uint16_t* im = inj + m * ld_inj;
-
-            /* (COMBINE) injection weights: iw[s] = 2 * sigmoid(inj[s] / HC) */
-            for (int s = 0; s < HC; ++s)
-                iw[s] = 2.0 * logistic(widen_bf16(im[s]) / HC);
-            /* (COMBINE) next residual: R2[s,c] = R[s,c] + y[c] * iw[s] */
-            for (int s = 0; s < HC; ++s)
-                for (int c = 0; c < HS; ++c)
-                    r2[(int64_t)s * HS + c] = widen_bf16(Rm[(int64_t)s * HS + c]) + widen_bf16(ym[c]) * iw[s];
+            if (parts & PART_COMBINE) {
+                const uint16_t* ym = y + m * HS;
+                const uint16_t* im = inj + m * ld_inj;
+                /* (COMBINE) injection weights: iw[s] = 2 * sigmoid(inj[s] / HC) */
+                for (int s = 0; s < HC; ++s)
+                    iw[s] = 2.0 * logistic(widen_bf16(im[s]) / HC);
+                /* (COMBINE) next residual: R2[s,c] = R[s,c] + y[c] * iw[s] */
+                for (int s = 0; s < HC; ++s)
+                    for (int c = 0; c < HS; ++c)
+                        r2[(int64_t)s * HS + c] = widen_bf16(Rm[(int64_t)s * HS + c]) + widen_bf16(ym[c]) * iw[s];
+            } else {
+                /* mix entry: no injection, the residual is R itself */
+                for (int64_t k = 0; k < K; ++k) r2[k] = widen_bf16(Rm[k]);
+            }
+            if (!mix) {
+                if (R2_out) memcpy(R2_out + m * K, r2, sizeof(double) * K);
+                continue;
+            }
 
             /* (N) per-stream reciprocal RMS: rrms[s] = 1 / sqrt(mean_c R2[s,c]^2 + eps) */
             for (int s = 0; s < HC; ++s) {
@@ -204,6 +224,49 @@ int hcgr_oracle_forward(const hcgr_oracle_cfg* cfg, int64_t M,
     }
     free(Wn); free(Wd); free(Wi); free(Wu);
     return status;
+}
+
+/* The whole op. Returns 0 on success, -1 on a bad argument, -2 on
+ * allocation failure. Outputs (double, row-major): R2 [M,K], rrms [M,HC],
+ * inj_next [M,HC], x [M,HS]. Optional intermediates (pass NULL to skip):
+ * xn [M,K], lora [M,r], h [M,r], gate [M,K], G [M,K]. */
+int hcgr_oracle_forward(const hcgr_oracle_cfg* cfg, int64_t M,
+                        const uint16_t* R, const uint16_t* y,
+                        const uint16_t* inj, int64_t ld_inj,
+                        const uint16_t* wnorm, const uint16_t* wd,
+                        const uint16_t* wi, const uint16_t* wu,
+                        double* R2_out, double* rrms_out, double* inj_next_out,
+                        double* x_out, double* xn_dbg, double* lora_dbg,
+                        double* h_dbg, double* gate_dbg, double* G_dbg,
+                        int nthreads)
+{
+    return run_tokens(cfg, M, PART_COMBINE | PART_MIX, R, y, inj, ld_inj, wnorm, wd, wi, wu,
+                      R2_out, rrms_out, inj_next_out, x_out, xn_dbg, lora_dbg, h_dbg, gate_dbg,
+                      G_dbg, nthreads);
+}
+
+/* (COMBINE) alone: R2 [M,K] from R, y and the (row stride ld_inj) logits. */
+int hcgr_oracle_combine(const hcgr_oracle_cfg* cfg, int64_t M,
+                        const uint16_t* R, const uint16_t* y,
+                        const uint16_t* inj, int64_t ld_inj,
+                        double* R2_out, int nthreads)
+{
+    return run_tokens(cfg, M, PART_COMBINE, R, y, inj, ld_inj, NULL, NULL, NULL, NULL,
+                      R2_out, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, nthreads);
+}
+
+/* Every step but COMBINE, on a residual R [M,K] that is taken as R2:
+ * rrms [M,HC], inj_next [M,HC], x [M,HS] (+ the optional intermediates). */
+int hcgr_oracle_mix(const hcgr_oracle_cfg* cfg, int64_t M, const uint16_t* R,
+                    const uint16_t* wnorm, const uint16_t* wd,
+                    const uint16_t* wi, const uint16_t* wu,
+                    double* rrms_out, double* inj_next_out, double* x_out,
+                    double* xn_dbg, double* lora_dbg, double* h_dbg,
+                    double* gate_dbg, double* G_dbg, int nthreads)
+{
+    return run_tokens(cfg, M, PART_MIX, R, NULL, NULL, 0, wnorm, wd, wi, wu,
+                      NULL, rrms_out, inj_next_out, x_out, xn_dbg, lora_dbg, h_dbg, gate_dbg,
+                      G_dbg, nthreads);
 }
 
 /* Number of threads an OpenMP parallel region of this library would use. */

@@ -424,4 +424,59 @@ def pin_decimal_small(lib):
         close(o[k], ref[k], rel=1e-12, abs_=1e-15)
 
 
+# ------------------------------------------- combine and mix entry points --
+def pin_combine_entry_closed_form(lib):
+    """(COMBINE entry point) with logits (HC, -HC, 2HC, 0) the injection weights
+    have the closed forms 2e/(e+1), 2/(e+1), 2e^2/(e^2+1) and 1, so R2 = R +
+    y*iw for random bf16 R and y; the logits sit in a strided view (row stride
+    HC + 3, padding 1000) that must not be read. Catches an entry point that
+    skips the injection, reads the wrong stream's logit or ignores the stride."""
+    cfg = TINY
+    e = math.e
+    iw = np.array([2 * e / (e + 1), 2 / (e + 1), 2 * e * e / (e * e + 1), 1.0])
+    d = rand_inputs(cfg, 3)
+    ld = cfg.hc + 3
+    inj = bf(np.full((3, ld), 1000.0))
+    inj[:, :cfg.hc] = bf([[cfg.hc, -cfg.hc, 2 * cfg.hc, 0]] * 3)
+    o = oracle.combine(cfg, d["R"], d["y"], inj, ld_inj=ld, lib_path=lib)
+    R = widen(d["R"]).reshape(3, cfg.hc, cfg.hs)
+    y = widen(d["y"]).reshape(3, 1, cfg.hs)
+    # the two sides' iw may differ in the last bit; where R and y*iw cancel that
+    # shows against the (small) result, so the bound adds a few ulps of |y*iw|
+    close(o["R2"].reshape(3, cfg.hc, cfg.hs), R + y * iw[None, :, None], rel=1e-15,
+          abs_=4e-16 * 2 * np.abs(y).max())
+
+
+def pin_mix_entry_decimal(lib):
+    """(mix entry point) HC=2, HS=8, r=4: rrms, inj_next and x of the mix entry
+    agree to 1e-12 relative with the 40-digit decimal evaluation of the six
+    steps with y = 0 (then R2 = R whatever the logits). Catches a mix entry
+    that injects, rescales or mis-indexes the residual."""
+    cfg = oracle.OracleConfig(hc=2, hs=8, r=4)
+    d = rand_inputs(cfg, 2, wd_std=0.7, wu_std=1.5)
+    o = oracle.mix(cfg, d["R"], d["wnorm"], d["wd"], d["wi"], d["wu"], lib_path=lib)
+    zero_y = np.zeros(d["y"].shape)
+    ref = _decimal_forward(cfg, widen(d["R"]), zero_y, widen(d["inj"]), widen(d["wnorm"]),
+                           widen(d["wd"]), widen(d["wi"]), widen(d["wu"]))
+    for k in ("rrms", "inj_next", "x"):
+        close(o[k], ref[k], rel=1e-12, abs_=1e-15)
+
+
+def pin_mix_entry_wd_zero(lib):
+    """(mix entry point) Wd = 0 and Wi = 0 give h = 0, G = 1/2, inj_next = 0,
+    so x[c] = (1/(2 HC)) sum_s xn[s,c]; with Wnorm = 0 and a constant stream s
+    equal to a_s, xn[s,c] = a_s/sqrt(a_s^2 + eps). Catches a mix entry that
+    drops the norm or the gate."""
+    cfg = TINY
+    d = rand_inputs(cfg, 1)
+    a = np.array([0.5, -2.0, 3.0, 0.25])
+    R = np.repeat(a, cfg.hs)[None, :]
+    o = oracle.mix(cfg, bf(R), bf(np.zeros(cfg.hs)), np.zeros_like(d["wd"]), np.zeros_like(d["wi"]),
+                   d["wu"], lib_path=lib)
+    xn = a / np.sqrt(a * a + cfg.eps)
+    assert np.all(o["inj_next"] == 0.0)
+    close(o["rrms"][0], 1.0 / np.sqrt(a * a + cfg.eps), rel=1e-15)
+    close(o["x"][0], np.full(cfg.hs, xn.sum() / (2 * cfg.hc)), rel=1e-14)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -67,6 +67,11 @@ MUTANTS = [
     ("mix_sums_r2", "acc += G[(int64_t)s * HS + c] * xn[(int64_t)s * HS + c];",
      "acc += G[(int64_t)s * HS + c] * r2[(int64_t)s * HS + c];"),
     ("mix_missing_div_hc", "x_out[m * HS + c] = acc / HC;", "x_out[m * HS + c] = acc;"),
+    ("mix_entry_stream0_residual", "r2[k] = widen_bf16(Rm[k]);", "r2[k] = widen_bf16(Rm[k % HS]);"),
+    ("mix_entry_doubles_residual", "r2[k] = widen_bf16(Rm[k]);", "r2[k] = 2.0 * widen_bf16(Rm[k]);"),
+    ("combine_entry_drops_injection",
+     "if (R2_out) memcpy(R2_out + m * K, r2, sizeof(double) * K);\n                continue;",
+     "if (R2_out) for (int64_t k = 0; k < K; ++k) R2_out[m * K + k] = widen_bf16(Rm[k]);\n                continue;"),
 ]
 
 _CHILD = r"""
