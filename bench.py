@@ -97,10 +97,10 @@ def stage_names(plan: str):
 class Sets:
     """NB independent buffer sets (inputs, weights, outputs, workspace) for M tokens."""
 
-    def __init__(self, H, op, M, nb, merged=False, scale_stream0=1.0, seed0=0):
+    def __init__(self, H, op, M, nb, merged=False, scale_stream0=1.0, seed0=0, entry="forward"):
         import torch
         import synth
-        self.M, self.nb, self.merged = M, nb, merged
+        self.M, self.nb, self.merged, self.entry = M, nb, merged, entry
         sh = synth.Shape(HC, HS, R_LOW)
         self.sets = []
         for i in range(nb):
@@ -114,6 +114,13 @@ class Sets:
 
     def call(self, H, op, i, stream, events=None):
         inp, out, ws = self.sets[i % self.nb]
+        if self.entry == "combine":
+            H.hcgr_combine(op.handle, inp["R"], inp["y"], inp["inj"], inp["inj"].stride(0), self.M, out["R2"], stream)
+            return
+        if self.entry == "mix":
+            H.hcgr_mix(op.handle, inp["R"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"], self.M, out["rrms"],
+                       out["inj_next"], out["ld_inj_next"], out["x"], ws, ws.numel(), stream)
+            return
         args = (op.handle, inp["R"], inp["y"], inp["inj"], inp["inj"].stride(0), inp["wnorm"], inp["wd"], inp["wi"],
                 inp["wu"], self.M, out["R2"], out["rrms"], out["inj_next"], out["ld_inj_next"], out["x"], ws,
                 ws.numel(), stream)
@@ -299,6 +306,28 @@ def cpu_baseline(M, budget_s=12.0):
             "us_per_call": round(dt / n * 1e6, 1)}
 
 
+def entry_bytes(entry, M):
+    """Algorithmic bytes of one call of the combine-only or mix entry point."""
+    if entry == "combine":  # R, y, inj in; R2 out
+        return M * (K * 2 + HS * 2 + HC * 2 + K * 2)
+    # mix: weights once; R in; rrms, inj_next, x out
+    return op_bytes(0) + M * (K * 2 + HC * 4 + HC * 2 + HS * 2)
+
+
+def run_entry(H, op, entry, M, steps, stream):
+    nb = 1 if entry == "combine" else set_count(M)
+    sets = Sets(H, op, M, nb, entry=entry)
+    us, _ = time_calls(H, op, sets, steps, 5, stream)
+    B = entry_bytes(entry, M)
+    gbs = B / (us * 1e-6) / 1e9
+    del sets
+    return {"entry": entry, "M": M, "buffer_sets": nb, "us_per_call": round(us, 3),
+            "tokens_per_s": round(M / (us * 1e-6), 1), "alg_bytes": B, "achieved_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+ENTRY_RUNS = [("combine", 8192), ("combine", 65536), ("mix", 32), ("mix", 8192)]
+
 WORKLOADS = {
     "decode_m1": (1, False, 1.0),
     "decode_m32": (32, False, 1.0),
@@ -367,6 +396,15 @@ def main():
             sweep.append(r)
             torch.cuda.empty_cache()
 
+    entries = []
+    if not args.no_sweep:
+        for entry, m in ENTRY_RUNS:
+            r = run_entry(H, op, entry, m, max(10, min(args.steps, int(2e5 / m) + 10)), stream)
+            print(f"[bench] {entry} M={m}: {r['us_per_call']} us/call, {r['achieved_gbs']} GB/s", file=sys.stderr,
+                  flush=True)
+            entries.append(r)
+            torch.cuda.empty_cache()
+
     dom = max(head["kernels_us"], key=lambda k: head["kernels_us"][k])
     roof = roofline_entry(dom, M, head["kernels_us"][dom], merged, head["plan"], args.workload)
     line = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
@@ -391,6 +429,8 @@ def main():
         line["sweep"] = [{k: r[k] for k in ("workload", "M", "us_per_call", "us_per_call_graph", "tokens_per_s",
                                             "op_roofline_frac", "op_hbm_frac", "op_mfma_frac", "kernels_us")}
                          for r in sweep]
+    if entries:
+        line["entries"] = entries
     if args.json_out:
         with open(args.json_out, "w") as f:
             json.dump({"line": line, "headline": head, "warm": warm, "sweep": sweep}, f, indent=1)

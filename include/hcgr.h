@@ -166,6 +166,53 @@ hcgr_status hcgr_validate(const hcgr_config* cfg,
                           const uint16_t* x,
                           const void* workspace, size_t workspace_bytes);
 
+/* (COMBINE) alone, for M tokens on `stream`:
+ *   R2[m, s*HS + c] = R[m, s*HS + c] + y[m, c] * iw[m, s],
+ *   iw[m, s] = 2*sigmoid(inj[m*ld_inj + s] / HC)
+ * (the "Technical Details" step of the aiter pull request; the page's "PR
+ * Self-Review" section lists this combine-only entry point beside the whole
+ * op, for a layer whose block output is injected but whose mixed input is
+ * not needed). R [M, K] and y [M, HS] as in hcgr_forward; inj is read at row
+ * stride ld_inj >= HC (a previous call's strided inj_next view is allowed);
+ * R2 [M, K] bf16, round-to-nearest-even of the fp32 value. No workspace.
+ * Alignment: R, y, R2 16 bytes; inj 2. M == 0 returns HCGR_OK and touches
+ * nothing. Errors: HCGR_ERR_INVALID_ARGUMENT (M < 0, NULL or misaligned
+ * pointer, ld_inj < HC, stream of another device), HCGR_ERR_ALIASING (R2
+ * overlaps R, y or inj), HCGR_ERR_HIP (launch failure); nothing is launched
+ * on error. */
+hcgr_status hcgr_combine(hcgr_handle h, const uint16_t* R, const uint16_t* y,
+                         const uint16_t* inj, int64_t ld_inj, int64_t M,
+                         uint16_t* R2, void* stream);
+
+/* Every step of the op except COMBINE, for M tokens whose residual needs no
+ * injection (the "mix" entry point that the same section lists, for the
+ * first layer): the residual R [M, K] is taken as R2 unchanged, and
+ *   rrms [M, HC], inj_next [M, ld_inj_next] and x [M, HS]
+ * are computed exactly as hcgr_forward computes them from its R2 (N, G1,
+ * INJ, G2, MIX). There is no y, inj or R2 argument. Weights, workspace
+ * (hcgr_workspace_size serves both entry points), alignment, ownership and
+ * errors as in hcgr_forward, with R an input only; an output that overlaps
+ * R, another output, a weight or the workspace gives HCGR_ERR_ALIASING. */
+hcgr_status hcgr_mix(hcgr_handle h, const uint16_t* R,
+                     const uint16_t* wnorm, const uint16_t* wd,
+                     const uint16_t* wi, const uint16_t* wu, int64_t M,
+                     float* rrms, uint16_t* inj_next, int64_t ld_inj_next,
+                     uint16_t* x, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Host-side checks of hcgr_combine and hcgr_mix for a configuration, without
+ * a handle, a device or a launch (what the entry point would return before
+ * launching, device and stream checks excluded). Pure host code. */
+hcgr_status hcgr_validate_combine(const hcgr_config* cfg, const uint16_t* R,
+                                  const uint16_t* y, const uint16_t* inj,
+                                  int64_t ld_inj, int64_t M, const uint16_t* R2);
+hcgr_status hcgr_validate_mix(const hcgr_config* cfg, const uint16_t* R,
+                              const uint16_t* wnorm, const uint16_t* wd,
+                              const uint16_t* wi, const uint16_t* wu, int64_t M,
+                              const float* rrms, const uint16_t* inj_next,
+                              int64_t ld_inj_next, const uint16_t* x,
+                              const void* workspace, size_t workspace_bytes);
+
 /* Workspace bytes for a configuration without a handle (pure host code). */
 hcgr_status hcgr_workspace_size_for(const hcgr_config* cfg, int64_t M, size_t* bytes);
 

@@ -87,14 +87,18 @@ def load_library(path: str = LIB_PATH):
     lib.hcgr_forward_timed.argtypes = [P, P, P, P, I64, P, P, P, P, I64, P, P, P, I64, P, P, SZ, P,
                                        ctypes.POINTER(P)]
     lib.hcgr_validate.argtypes = [CFG, P, P, P, I64, P, P, P, P, I64, P, P, P, I64, P, P, SZ]
+    lib.hcgr_combine.argtypes = [P, P, P, P, I64, I64, P, P]
+    lib.hcgr_mix.argtypes = [P, P, P, P, P, P, I64, P, P, I64, P, P, SZ, P]
+    lib.hcgr_validate_combine.argtypes = [CFG, P, P, P, I64, I64, P]
+    lib.hcgr_validate_mix.argtypes = [CFG, P, P, P, P, P, I64, P, P, I64, P, P, SZ]
     lib.hcgr_describe_plan.argtypes = [CFG, I64, ctypes.c_char_p, SZ]
     lib.hcgr_status_string.argtypes = [ctypes.c_int]
     lib.hcgr_status_string.restype = ctypes.c_char_p
     lib.hcgr_last_error.argtypes = []
     lib.hcgr_last_error.restype = ctypes.c_char_p
     for name in ("hcgr_create", "hcgr_workspace_size", "hcgr_workspace_size_for", "hcgr_forward",
-                 "hcgr_forward_timed",
-                 "hcgr_validate", "hcgr_describe_plan"):
+                 "hcgr_forward_timed", "hcgr_combine", "hcgr_mix", "hcgr_validate_combine",
+                 "hcgr_validate_mix", "hcgr_validate", "hcgr_describe_plan"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -156,16 +160,21 @@ def hcgr_describe_plan(cfg: Config, M: int) -> str:
     return buf.value.decode()
 
 
+def _stream(stream, like):
+    """Raw hipStream_t from an int, a torch stream, or None (torch's current
+    stream on the device of the tensor ``like``)."""
+    if stream is None:
+        import torch
+        dev = like.device if hasattr(like, "device") else None
+        return torch.cuda.current_stream(dev).cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
 def hcgr_forward(handle, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x,
                  workspace, workspace_bytes, stream=None, *, check: bool = True) -> int:
     """Tensors (or raw addresses) in, status out; ``stream`` is a raw hipStream_t
     (an int), a torch stream, or None for torch's current stream on ``R``'s device."""
-    if stream is None:
-        import torch
-        dev = R.device if hasattr(R, "device") else None
-        stream = torch.cuda.current_stream(dev).cuda_stream
-    elif not isinstance(stream, int):
-        stream = stream.cuda_stream
+    stream = _stream(stream, R)
     st = load_library().hcgr_forward(handle, _p(R), _p(y), _p(inj), int(ld_inj), _p(wnorm), _p(wd), _p(wi),
                                      _p(wu), int(M), _p(R2), _p(rrms), _p(inj_next), int(ld_inj_next), _p(x),
                                      _p(workspace), int(workspace_bytes), stream)
@@ -188,6 +197,42 @@ def hcgr_forward_timed(handle, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms
                                            _p(wu), int(M), _p(R2), _p(rrms), _p(inj_next), int(ld_inj_next), _p(x),
                                            _p(workspace), int(workspace_bytes), stream, ev)
     return _check(st, "hcgr_forward_timed")
+
+
+def hcgr_combine(handle, R, y, inj, ld_inj, M, R2, stream=None, *, check: bool = True) -> int:
+    """(COMBINE) alone: R2 = R + y*iw (stream as in ``hcgr_forward``)."""
+    st = load_library().hcgr_combine(handle, _p(R), _p(y), _p(inj), int(ld_inj), int(M), _p(R2),
+                                     _stream(stream, R))
+    if check:
+        _check(st, "hcgr_combine")
+    return st
+
+
+def hcgr_mix(handle, R, wnorm, wd, wi, wu, M, rrms, inj_next, ld_inj_next, x, workspace, workspace_bytes,
+             stream=None, *, check: bool = True) -> int:
+    """Every step but COMBINE on a residual R taken as R2 (stream as in ``hcgr_forward``)."""
+    st = load_library().hcgr_mix(handle, _p(R), _p(wnorm), _p(wd), _p(wi), _p(wu), int(M), _p(rrms),
+                                 _p(inj_next), int(ld_inj_next), _p(x), _p(workspace), int(workspace_bytes),
+                                 _stream(stream, R))
+    if check:
+        _check(st, "hcgr_mix")
+    return st
+
+
+def hcgr_validate_combine(cfg: Config, R, y, inj, ld_inj, M, R2) -> int:
+    """Host-only checks of ``hcgr_combine``; returns the status code (does not raise)."""
+    c = cfg.c()
+    return load_library().hcgr_validate_combine(ctypes.byref(c), _p(R), _p(y), _p(inj), int(ld_inj), int(M),
+                                                _p(R2))
+
+
+def hcgr_validate_mix(cfg: Config, R, wnorm, wd, wi, wu, M, rrms, inj_next, ld_inj_next, x, workspace,
+                      workspace_bytes) -> int:
+    """Host-only checks of ``hcgr_mix``; returns the status code (does not raise)."""
+    c = cfg.c()
+    return load_library().hcgr_validate_mix(ctypes.byref(c), _p(R), _p(wnorm), _p(wd), _p(wi), _p(wu), int(M),
+                                            _p(rrms), _p(inj_next), int(ld_inj_next), _p(x), _p(workspace),
+                                            int(workspace_bytes))
 
 
 def hcgr_validate(cfg: Config, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x,
@@ -237,6 +282,24 @@ class HCGR:
                 "rrms": torch.empty((M, c.hc), dtype=torch.float32, device=dev),
                 "inj_next_buf": packed, "inj_next": packed[:, :c.hc], "ld_inj_next": ld,
                 "x": torch.empty((M, c.hs), dtype=torch.bfloat16, device=dev)}
+
+    def combine(self, R, y, inj, *, ld_inj: int | None = None, R2=None, stream=None):
+        import torch
+        M = R.shape[0]
+        if R2 is None:
+            R2 = torch.empty((M, self.cfg.k), dtype=torch.bfloat16, device=R.device)
+        ld = inj.stride(0) if ld_inj is None else ld_inj
+        hcgr_combine(self.handle, R, y, inj, ld, M, R2, stream)
+        return R2
+
+    def mix(self, R, wnorm, wd, wi, wu, *, out: dict | None = None, workspace=None, stream=None) -> dict:
+        M = R.shape[0]
+        if out is None:
+            out = self.alloc_outputs(M)
+        ws = self.workspace(M) if workspace is None else workspace
+        hcgr_mix(self.handle, R, wnorm, wd, wi, wu, M, out["rrms"], out["inj_next"], out["ld_inj_next"],
+                 out["x"], ws, ws.numel(), stream)
+        return out
 
     def forward(self, R, y, inj, wnorm, wd, wi, wu, *, ld_inj: int | None = None, out: dict | None = None,
                 workspace=None, stream=None) -> dict:

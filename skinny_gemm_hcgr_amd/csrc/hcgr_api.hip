@@ -75,32 +75,48 @@ struct Range {
 
 bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
 
+struct PtrCheck {
+  const void* p;
+  const char* name;
+  size_t align;
+};
+
+hcgr_status check_ptrs(const PtrCheck* ptrs, int n) {
+  for (int i = 0; i < n; ++i) {
+    const PtrCheck& p = ptrs[i];
+    if (!p.p) return fail(HCGR_ERR_INVALID_ARGUMENT, "%s is NULL", p.name);
+    if ((uintptr_t)p.p % p.align) return fail(HCGR_ERR_INVALID_ARGUMENT, "%s is not %zu-byte aligned", p.name, p.align);
+  }
+  return HCGR_OK;
+}
+
+// Checks of the whole op (mix = false) or of the mix entry point (mix =
+// true: y, inj and R2 are not part of the call and must be NULL).
 hcgr_status check_forward(const hcgr_config* cfg, const hcgr::Shape& s, const uint16_t* R, const uint16_t* y,
                           const uint16_t* inj, int64_t ld_inj, const uint16_t* wnorm, const uint16_t* wd,
                           const uint16_t* wi, const uint16_t* wu, int64_t M, const void* R2, const float* rrms,
                           const void* inj_next, int64_t ld_inj_next, const void* x, const void* ws,
-                          size_t ws_bytes, hcgr::Plan* plan_out) {
+                          size_t ws_bytes, hcgr::Plan* plan_out, bool mix = false) {
   if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
   if (M > (int64_t)1 << 31) return fail(HCGR_ERR_UNSUPPORTED, "M=%lld exceeds 2^31", (long long)M);
   if (M == 0) return ok();
   const bool merged = s.merged;
-  struct P {
-    const void* p;
-    const char* name;
-    size_t align;
-  } ptrs[] = {{R, "R", 16},        {y, "y", 16},   {inj, "inj", 2},       {wnorm, "wnorm", 16},
-              {wd, "wd", 16},      {wu, "wu", 16}, {R2, "R2", 16},        {rrms, "rrms", 4},
-              {inj_next, "inj_next", 2}, {x, "x", 16}};
-  for (const P& p : ptrs) {
-    if (!p.p) return fail(HCGR_ERR_INVALID_ARGUMENT, "%s is NULL", p.name);
-    if ((uintptr_t)p.p % p.align) return fail(HCGR_ERR_INVALID_ARGUMENT, "%s is not %zu-byte aligned", p.name, p.align);
+  const PtrCheck common[] = {{R, "R", 16},    {wnorm, "wnorm", 16}, {wd, "wd", 16},          {wu, "wu", 16},
+                             {rrms, "rrms", 4}, {inj_next, "inj_next", 2}, {x, "x", 16}};
+  hcgr_status pst = check_ptrs(common, sizeof common / sizeof common[0]);
+  if (pst != HCGR_OK) return pst;
+  if (mix) {
+    if (y || inj || R2) return fail(HCGR_ERR_INVALID_ARGUMENT, "mix takes no y, inj or R2");
+  } else {
+    const PtrCheck comb[] = {{y, "y", 16}, {inj, "inj", 2}, {R2, "R2", 16}};
+    if ((pst = check_ptrs(comb, 3)) != HCGR_OK) return pst;
   }
   if (merged && wi) return fail(HCGR_ERR_INVALID_ARGUMENT, "wi must be NULL with the merged/folded layout");
   if (!merged) {
     if (!wi) return fail(HCGR_ERR_INVALID_ARGUMENT, "wi is NULL");
     if ((uintptr_t)wi % 16) return fail(HCGR_ERR_INVALID_ARGUMENT, "wi is not 16-byte aligned");
   }
-  if (ld_inj < s.hc) return fail(HCGR_ERR_INVALID_ARGUMENT, "ld_inj=%lld < hc=%d", (long long)ld_inj, s.hc);
+  if (!mix && ld_inj < s.hc) return fail(HCGR_ERR_INVALID_ARGUMENT, "ld_inj=%lld < hc=%d", (long long)ld_inj, s.hc);
   if (ld_inj_next < s.hc)
     return fail(HCGR_ERR_INVALID_ARGUMENT, "ld_inj_next=%lld < hc=%d", (long long)ld_inj_next, s.hc);
   hcgr::Plan plan = hcgr::make_plan(s, M);
@@ -118,15 +134,15 @@ hcgr_status check_forward(const hcgr_config* cfg, const hcgr::Shape& s, const ui
   const uint64_t wrows = merged ? (uint64_t)s.n_pad : r;
   const Range ins[] = {
       rng(R, m * K * 2, "R"),
-      rng(y, m * HS * 2, "y"),
-      rng(inj, ((m - 1) * (uint64_t)ld_inj + HC) * 2, "inj"),
+      rng(y, mix ? 0 : m * HS * 2, "y"),
+      rng(inj, mix ? 0 : ((m - 1) * (uint64_t)ld_inj + HC) * 2, "inj"),
       rng(wnorm, (uint64_t)cfg->wnorm_len * 2, "wnorm"),
       rng(wd, wrows * K * 2, "wd"),
       rng(merged ? nullptr : wi, merged ? 0 : HC * K * 2, "wi"),
       rng(wu, K * r * 2, "wu"),
   };
   const Range outs[] = {
-      rng(R2, m * K * 2, "R2"),
+      rng(R2, mix ? 0 : m * K * 2, "R2"),
       rng(rrms, m * HC * 4, "rrms"),
       rng(inj_next, ((m - 1) * (uint64_t)ld_inj_next + HC) * 2, "inj_next"),
       rng(x, m * HS * 2, "x"),
@@ -134,8 +150,9 @@ hcgr_status check_forward(const hcgr_config* cfg, const hcgr::Shape& s, const ui
   };
   const int nin = sizeof ins / sizeof ins[0], nout = sizeof outs / sizeof outs[0];
   for (int i = 0; i < nout; ++i) {
+    if (outs[i].hi == outs[i].lo) continue;  // not part of this call
     for (int j = i + 1; j < nout; ++j)
-      if (overlap(outs[i], outs[j]))
+      if (outs[j].hi > outs[j].lo && overlap(outs[i], outs[j]))
         return fail(HCGR_ERR_ALIASING, "output %s overlaps output %s", outs[i].name, outs[j].name);
     for (int j = 0; j < nin; ++j)
       if (ins[j].hi > ins[j].lo && overlap(outs[i], ins[j]))
@@ -277,16 +294,9 @@ hcgr_status hcgr_validate(const hcgr_config* cfg, const uint16_t* R, const uint1
                        workspace, workspace_bytes, nullptr);
 }
 
-static hcgr_status forward_impl(hcgr_handle h, const uint16_t* R, const uint16_t* y, const uint16_t* inj,
-                                int64_t ld_inj, const uint16_t* wnorm, const uint16_t* wd, const uint16_t* wi,
-                                const uint16_t* wu, int64_t M, uint16_t* R2, float* rrms, uint16_t* inj_next,
-                                int64_t ld_inj_next, uint16_t* x, void* workspace, size_t workspace_bytes,
-                                void* stream, void* const* events) {
-  if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
-  hcgr::Plan plan;
-  hcgr_status st = check_forward(&h->cfg, h->shape, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next,
-                                 ld_inj_next, x, workspace, workspace_bytes, &plan);
-  if (st != HCGR_OK || M == 0) return st;
+// Stream and device checks shared by every launching entry point; on success
+// *prev is the caller's current device (restore it with restore_device).
+static hcgr_status enter_device(hcgr_handle h, void* stream, int* prev) {
   int dev = -1;
   hipError_t e;
   if (stream) {
@@ -305,12 +315,32 @@ static hcgr_status forward_impl(hcgr_handle h, const uint16_t* R, const uint16_t
     e = hipSetDevice(h->device);
     if (e != hipSuccess) return fail(HCGR_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(e));
   }
+  *prev = cur;
+  return HCGR_OK;
+}
+static void restore_device(hcgr_handle h, int prev) {
+  if (prev != h->device) (void)hipSetDevice(prev);
+}
+
+static hcgr_status forward_impl(hcgr_handle h, const uint16_t* R, const uint16_t* y, const uint16_t* inj,
+                                int64_t ld_inj, const uint16_t* wnorm, const uint16_t* wd, const uint16_t* wi,
+                                const uint16_t* wu, int64_t M, uint16_t* R2, float* rrms, uint16_t* inj_next,
+                                int64_t ld_inj_next, uint16_t* x, void* workspace, size_t workspace_bytes,
+                                void* stream, void* const* events, bool mix = false) {
+  if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
+  hcgr::Plan plan;
+  hcgr_status st = check_forward(&h->cfg, h->shape, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next,
+                                 ld_inj_next, x, workspace, workspace_bytes, &plan, mix);
+  if (st != HCGR_OK || M == 0) return st;
+  int cur = -1;
+  if ((st = enter_device(h, stream, &cur)) != HCGR_OK) return st;
   hcgr::ForwardArgs a;
   a.R = R; a.y = y; a.inj = inj; a.wnorm = wnorm; a.wd = wd; a.wi = wi; a.wu = wu;
   a.ld_inj = ld_inj; a.ld_inj_next = ld_inj_next; a.M = M;
   a.R2 = R2; a.inj_next = inj_next; a.x = x; a.rrms = rrms; a.ws = workspace;
+  a.res = mix ? R : R2;
   int le = hcgr::launch_forward(h->shape, plan, a, stream, events);
-  if (cur != h->device) (void)hipSetDevice(cur);
+  restore_device(h, cur);
   if (le != (int)hipSuccess)
     return fail(HCGR_ERR_HIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)le));
   return ok();
@@ -334,6 +364,62 @@ hcgr_status hcgr_forward_timed(hcgr_handle h, const uint16_t* R, const uint16_t*
     if (!events[i]) return fail(HCGR_ERR_INVALID_ARGUMENT, "events[%d] is NULL", i);
   return forward_impl(h, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x, workspace,
                       workspace_bytes, stream, events);
+}
+
+hcgr_status hcgr_mix(hcgr_handle h, const uint16_t* R, const uint16_t* wnorm, const uint16_t* wd,
+                     const uint16_t* wi, const uint16_t* wu, int64_t M, float* rrms, uint16_t* inj_next,
+                     int64_t ld_inj_next, uint16_t* x, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(h, R, nullptr, nullptr, 0, wnorm, wd, wi, wu, M, nullptr, rrms, inj_next, ld_inj_next, x,
+                      workspace, workspace_bytes, stream, nullptr, true);
+}
+
+hcgr_status hcgr_validate_mix(const hcgr_config* cfg, const uint16_t* R, const uint16_t* wnorm, const uint16_t* wd,
+                              const uint16_t* wi, const uint16_t* wu, int64_t M, const float* rrms,
+                              const uint16_t* inj_next, int64_t ld_inj_next, const uint16_t* x, const void* workspace,
+                              size_t workspace_bytes) {
+  hcgr::Shape s;
+  hcgr_status st = check_config(cfg, &s);
+  if (st != HCGR_OK) return st;
+  return check_forward(cfg, s, R, nullptr, nullptr, 0, wnorm, wd, wi, wu, M, nullptr, rrms, inj_next, ld_inj_next,
+                       x, workspace, workspace_bytes, nullptr, true);
+}
+
+hcgr_status hcgr_validate_combine(const hcgr_config* cfg, const uint16_t* R, const uint16_t* y,
+                                  const uint16_t* inj, int64_t ld_inj, int64_t M, const uint16_t* R2) {
+  hcgr::Shape s;
+  hcgr_status st = check_config(cfg, &s);
+  if (st != HCGR_OK) return st;
+  if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
+  if (M > (int64_t)1 << 31) return fail(HCGR_ERR_UNSUPPORTED, "M=%lld exceeds 2^31", (long long)M);
+  if (M == 0) return ok();
+  const PtrCheck ptrs[] = {{R, "R", 16}, {y, "y", 16}, {inj, "inj", 2}, {R2, "R2", 16}};
+  if ((st = check_ptrs(ptrs, 4)) != HCGR_OK) return st;
+  if (ld_inj < s.hc) return fail(HCGR_ERR_INVALID_ARGUMENT, "ld_inj=%lld < hc=%d", (long long)ld_inj, s.hc);
+  const uint64_t m = (uint64_t)M, K = (uint64_t)s.k();
+  const Range out{(uintptr_t)R2, (uintptr_t)R2 + (uintptr_t)(m * K * 2), "R2"};
+  const Range ins[] = {{(uintptr_t)R, (uintptr_t)R + (uintptr_t)(m * K * 2), "R"},
+                       {(uintptr_t)y, (uintptr_t)y + (uintptr_t)(m * (uint64_t)s.hs * 2), "y"},
+                       {(uintptr_t)inj, (uintptr_t)inj + (uintptr_t)(((m - 1) * (uint64_t)ld_inj + (uint64_t)s.hc) * 2),
+                        "inj"}};
+  for (const Range& in : ins)
+    if (overlap(out, in)) return fail(HCGR_ERR_ALIASING, "output R2 overlaps input %s", in.name);
+  return ok();
+}
+
+hcgr_status hcgr_combine(hcgr_handle h, const uint16_t* R, const uint16_t* y, const uint16_t* inj, int64_t ld_inj,
+                         int64_t M, uint16_t* R2, void* stream) {
+  if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
+  hcgr_status st = hcgr_validate_combine(&h->cfg, R, y, inj, ld_inj, M, R2);
+  if (st != HCGR_OK || M == 0) return st;
+  int cur = -1;
+  if ((st = enter_device(h, stream, &cur)) != HCGR_OK) return st;
+  hcgr::CombineArgs a;
+  a.R = R; a.y = y; a.inj = inj; a.ld_inj = ld_inj; a.M = M; a.HS = h->shape.hs; a.HC = h->shape.hc; a.R2 = R2;
+  int le = hcgr::launch_combine(a, stream);
+  restore_device(h, cur);
+  if (le != (int)hipSuccess)
+    return fail(HCGR_ERR_HIP, "kernel launch failed: %s", hipGetErrorString((hipError_t)le));
+  return ok();
 }
 
 }  // extern "C"

@@ -281,13 +281,28 @@ inline size_t workspace_bound(const Shape& s, int64_t M) {
   return best;
 }
 
+// Arguments of one call. The whole op passes every pointer and res == R2.
+// The mix entry point (every step but COMBINE) passes y, inj and R2 as NULL
+// and res == R: the down kernels then read y as zeros (R2 = R exactly),
+// store no R2, and the up kernel rebuilds xn from the input residual.
 struct ForwardArgs {
   const uint16_t *R, *y, *inj, *wnorm, *wd, *wi, *wu;
   int64_t ld_inj, ld_inj_next, M;
   uint16_t *R2, *inj_next, *x;
+  const uint16_t* res;  // residual the up kernel reads: R2 (whole op) or R (mix)
   float* rrms;
   void* ws;
 };
+
+struct CombineArgs {
+  const uint16_t *R, *y, *inj;
+  int64_t ld_inj, M;
+  int HS, HC;
+  uint16_t* R2;
+};
+// Enqueues the combine-only kernel (R2 = R + y*iw) on `stream`; returns the
+// hipError_t of the launch.
+int launch_combine(const CombineArgs& a, void* stream);
 
 // Raises the dynamic-LDS limit of the up kernels on the current device.
 int configure_kernels();

@@ -50,6 +50,12 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Range of an optional tensor: a NULL base gives an empty range, whose loads
+// return 0 and whose stores are dropped (the mix entry point passes no y and
+// no R2 output this way).
+__device__ __forceinline__ rsrc_t make_rsrc_opt(const uint16_t* base, int64_t off, uint32_t bytes) {
+  return base ? make_rsrc(base + off, bytes) : make_rsrc(nullptr, 0u);
+}
 __device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(RB * KW * 64) void hcgr_k1_dec(DownArgs a) {
   const bool lead = rt == 0;  // row tile 0 writes R2 and the sums of squares
   const int koff = 8 * (lane >> 4);
   // 0. injection logit of this thread's token (clamped row: no branch)
-  const uint16_t injb = a.inj[(m0 + min(tid % TM, rows - 1)) * a.ld_inj + s];
+  const uint16_t injb = a.inj ? a.inj[(m0 + min(tid % TM, rows - 1)) * a.ld_inj + s] : (uint16_t)0;
   const uint32_t rowb = (uint32_t)a.K * 2u;
   const int nblk = (a.n_rows + 15) / 16;
 
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(RB * KW * 64) void hcgr_k1_dec(DownArgs a) {
 
   // 2. activation chunks (R, y, Wnorm); a thread's chunks share one column
   const rsrc_t rR = make_rsrc(a.R + m0 * a.K, (uint32_t)rows * rowb);
-  const rsrc_t rY = make_rsrc(a.y + m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
+  const rsrc_t rY = make_rsrc_opt(a.y, m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
   const rsrc_t rWn = make_rsrc(a.wn, a.folded ? 0u : (uint32_t)(a.wn_full ? a.K : a.HS) * 2u);
   uint4 rv[CPT], yv[CPT];
 #pragma unroll
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(RB * KW * 64) void hcgr_k1_dec(DownArgs a) {
 
   // 4. R2 = R + y*iw (fp32), sum of squares, R2 -> bf16 output, activation
   //    R2*(1+Wnorm) -> LDS (Wnorm reads as 0 for folded weights)
-  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, lead ? (uint32_t)rows * rowb : 0u);
+  const rsrc_t rR2 = make_rsrc_opt(a.R2, m0 * a.K, lead ? (uint32_t)rows * rowb : 0u);
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     const int q = tid + j * NT;
@@ -571,9 +577,9 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_full(FullArgs a) {
 
   // range-limited descriptors (scalar)
   const rsrc_t rR = make_rsrc(a.R + m0 * a.K, (uint32_t)rows * rowb);
-  const rsrc_t rY = make_rsrc(a.y + m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
+  const rsrc_t rY = make_rsrc_opt(a.y, m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
   const rsrc_t rWn = make_rsrc(a.wn, a.folded ? 0u : (uint32_t)a.wn_len * 2u);  // folded: reads 0 -> factor 1
-  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, lead ? (uint32_t)rows * rowb : 0u);
+  const rsrc_t rR2 = make_rsrc_opt(a.R2, m0 * a.K, lead ? (uint32_t)rows * rowb : 0u);
   const rsrc_t rW0 = make_rsrc(a.w0, (uint32_t)(a.w1 ? a.r : a.n_rows) * rowb);
   const rsrc_t rW1 = make_rsrc(a.w1 ? a.w1 : a.w0, a.w1 ? (uint32_t)a.HC * rowb : 0u);
 
@@ -583,7 +589,7 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k1_full(FullArgs a) {
     const int s = i / TM, t = i % TM;
     const int64_t m = m0 + t;
     double v = 0.0;
-    if (t < rows) v = 2.0 / (1.0 + exp(-(double)bf1(a.inj[m * a.ld_inj + s]) / (double)a.HC));
+    if (t < rows && a.inj) v = 2.0 / (1.0 + exp(-(double)bf1(a.inj[m * a.ld_inj + s]) / (double)a.HC));
     const float hi = (float)v;
     iwh[s][t] = hi;
     iwl[s][t] = (float)(v - (double)hi);
@@ -866,16 +872,16 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   const uint32_t rowb = (uint32_t)a.K * 2u;
 
   const rsrc_t rR = make_rsrc(a.R + m0 * a.K, (uint32_t)rows * rowb);
-  const rsrc_t rY = make_rsrc(a.y + m0 * HS, (uint32_t)rows * (uint32_t)HS * 2u);
+  const rsrc_t rY = make_rsrc_opt(a.y, m0 * HS, (uint32_t)rows * (uint32_t)HS * 2u);
   const rsrc_t rWn = make_rsrc(a.wn, a.folded ? 0u : (uint32_t)a.wn_len * 2u);  // folded: reads 0 -> factor 1
-  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, lead ? (uint32_t)rows * rowb : 0u);
+  const rsrc_t rR2 = make_rsrc_opt(a.R2, m0 * a.K, lead ? (uint32_t)rows * rowb : 0u);
   const rsrc_t rW0 = make_rsrc(a.w0, (uint32_t)a.r * rowb);
   const rsrc_t rW1 = make_rsrc(a.w1, (uint32_t)a.HC * rowb);  // rows past HC read as zero
 
   // injection logit of table entry tid (loaded before the prefetches below,
   // which then stay in flight while iw is formed)
   const int it = tid % TM, isl = (tid / TM) % SPW;
-  const uint16_t injb = a.inj[(m0 + min(it, rows - 1)) * a.ld_inj + s_first + isl];
+  const uint16_t injb = a.inj ? a.inj[(m0 + min(it, rows - 1)) * a.ld_inj + s_first + isl] : (uint16_t)0;
 
   // chunk this lane moves inside its 128-byte row (rows t with t & 7 == lane >> 3)
   const uint32_t swz = (uint32_t)((lane & 7) ^ (lane >> 3));
@@ -1751,6 +1757,84 @@ __global__ __launch_bounds__(512) void hcgr_k2_sweep(SweepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// hcgr_combine_k: (COMBINE) alone, R2[s,c] = R[s,c] + y[c]*iw[s] with
+// iw[s] = 2*sigmoid(inj[s]/HC), for M tokens. Pure streaming: per token it
+// reads R (HC*HS values) and y (HS) and writes R2 (HC*HS). Workgroup =
+// (token, stream); its 256 threads move 16-byte chunks of that stream's row.
+// Workgroup b serves token 8*(b / (8*HC)) + b % 8 and stream (b / 8) % HC, so
+// the HC workgroups of one token share b % 8, which places them on one XCD
+// (workgroups go round-robin over the 8 XCDs) and lets y come from that XCD's
+// L2 after the first read. Every load of a thread is issued before iw is
+// formed; iw is formed in fp64 by one wave and kept as an fp32 hi + lo pair,
+// so R2 = (R + y*hi) + y*lo stays within an ulp under cancellation.
+// ---------------------------------------------------------------------------
+constexpr int kCombineThreads = 256;
+
+// CPT: 16-byte chunks per thread per pass (1, 2, 4 or 8; rows longer than
+// 8 * 256 * CPT values take several passes)
+template <int CPT>
+__global__ __launch_bounds__(kCombineThreads) void hcgr_combine_k(CombineArgs a) {
+  const int b = (int)blockIdx.x;
+  const int s = (b >> 3) % a.HC;
+  const int64_t m = (int64_t)(b / (8 * a.HC)) * 8 + (b & 7);
+  if (m >= a.M) return;  // whole workgroup
+  const int tid = threadIdx.x;
+  const int nch = a.HS / 8;  // chunks in a stream row
+  const rsrc_t rR = make_rsrc(a.R + m * (int64_t)a.HC * a.HS + (int64_t)s * a.HS, (uint32_t)a.HS * 2u);
+  const rsrc_t rY = make_rsrc(a.y + m * a.HS, (uint32_t)a.HS * 2u);
+  const rsrc_t rO = make_rsrc(a.R2 + m * (int64_t)a.HC * a.HS + (int64_t)s * a.HS, (uint32_t)a.HS * 2u);
+  __shared__ float iw_hl[2];
+  for (int c0 = 0; c0 < nch; c0 += kCombineThreads * CPT) {
+    uint4 rv[CPT], yv[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {  // chunks past the row read as zero
+      const uint32_t off = (uint32_t)(c0 + tid + j * kCombineThreads) * 16u;
+      rv[j] = bld16(rR, off);
+      yv[j] = bld16(rY, off);
+    }
+    if (c0 == 0) {
+      if (tid < 64) {
+        const double v = 2.0 / (1.0 + exp(-(double)bf1(a.inj[m * a.ld_inj + s]) / (double)a.HC));
+        const float hi = (float)v;
+        if (tid == 0) {
+          iw_hl[0] = hi;
+          iw_hl[1] = (float)(v - (double)hi);
+        }
+      }
+      __syncthreads();
+    }
+    const float ih = iw_hl[0], il = iw_hl[1];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = c0 + tid + j * kCombineThreads;
+      if (c >= nch) break;
+      const uint32_t rw[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
+      const uint32_t yw[4] = {yv[j].x, yv[j].y, yv[j].z, yv[j].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float r0 = fmaf(bf_lo(yw[e]), il, fmaf(bf_lo(yw[e]), ih, bf_lo(rw[e])));
+        const float r1 = fmaf(bf_hi(yw[e]), il, fmaf(bf_hi(yw[e]), ih, bf_hi(rw[e])));
+        o[e] = pack_bf2(r0, r1);
+      }
+      bst16(rO, (uint32_t)c * 16u, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  }
+}
+
+int launch_combine(const CombineArgs& a, void* stream) {
+  const int64_t groups = cdiv(a.M, 8) * 8 * a.HC;  // token octets x streams x 8
+  const int passes = (int)cdiv(a.HS / 8, kCombineThreads);  // chunks per thread in one pass
+  const dim3 g((unsigned)groups), blk(kCombineThreads);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (passes <= 1) hipLaunchKernelGGL(hcgr_combine_k<1>, g, blk, 0, st, a);
+  else if (passes <= 2) hipLaunchKernelGGL(hcgr_combine_k<2>, g, blk, 0, st, a);
+  else if (passes <= 4) hipLaunchKernelGGL(hcgr_combine_k<4>, g, blk, 0, st, a);
+  else hipLaunchKernelGGL(hcgr_combine_k<8>, g, blk, 0, st, a);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Every launch goes through hipExtLaunchKernelGGL: with a pair of timing
 // events (start, stop) the runtime stamps them at the kernel's own start and
 // end, so per-kernel durations exclude the dispatch gaps between kernels.
@@ -1845,7 +1929,7 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
 
   UpArgs u;
   u.h = H; u.Mpad = p.mpad; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = K;
-  u.wu = f.wu; u.R2 = f.R2; u.rrms = f.rrms; u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0;
+  u.wu = f.wu; u.R2 = f.res; u.rrms = f.rrms; u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0;
   u.x = f.x;
   const size_t lds = (size_t)(kDecUpWaves * 16 + p.tm) * (size_t)s.r * sizeof(uint16_t)  // Wu rows, h tile
                     + (size_t)p.tm * 4 * (kDecUpWaves * 4) * sizeof(uint16_t)             // R2 rows
@@ -1915,7 +1999,7 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   const KTShape ts = kt_shape(p.kt);
   if (p.kt == KT_SWEEP) {
     SweepArgs wa;
-    wa.h = H; wa.M = f.M; wa.r = s.r; wa.HS = s.hs; wa.K = K; wa.wu = f.wu; wa.R2 = f.R2; wa.rrms = f.rrms;
+    wa.h = H; wa.M = f.M; wa.r = s.r; wa.HS = s.hs; wa.K = K; wa.wu = f.wu; wa.R2 = f.res; wa.rrms = f.rrms;
     wa.wn = f.wnorm; wa.wn_len = s.wn_full ? K : s.hs; wa.x = f.x; wa.ngroups = s.hs / kSweepCg; wa.nranges = p.nranges;
     const dim3 g2((unsigned)(cdiv(f.M, (int64_t)kSweepTm) * p.nranges));
     const int nks = sweep_nks(s.r);
@@ -1928,7 +2012,7 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     }
   } else {
     StageArgs sa;
-    sa.h = H; sa.M = f.M; sa.r = s.r; sa.HS = s.hs; sa.K = K; sa.wu = f.wu; sa.R2 = f.R2; sa.rrms = f.rrms;
+    sa.h = H; sa.M = f.M; sa.r = s.r; sa.HS = s.hs; sa.K = K; sa.wu = f.wu; sa.R2 = f.res; sa.rrms = f.rrms;
     sa.wn = f.wnorm; sa.wn_len = s.wn_full ? K : s.hs; sa.x = f.x; sa.npairs = s.hs / 64;
     const int64_t pairs = cdiv(f.M, (int64_t)ts.tm) * sa.npairs;
     klaunch(hcgr_k2_stage, dim3((unsigned)(cdiv(pairs, 8) * 16)), dim3(256), 0, st, tm.stage(2), sa);

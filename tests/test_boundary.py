@@ -193,3 +193,54 @@ def test_create_without_gfx950_fails_cleanly(lib):
     with pytest.raises(H.HcgrError) as e:
         H.hcgr_create(CFG, 0)
     assert e.value.status in (H.HCGR_ERR_HIP, H.HCGR_ERR_INVALID_ARGUMENT, H.HCGR_ERR_UNSUPPORTED)
+
+
+# ------------------------------------------------ combine and mix entries --
+def _combine(L, **over):
+    a = dict(L.addr)
+    a.update({k: v for k, v in over.items() if k in a})
+    return H.hcgr_validate_combine(over.get("cfg", L.cfg), a["R"], a["y"], a["inj"], over.get("ld_inj", L.ld_inj),
+                                   over.get("M", L.M), a["R2"])
+
+
+def _mix(L, **over):
+    a = dict(L.addr)
+    a.update({k: v for k, v in over.items() if k in a})
+    return H.hcgr_validate_mix(over.get("cfg", L.cfg), a["R"], a["wnorm"], a["wd"], a["wi"], a["wu"],
+                               over.get("M", L.M), a["rrms"], a["inj_next"], over.get("ld_next", L.ld_next),
+                               a["x"], a["ws"], over.get("ws_bytes", L.ws_bytes))
+
+
+@pytest.mark.parametrize("M", [1, 32, 8192, 65536])
+def test_combine_and_mix_valid_calls(lib, M):
+    L = Layout(CFG, M, ld_inj=336)
+    assert _combine(L) == H.HCGR_OK
+    assert _mix(L) == H.HCGR_OK
+    assert _mix(Layout(MCFG, M)) == H.HCGR_OK
+
+
+def test_combine_errors(lib):
+    L = Layout(CFG, 8)
+    assert _combine(L, M=0, R=0, y=0, inj=0, R2=0) == H.HCGR_OK
+    assert _combine(L, M=-1) == H.HCGR_ERR_INVALID_ARGUMENT
+    for name in ("R", "y", "inj", "R2"):
+        assert _combine(L, **{name: 0}) == H.HCGR_ERR_INVALID_ARGUMENT, name
+    assert _combine(L, R2=L.addr["R2"] + 8) == H.HCGR_ERR_INVALID_ARGUMENT
+    assert _combine(L, ld_inj=3) == H.HCGR_ERR_INVALID_ARGUMENT
+    for other in ("R", "y", "inj"):
+        assert _combine(L, R2=L.addr[other]) == H.HCGR_ERR_ALIASING, other
+        assert "R2" in H.last_error()
+    assert _combine(L, cfg=H.Config(hc=2)) == H.HCGR_ERR_UNSUPPORTED
+
+
+def test_mix_errors(lib):
+    L = Layout(CFG, 16)
+    assert _mix(L, M=0, R=0, wnorm=0, wd=0, wi=0, wu=0, rrms=0, inj_next=0, x=0, ws=0) == H.HCGR_OK
+    for name in ("R", "wnorm", "wd", "wi", "wu", "rrms", "inj_next", "x", "ws"):
+        assert _mix(L, **{name: 0}) == H.HCGR_ERR_INVALID_ARGUMENT, name
+    assert _mix(L, ld_next=3) == H.HCGR_ERR_INVALID_ARGUMENT
+    assert _mix(L, ws_bytes=L.ws_bytes - 1) == H.HCGR_ERR_WORKSPACE_TOO_SMALL
+    for out, other in (("x", "R"), ("rrms", "wu"), ("inj_next", "x"), ("ws", "R"), ("x", "wd")):
+        assert _mix(L, **{out: L.addr[other]}) == H.HCGR_ERR_ALIASING, (out, other)
+    # the inputs mix does not take may share memory with its outputs freely
+    assert _mix(L, x=L.addr["y"], rrms=L.addr["R2"]) == H.HCGR_OK
