@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-sweep] [--no-cpu] [--warm]
+    python bench.py --entry combine|mix [--entry-m M] [--steps K]
 
 A step is one hcgr_forward call (all three kernels) over one batch of M
 tokens. The headline line is the decode batch M=32 (HC=4, HS=2560, r=320,
@@ -348,6 +349,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--warm", action="store_true", help="headline on one re-read buffer set")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--entry", choices=("combine", "mix"), default=None,
+                    help="only time this entry point at --entry-m tokens (for profiling) and exit")
+    ap.add_argument("--entry-m", type=int, default=8192)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 5 device-to-device copies of BYTES (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -371,6 +375,10 @@ def main():
         return
     H.load_library()
     op = H.HCGR(H.Config(), 0)
+    if args.entry:
+        r = run_entry(H, op, args.entry, args.entry_m, args.steps, torch.cuda.current_stream().cuda_stream)
+        print(json.dumps(r), flush=True)
+        return
     opm = H.HCGR(H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336), 0)
     stream = torch.cuda.current_stream().cuda_stream
 

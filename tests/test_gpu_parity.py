@@ -451,3 +451,22 @@ def test_m0_and_errors_on_device(H, op, weights):
     assert e.value.status == H.HCGR_ERR_WORKSPACE_TOO_SMALL
     torch.cuda.synchronize()
     assert torch.equal(before, out["x"])
+
+
+@pytest.mark.parametrize("hs,r,M", [(8192, 320, 1), (8192, 320, 32), (8192, 320, 300), (40960, 320, 2),
+                                    (40960, 320, 40), (40960, 64, 130)])
+def test_wide_stream(H, hs, r, M):
+    """Wide streams (HS = 8192 and 40960, the widths the pages' wide-stream
+    test uses): at decode sizes the stream splits into more K chunks than the
+    decode reduction takes, so the stream-wise fallback down kernels run; the
+    tile plan above. Every row against the oracle."""
+    shape = synth.Shape(hs=hs, r=r)
+    o = H.HCGR(H.Config(hs=hs, r=r), 0)
+    _say(f"[parity] wide stream hs={hs} r={r} M={M}: {H.hcgr_describe_plan(o.cfg, M)}")
+    inp = synth.make_inputs(M, shape, seed=19, device="cuda")
+    out = gpu_forward(o, inp)
+    cfg = oracle.OracleConfig(hs=hs, r=r)
+    ref = oracle.forward(cfg, inp["R"].cpu(), inp["y"].cpu(), inp["inj"].cpu(), inp["wnorm"].cpu(), inp["wd"].cpu(),
+                         inp["wi"].cpu(), inp["wu"].cpu())
+    check_all(out, ref)
+    o.close()
