@@ -61,7 +61,7 @@ typedef enum hcgr_weight_layout {
 } hcgr_weight_layout;
 
 typedef struct hcgr_config {
-    int32_t hc;            /* residual streams HC. Supported: 4.                              */
+    int32_t hc;            /* residual streams HC. Supported: 1, 2, 4, 8 (4 is the tuned one). */
     int32_t hs;            /* stream width HS. Supported: multiple of 128, 128..65536.        */
     int32_t r;             /* low-rank width r. Supported: multiple of 32, 32..512.           */
     float eps;             /* RMSNorm epsilon (>= 0, finite), added to the mean square.       */

@@ -51,7 +51,8 @@ hcgr_status check_config(const hcgr_config* c, hcgr::Shape* out) {
                 (long long)k, c->wnorm_len);
   if (c->weight_layout == HCGR_WEIGHTS_MERGED_FOLDED && c->n_pad < c->r + c->hc)
     return fail(HCGR_ERR_INVALID_ARGUMENT, "n_pad (%d) must be >= r + hc (%d)", c->n_pad, c->r + c->hc);
-  if (c->hc != 4) return fail(HCGR_ERR_UNSUPPORTED, "hc=%d: the kernels support hc=4", c->hc);
+  if (c->hc != 1 && c->hc != 2 && c->hc != 4 && c->hc != 8)
+    return fail(HCGR_ERR_UNSUPPORTED, "hc=%d: the kernels support hc = 1, 2, 4 or 8", c->hc);
   if (c->hs % 128 != 0 || c->hs > 65536)
     return fail(HCGR_ERR_UNSUPPORTED, "hs=%d: the kernels support multiples of 128 up to 65536", c->hs);
   if (c->r % 32 != 0 || c->r > 512)
@@ -190,9 +191,12 @@ hcgr_status hcgr_workspace_size_for(const hcgr_config* cfg, int64_t M, size_t* b
   return ok();
 }
 
-static const char* k2_name(int kt) { return kt == hcgr::KT_SWEEP ? "k2_sweep" : "k2_stage"; }
+static const char* k2_name(int kt) {
+  return kt == hcgr::KT_SWEEP ? "k2_sweep" : kt == hcgr::KT_GEN ? "k2_gen" : "k2_stage";
+}
 static long long k2_grid(const hcgr::Shape& s, const hcgr::Plan& p, int64_t M) {
   const hcgr::KTShape t = hcgr::kt_shape(p.kt);
+  if (p.kt == hcgr::KT_GEN) return (long long)(hcgr::cdiv(M, t.tm) * (s.hs / t.cb));
   if (p.kt == hcgr::KT_SWEEP) return (long long)(hcgr::cdiv(M, t.tm) * p.nranges);
   return (long long)(hcgr::cdiv(hcgr::cdiv(M, t.tm) * (s.hs / 64), 8) * 16);
 }
@@ -223,7 +227,7 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
                "M=%lld plan=tile | k1_tile tm=%d waves=8 stage_k=64 streams/wg=%d row_splits=%d segments=%d grid=%lld%s | "
                "%s tm=%d channels=%d ranges=%d grid=%lld | workspace=%zu",
                (long long)M, (int)hcgr::kTileTm, p.spw, p.nsplit, p.nseg,
-               (long long)(hcgr::cdiv(M, hcgr::kTileTm) * p.nsplit * (4 / p.spw) * p.nseg), p.spw == 1 ? " | k1_sum" : "",
+               (long long)(hcgr::cdiv(M, hcgr::kTileTm) * p.nsplit * (s.hc / p.spw) * p.nseg), p.spw == 1 ? " | k1_sum" : "",
                k2_name(p.kt), t.tm, t.cb, p.nranges, k2_grid(s, p, M), p.ws_bytes);
     } else {
       hcgr::KFShape f = hcgr::kf_shape(p.kf);

@@ -36,6 +36,10 @@
 //                         h and Wu staged through LDS by direct global->LDS
 //                         loads, R2 and rrms in registers, and the sigmoid +
 //                         MIX epilogue in registers
+//   Stream counts other than 4 (HC = 1, 2, 8) take the TILE plan at every M
+//   with one stream per down workgroup, hcgr_k1_sum over the HC stream
+//   partials, and K2 hcgr_k2_gen: 64 tokens x 32 channels x HC streams, one
+//   16-row MFMA block per stream so that MIX stays lane-local.
 #pragma once
 
 #include <stddef.h>
@@ -88,10 +92,12 @@ inline KFShape kf_shape(int v) {
 // KT_S128: hcgr_k2_stage (operands staged by direct global->LDS loads);
 // KT_SWEEP: hcgr_k2_sweep (h of a 128-token tile held in registers while the
 // workgroup sweeps a range of 32-channel groups).
-enum KTVariant { KT_S128 = 0, KT_SWEEP = 1, KT_NVAR };
+// KT_GEN: hcgr_k2_gen, for stream counts other than 4 (64 tokens x 32
+// channels x HC streams per workgroup).
+enum KTVariant { KT_S128 = 0, KT_SWEEP = 1, KT_GEN = 2, KT_NVAR };
 struct KTShape { int tm, cb; };
 inline KTShape kt_shape(int v) {
-  static const KTShape t[KT_NVAR] = {{128, 32}, {128, 32}};
+  static const KTShape t[KT_NVAR] = {{128, 32}, {128, 32}, {64, 32}};
   return t[v];
 }
 // hcgr_k2_sweep serves 96 <= r <= 320 (2 to 5 k stages of 64) from
@@ -179,7 +185,10 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   if (M <= 0) return p;
   const int hs = s.hs;
   const size_t np = (size_t)s.np();
-  if (M <= kSplitMaxM) {
+  // stream counts other than 4 (1, 2 or 8) take the tile plan at every M:
+  // one stream per down workgroup, the stream sum, and hcgr_k2_gen
+  const bool generic = s.hc != 4;
+  if (M <= kSplitMaxM && !generic) {
     const int kd = M <= 16 ? KD_T16_R7_K1_C128 : M <= 32 ? KD_T32_R7_K1_C128 : M <= 64 ? KD_T64_R7_K1_C128 : KD_T64_R3_K1_C256;
     const int kd_wide = M <= 16 ? KD_T16_R3_K2_C512 : M <= 32 ? KD_T32_R3_K2_C512 : KD_T64_R3_K1_C256;
     if (make_split(s, M, kd, &p) || make_split(s, M, kd_wide, &p)) return p;
@@ -188,9 +197,9 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   const int64_t target = 256;
   const int64_t tiles = cdiv(M, kTileTm);
   const int tsplit = (int)cdiv(s.nblk(), kTileMaxBlk);  // row splits of the tile down kernel
-  if (M >= kTileMinM) {
+  if (M >= kTileMinM || generic) {
     p.kind = PLAN_TILE;
-    p.spw = tiles * tsplit >= target ? 4 : 1;
+    p.spw = tiles * tsplit >= target && !generic ? 4 : 1;
     p.nsplit = tsplit;
     // below one workgroup per CU, split each stream's columns into segments
     // (an even number of 64-column stages each); hcgr_k1_sum then forms rrms.
@@ -207,14 +216,14 @@ inline Plan make_plan(const Shape& s, int64_t M) {
       double best = 1e300;
       for (int d = 1; d <= pairs; ++d) {
         if (pairs % d != 0) continue;
-        const int64_t rounds = cdiv(tiles * 4 * tsplit * d, target);
+        const int64_t rounds = cdiv(tiles * s.hc * tsplit * d, target);
         const int64_t nst = cdiv(2 * pairs / d, 4) * 4;
         const double cost = (double)rounds * (8.5 + 1.3 * (double)nst) + (double)d * (0.4 + 0.0004 * mt);
         if (cost < best) { best = cost; p.nseg = d; }
       }
     }
-    p.kt = KT_S128;
-    if (M >= kSweepMinM && sweep_fits(s.r)) {
+    p.kt = generic ? KT_GEN : KT_S128;
+    if (M >= kSweepMinM && sweep_fits(s.r) && !generic) {
       p.kt = KT_SWEEP;
       const int64_t t2 = cdiv(M, kt_shape(KT_SWEEP).tm);
       const int ng = hs / kt_shape(KT_SWEEP).cb;

@@ -852,7 +852,7 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rq = wave & 3, th = wave >> 2;
-  constexpr int NG = 4 / SPW;
+  const int NG = a.HC / SPW;  // stream groups (SPW = 4 only with HC = 4)
   const int nseg = SPW == 1 ? a.nseg : 1;
   const int seg = (int)(blockIdx.x % nseg);
   const int bid = (int)(blockIdx.x / nseg);
@@ -1113,7 +1113,7 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   if (lead && nseg == 1)
     for (int i = tid; i < SPW * TM; i += NT) {
       const int sl = i / TM, t = i % TM;
-      if (t < rows) a.rrms[(m0 + t) * 4 + s_first + sl] = rrs[sl][t];
+      if (t < rows) a.rrms[(m0 + t) * a.HC + s_first + sl] = rrs[sl][t];
     }
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
@@ -1174,13 +1174,16 @@ struct SumArgs {
   float eps, inv_hs;
 };
 
+template <int HC>
 __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
   // lane = (token m, chunk c of 8 rows, stream s); s is the fastest index, so
-  // the four streams of a (token, chunk) sit in adjacent lanes
-  const int nch = a.r / 8 + 1;  // r/8 chunks of h, then the chunk holding the inject rows
+  // the HC streams of a (token, chunk) sit in adjacent lanes (HC = 1, 2, 4, 8)
+  static_assert(HC == 1 || HC == 2 || HC == 4 || HC == 8, "stream lanes form an aligned group");
+  constexpr int LG = HC == 1 ? 0 : HC == 2 ? 1 : HC == 4 ? 2 : 3;
+  const int nch = a.r / 8 + (HC + 7) / 8;  // r/8 chunks of h, then the chunk(s) holding the inject rows
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int s = (int)(idx & 3);
-  const int64_t mc = idx >> 2;
+  const int s = (int)(idx & (HC - 1));
+  const int64_t mc = idx >> LG;
   const int64_t m = min(mc / nch, a.M - 1);  // lanes past M recompute the last token and store nothing
   const int c = (int)(mc % nch);
   const bool live = mc / nch < a.M;
@@ -1190,7 +1193,7 @@ __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
     float sq = 0.0f;
     for (int g = 0; g < a.nseg; ++g) sq += a.SSp[(int64_t)(s * a.nseg + g) * a.Mq + m];
     rr = 1.0f / sqrtf(sq * a.inv_hs + a.eps);
-    if (live && c == 0) a.rrms[m * 4 + s] = rr;
+    if (live && c == 0) a.rrms[m * HC + s] = rr;
   }
   float u[8];
 #pragma unroll
@@ -1224,10 +1227,10 @@ __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
   }
   float v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {  // sum over the four stream lanes
+  for (int e = 0; e < 8; ++e) {  // sum over the HC stream lanes
     v[e] = rr * u[e];
-    v[e] += __shfl_xor(v[e], 1, 64);
-    v[e] += __shfl_xor(v[e], 2, 64);
+#pragma unroll
+    for (int d = 1; d < HC; d <<= 1) v[e] += __shfl_xor(v[e], d, 64);
   }
   if (!live || s != 0) return;
   if (n < a.r) {
@@ -1240,8 +1243,8 @@ __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
     st16(a.h + m * a.r + n, make_uint4(o[0], o[1], o[2], o[3]));
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (n + e < a.n_rows) a.inj_next[m * a.ld_inj_next + e] = to_bf(v[e]);  // (INJ)
+    for (int e = 0; e < 8; ++e)
+      if (n + e < a.n_rows) a.inj_next[m * a.ld_inj_next + (n - a.r + e)] = to_bf(v[e]);  // (INJ)
   }
 }
 
@@ -1757,6 +1760,135 @@ __global__ __launch_bounds__(512) void hcgr_k2_sweep(SweepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// hcgr_k2_gen (stream counts other than 4): (G2) gate = h . Wu^T, G =
+// sigmoid(gate), (MIX) x[c] = 1/HC sum_s G[s,c] xn[s,c], for a tile of 64
+// tokens x 32 channels x HC streams, 4 waves. Wave (ch, th) owns channels
+// 16ch.. of the tile and tokens 32th..: for each stream s one 16-row MFMA
+// block whose row i is Wu row s*HS + c0 + 16ch + i, so lane l ends with the
+// same four channels 4(l/16).. of token l%16 for every stream and the MIX sum
+// over streams is lane-local. h (64 rows) and the tile's Wu rows (32 HC rows)
+// pass through LDS in stages of 64 k by direct global->LDS loads, 16-byte
+// chunk c of LDS row t in slot c ^ (t & 7); a half last stage (r % 64 == 32)
+// contracts its first 32 k only.
+// ---------------------------------------------------------------------------
+struct GenUpArgs {
+  const uint16_t* h;  // [>= M, r]
+  int64_t M;
+  int r, HS, K;
+  const uint16_t* wu;  // [K, r]
+  const uint16_t* R2;  // [M, K]
+  const float* rrms;   // [M, HC]
+  const uint16_t* wn;
+  int wn_len;
+  uint16_t* x;  // [M, HS]
+  int ngroups;  // HS / 32
+};
+
+constexpr int kGenTm = 64, kGenCg = 32;
+
+template <int HC>
+__global__ __launch_bounds__(256) void hcgr_k2_gen(GenUpArgs a) {
+  constexpr int TM = kGenTm, CG = kGenCg, NTB = 2;
+  constexpr int HB = TM * 128, WB = HC * CG * 128;  // LDS bytes of one stage of h and of Wu
+  __shared__ __attribute__((aligned(1024))) uint8_t hb[HB];
+  __shared__ __attribute__((aligned(1024))) uint8_t wb[WB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ch = wave & 1, th = wave >> 1;
+  const int64_t tile = (int64_t)blockIdx.x / a.ngroups;
+  const int c0 = (int)((int64_t)blockIdx.x % a.ngroups) * CG;
+  const int64_t m0 = tile * TM;
+  const int rows = (int)min((int64_t)TM, a.M - m0);
+  const uint32_t rowb = (uint32_t)a.K * 2u, hrow = (uint32_t)a.r * 2u;
+  const int nstage = (a.r + 63) / 64;
+
+  const rsrc_t rH = make_rsrc(a.h + m0 * a.r, (uint32_t)rows * hrow);  // tokens past M read zeros
+  const rsrc_t rWu = make_rsrc(a.wu, (uint32_t)a.K * hrow);
+  const rsrc_t rR2 = make_rsrc(a.R2 + m0 * a.K, (uint32_t)rows * rowb);
+  const rsrc_t rX = make_rsrc(a.x + m0 * a.HS, (uint32_t)rows * (uint32_t)a.HS * 2u);
+
+  // one wave instruction moves 8 rows x 128 bytes: lane -> row lane >> 3, chunk swz
+  const uint32_t swz = (uint32_t)((lane & 7) ^ (lane >> 3));
+  auto issue = [&](int stg) {
+    const uint32_t kb = (uint32_t)stg * 128u;
+#pragma unroll
+    for (int i = 0; i < TM / 32; ++i) {  // h: TM / 8 groups of 8 rows over 4 waves
+      const int g = wave + 4 * i;
+      const uint32_t row = (uint32_t)(g * 8 + (lane >> 3));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rH, (lds_void_t*)(hb + g * 1024), 16, row * hrow + swz * 16u + kb, 0,
+                                               0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < HC; ++i) {  // Wu: HC * CG / 8 groups of 8 rows over 4 waves
+      const int g = wave + 4 * i;
+      const int rl = g * 8 + (lane >> 3);  // LDS row: stream rl / CG, channel c0 + rl % CG
+      const uint32_t grow = (uint32_t)((rl / CG) * a.HS + c0 + rl % CG);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rWu, (lds_void_t*)(wb + g * 1024), 16, grow * hrow + swz * 16u + kb, 0,
+                                               0, 0);
+    }
+  };
+
+  f32x4_t acc[HC][NTB];
+#pragma unroll
+  for (int s = 0; s < HC; ++s)
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) acc[s][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int fr = lane & 15;  // fragment row inside a 16-row block (row & 7 == lane & 7)
+  for (int stg = 0; stg < nstage; ++stg) {
+    issue(stg);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's part of the stage has landed
+    const int nks = 64 * stg + 64 <= a.r ? 2 : 1;
+    for (int ks = 0; ks < nks; ++ks) {
+      const int slot = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
+      uint4 bq[NTB];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+        bq[tb] = *reinterpret_cast<const uint4*>(hb + (th * 32 + tb * 16 + fr) * 128 + slot);
+#pragma unroll
+      for (int s = 0; s < HC; ++s) {
+        const uint4 af = *reinterpret_cast<const uint4*>(wb + (s * CG + ch * 16 + fr) * 128 + slot);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) acc[s][tb] = mfma16(af, bq[tb], acc[s][tb]);
+      }
+    }
+    __syncthreads();  // every wave is done with the stage before it is refilled
+  }
+
+  // (G2) sigmoid and (MIX): lane holds channels cl..cl+3 of token t for every stream
+  const int cl = c0 + ch * 16 + 4 * (lane >> 4);
+  float onep[HC][4];
+#pragma unroll
+  for (int s = 0; s < HC; ++s) {
+    const uint2 w = *reinterpret_cast<const uint2*>(a.wn + (a.wn_len == a.HS ? 0 : s * a.HS) + cl);
+    onep[s][0] = 1.0f + bf_lo(w.x);
+    onep[s][1] = 1.0f + bf_hi(w.x);
+    onep[s][2] = 1.0f + bf_lo(w.y);
+    onep[s][3] = 1.0f + bf_hi(w.y);
+  }
+  const float inv_hc = 1.0f / (float)HC;
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    const int t = th * 32 + tb * 16 + fr;
+    if (t >= rows) continue;
+    float xo[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < HC; ++s) {
+      const float rr = a.rrms[(m0 + t) * HC + s];
+      const uint2 w = bld8(rR2, (uint32_t)t * rowb + (uint32_t)(s * a.HS + cl) * 2u);
+      const float r2[4] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xo[q] = fmaf(sigmoid_f(acc[s][tb][q]), r2[q] * rr * onep[s][q], xo[q]);
+    }
+    bst8(rX, ((uint32_t)t * (uint32_t)a.HS + (uint32_t)cl) * 2u,
+         make_uint2(pack_bf2(xo[0] * inv_hc, xo[1] * inv_hc), pack_bf2(xo[2] * inv_hc, xo[3] * inv_hc)));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // hcgr_combine_k: (COMBINE) alone, R2[s,c] = R[s,c] + y[c]*iw[s] with
 // iw[s] = 2*sigmoid(inj[s]/HC), for M tokens. Pure streaming: per token it
 // reads R (HC*HS values) and y (HS) and writes R2 (HC*HS). Workgroup =
@@ -1962,7 +2094,7 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     a.R2 = f.R2; a.rrms = f.rrms; a.h = H; a.inj_next = f.inj_next; a.ld_inj_next = f.ld_inj_next;
     a.Q = Q; a.Mq = p.mq; a.NP = s.np();
     a.nseg = p.nseg; a.SSp = reinterpret_cast<float*>(ws + p.off_ss);
-    const dim3 g1((unsigned)(cdiv(f.M, kTileTm) * p.nsplit * (4 / p.spw) * p.nseg));
+    const dim3 g1((unsigned)(cdiv(f.M, kTileTm) * p.nsplit * (s.hc / p.spw) * p.nseg));
     if (p.spw == 4) klaunch(hcgr_k1_tile<4>, g1, dim3(512), 0, st, tm.stage(0), a);
     else klaunch(hcgr_k1_tile<1>, g1, dim3(512), 0, st, tm.stage(0), a);
   } else {
@@ -1989,15 +2121,32 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     sa.inv_hc = 1.0f / (float)s.hc; sa.h = H; sa.inj_next = f.inj_next; sa.ld_inj_next = f.ld_inj_next;
     sa.nseg = p.kind == PLAN_TILE ? p.nseg : 1; sa.SSp = reinterpret_cast<const float*>(ws + p.off_ss);
     sa.rrms = f.rrms; sa.eps = s.eps; sa.inv_hs = 1.0f / (float)s.hs;
-    const int64_t threads = f.M * (s.r / 8 + 1) * 4;
-    klaunch(hcgr_k1_sum, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st, tm.stage(1), sa);
+    const int64_t threads = f.M * (s.r / 8 + 1) * s.hc;
+    const dim3 gs((unsigned)cdiv(threads, 256)), bs(256);
+    switch (s.hc) {
+      case 1: klaunch(hcgr_k1_sum<1>, gs, bs, 0, st, tm.stage(1), sa); break;
+      case 2: klaunch(hcgr_k1_sum<2>, gs, bs, 0, st, tm.stage(1), sa); break;
+      case 8: klaunch(hcgr_k1_sum<8>, gs, bs, 0, st, tm.stage(1), sa); break;
+      default: klaunch(hcgr_k1_sum<4>, gs, bs, 0, st, tm.stage(1), sa); break;
+    }
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   } else if ((e = tm.skip(1, st)) != hipSuccess) {
     return (int)e;
   }
 
   const KTShape ts = kt_shape(p.kt);
-  if (p.kt == KT_SWEEP) {
+  if (p.kt == KT_GEN) {
+    GenUpArgs ga;
+    ga.h = H; ga.M = f.M; ga.r = s.r; ga.HS = s.hs; ga.K = K; ga.wu = f.wu; ga.R2 = f.res; ga.rrms = f.rrms;
+    ga.wn = f.wnorm; ga.wn_len = s.wn_full ? K : s.hs; ga.x = f.x; ga.ngroups = s.hs / kGenCg;
+    const dim3 g2((unsigned)(cdiv(f.M, (int64_t)kGenTm) * ga.ngroups)), b2(256);
+    switch (s.hc) {
+      case 1: klaunch(hcgr_k2_gen<1>, g2, b2, 0, st, tm.stage(2), ga); break;
+      case 2: klaunch(hcgr_k2_gen<2>, g2, b2, 0, st, tm.stage(2), ga); break;
+      case 8: klaunch(hcgr_k2_gen<8>, g2, b2, 0, st, tm.stage(2), ga); break;
+      default: return (int)hipErrorInvalidValue;  // make_plan takes this kernel for HC = 1, 2, 8 only
+    }
+  } else if (p.kt == KT_SWEEP) {
     SweepArgs wa;
     wa.h = H; wa.M = f.M; wa.r = s.r; wa.HS = s.hs; wa.K = K; wa.wu = f.wu; wa.R2 = f.res; wa.rrms = f.rrms;
     wa.wn = f.wnorm; wa.wn_len = s.wn_full ? K : s.hs; wa.x = f.x; wa.ngroups = s.hs / kSweepCg; wa.nranges = p.nranges;

@@ -424,6 +424,19 @@ def pin_decimal_small(lib):
         close(o[k], ref[k], rel=1e-12, abs_=1e-15)
 
 
+def pin_decimal_eight_streams(lib):
+    """HC=8, HS=8, r=4: the oracle against the 40-digit decimal evaluation with
+    eight streams (the 1/HC scales inside iw, SiLU and the gated mean, and the
+    per-stream RMS groups, at a stream count other than 2 and 4)."""
+    cfg = oracle.OracleConfig(hc=8, hs=8, r=4)
+    d = rand_inputs(cfg, 2, wd_std=0.7, wu_std=1.5)
+    o = run(lib, cfg, d)
+    ref = _decimal_forward(cfg, widen(d["R"]), widen(d["y"]), widen(d["inj"]), widen(d["wnorm"]),
+                           widen(d["wd"]), widen(d["wi"]), widen(d["wu"]))
+    for k in ref:
+        close(o[k], ref[k], rel=1e-12, abs_=1e-15)
+
+
 # ------------------------------------------- combine and mix entry points --
 def pin_combine_entry_closed_form(lib):
     """(COMBINE entry point) with logits (HC, -HC, 2HC, 0) the injection weights

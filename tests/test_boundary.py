@@ -144,7 +144,8 @@ def test_partial_overlap_is_aliasing(lib):
 
 
 @pytest.mark.parametrize("kw,st", [
-    (dict(hc=2), H.HCGR_ERR_UNSUPPORTED), (dict(hs=2500), H.HCGR_ERR_UNSUPPORTED),
+    (dict(hc=3), H.HCGR_ERR_UNSUPPORTED), (dict(hc=16), H.HCGR_ERR_UNSUPPORTED),
+    (dict(hs=2500), H.HCGR_ERR_UNSUPPORTED),
     (dict(r=100), H.HCGR_ERR_UNSUPPORTED), (dict(r=1024), H.HCGR_ERR_UNSUPPORTED),
     (dict(hc=0), H.HCGR_ERR_INVALID_ARGUMENT), (dict(eps=-1.0), H.HCGR_ERR_INVALID_ARGUMENT),
     (dict(eps=float("nan")), H.HCGR_ERR_INVALID_ARGUMENT), (dict(wnorm_len=7), H.HCGR_ERR_INVALID_ARGUMENT),
@@ -156,6 +157,27 @@ def test_config_errors(lib, kw, st):
     with pytest.raises(H.HcgrError) as e:
         H.hcgr_workspace_size_for(cfg, 4)
     assert e.value.status == st
+
+
+@pytest.mark.parametrize("hc", [1, 2, 8])
+def test_other_stream_counts(lib, hc):
+    """HC = 1, 2 and 8 are accepted; their plan is the tile plan at every M
+    (one stream per down workgroup, the stream sum, the HC-generic up kernel)
+    and one workspace sized for the largest M serves every smaller one."""
+    cfg = H.Config(hc=hc)
+    for M in (1, 5, 64, 65, 1000, 8192):
+        assert Layout(cfg, M).call() == H.HCGR_OK
+        L = Layout(cfg, M)
+        assert _mix(L) == H.HCGR_OK and _combine(L) == H.HCGR_OK
+        d = H.hcgr_describe_plan(cfg, M)
+        assert "plan=tile" in d and "k1_sum" in d and "k2_gen" in d, d
+    for hs, r in ((2560, 320), (256, 96), (1024, 512)):
+        c = H.Config(hc=hc, hs=hs, r=r)
+        prev = 0
+        for M in range(1, 400):
+            n = H.hcgr_workspace_size_for(c, M)
+            assert n >= prev, (hc, hs, r, M)
+            prev = n
 
 
 def test_full_width_wnorm_and_other_shapes_accepted(lib):
@@ -230,7 +252,7 @@ def test_combine_errors(lib):
     for other in ("R", "y", "inj"):
         assert _combine(L, R2=L.addr[other]) == H.HCGR_ERR_ALIASING, other
         assert "R2" in H.last_error()
-    assert _combine(L, cfg=H.Config(hc=2)) == H.HCGR_ERR_UNSUPPORTED
+    assert _combine(L, cfg=H.Config(hc=3)) == H.HCGR_ERR_UNSUPPORTED
 
 
 def test_mix_errors(lib):
