@@ -41,17 +41,19 @@ HC, HS, R_LOW = 4, 2560, 320
 K = HC * HS
 
 
-def op_bytes(M, merged=False):
-    """Algorithmic bytes of one call: weights once (Wd, Wi or the 324 used rows
+def op_bytes(M, merged=False, hc=HC, hs=HS, r=R_LOW):
+    """Algorithmic bytes of one call: weights once (Wd, Wi or the r + HC used rows
     of Wm, Wu, Wnorm) + per token R, y, inj in and R2, rrms, inj_next, x out."""
-    w = (R_LOW + HC) * K * 2 + K * R_LOW * 2 + (0 if merged else HS * 2)
+    k = hc * hs
+    w = (r + hc) * k * 2 + k * r * 2 + (0 if merged else hs * 2)
     if merged:
-        w += HS * 2  # the up kernel still reads Wnorm
-    return w + M * (K * 2 + HS * 2 + HC * 2 + K * 2 + HC * 4 + HC * 2 + HS * 2)
+        w += hs * 2  # the up kernel still reads Wnorm
+    return w + M * (k * 2 + hs * 2 + hc * 2 + k * 2 + hc * 4 + hc * 2 + hs * 2)
 
 
-def op_flops(M):
-    return M * 2 * (R_LOW + HC) * K + M * 2 * R_LOW * K
+def op_flops(M, hc=HC, hs=HS, r=R_LOW):
+    k = hc * hs
+    return M * 2 * (r + hc) * k + M * 2 * r * k
 
 
 def kernel_bytes(name, M, merged=False, plan=""):
@@ -98,11 +100,11 @@ def stage_names(plan: str):
 class Sets:
     """NB independent buffer sets (inputs, weights, outputs, workspace) for M tokens."""
 
-    def __init__(self, H, op, M, nb, merged=False, scale_stream0=1.0, seed0=0, entry="forward"):
+    def __init__(self, H, op, M, nb, merged=False, scale_stream0=1.0, seed0=0, entry="forward", hc=HC):
         import torch
         import synth
         self.M, self.nb, self.merged, self.entry = M, nb, merged, entry
-        sh = synth.Shape(HC, HS, R_LOW)
+        sh = synth.Shape(hc, HS, R_LOW)
         self.sets = []
         for i in range(nb):
             inp = synth.make_inputs(M, sh, seed=seed0 + i, device="cuda", scale_stream0=scale_stream0)
@@ -131,10 +133,10 @@ class Sets:
             H.hcgr_forward_timed(*args, events)
 
 
-def set_count(M, merged=False, cold=True):
+def set_count(M, merged=False, cold=True, hc=HC):
     if not cold:
         return 1
-    per = op_bytes(M, merged) + M * (K * 2 + HS * 2)  # + outputs written
+    per = op_bytes(M, merged, hc) + M * (hc * HS * 2 + HS * 2)  # + outputs written
     return max(1, min(64, math.ceil(1.25 * CACHE_BYTES / per)))
 
 
@@ -329,6 +331,26 @@ def run_entry(H, op, entry, M, steps, stream):
 
 ENTRY_RUNS = [("combine", 8192), ("combine", 65536), ("mix", 32), ("mix", 8192)]
 
+
+def run_streams(H, hc, M, steps, stream):
+    """The whole op at another stream count (HS = 2560, r = 320): the tile plan
+    with the stream sum and the HC-generic up kernel."""
+    op = H.HCGR(H.Config(hc=hc), 0)
+    nb = set_count(M, hc=hc)
+    sets = Sets(H, op, M, nb, hc=hc)
+    us, _ = time_calls(H, op, sets, steps, 5, stream)
+    B, F = op_bytes(M, hc=hc), op_flops(M, hc=hc)
+    res = {"hc": hc, "M": M, "buffer_sets": nb, "us_per_call": round(us, 3),
+           "tokens_per_s": round(M / (us * 1e-6), 1), "op_hbm_frac": round(B / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+           "op_mfma_frac": round(F / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+           "plan": H.hcgr_describe_plan(op.cfg, M)}
+    del sets
+    op.close()
+    return res
+
+
+STREAM_RUNS = [(2, 32), (2, 8192), (8, 32), (8, 8192)]
+
 WORKLOADS = {
     "decode_m1": (1, False, 1.0),
     "decode_m32": (32, False, 1.0),
@@ -413,6 +435,14 @@ def main():
             entries.append(r)
             torch.cuda.empty_cache()
 
+    streams = []
+    if not args.no_sweep:
+        for hc, m in STREAM_RUNS:
+            r = run_streams(H, hc, m, max(10, min(args.steps, int(2e5 / m) + 10)), stream)
+            print(f"[bench] HC={hc} M={m}: {r['us_per_call']} us/call", file=sys.stderr, flush=True)
+            streams.append(r)
+            torch.cuda.empty_cache()
+
     dom = max(head["kernels_us"], key=lambda k: head["kernels_us"][k])
     roof = roofline_entry(dom, M, head["kernels_us"][dom], merged, head["plan"], args.workload)
     line = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
@@ -439,6 +469,8 @@ def main():
                          for r in sweep]
     if entries:
         line["entries"] = entries
+    if streams:
+        line["stream_counts"] = [{k: v for k, v in r.items() if k != "plan"} for r in streams]
     if args.json_out:
         with open(args.json_out, "w") as f:
             json.dump({"line": line, "headline": head, "warm": warm, "sweep": sweep}, f, indent=1)
