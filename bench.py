@@ -18,6 +18,9 @@ bf16, separate Wd/Wi). Timing:
     "warm" re-reads one set.
   * per-kernel durations come from the start/end HIP events that
     hcgr_forward_timed takes around each kernel on the same stream.
+Plans: the tuned tables shipped with the package (skinny_gemm_hcgr_amd/plans,
+written by skinny_gemm_hcgr_amd.tune on an MI355X); --heuristic plans by the
+library's own heuristic instead.
 Inputs are seeded synthetic data (synth/) with the study's distributions.
 Prints ONE JSON line on stdout; --json-out also writes it (and the sweep) to a file.
 """
@@ -189,7 +192,7 @@ def time_kernels(H, op, sets, steps, stream, host_us):
     for row in evs:
         for j in range(3):  # start and end of stage j's kernel
             sums[j] += row[2 * j].elapsed_time(row[2 * j + 1]) * 1e3
-    names = stage_names(H.hcgr_describe_plan(op.cfg, sets.M))
+    names = stage_names(op.describe(sets.M))
     return {names[j]: sums[j] / steps for j in range(3) if names[j]}
 
 
@@ -280,7 +283,7 @@ def run_workload(H, op_sep, op_merged, name, M, merged, scale0, steps, warmup, c
            "op_mfma_frac": round(F / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
            "op_roofline_us": round(max(B / (HBM_PEAK_GBS * 1e9), F / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6, 3),
            "kernels_us": {k: round(v, 3) for k, v in kern.items()},
-           "plan": H.hcgr_describe_plan(op.cfg, M)}
+           "plan": op.describe(M)}
     res["op_roofline_frac"] = round(res["op_roofline_us"] / us, 4)
     del sets
     return res
@@ -370,6 +373,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--warm", action="store_true", help="headline on one re-read buffer set")
+    ap.add_argument("--heuristic", action="store_true",
+                    help="plan by the library's heuristic instead of the tuned tables shipped with the package")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--entry", choices=("combine", "mix"), default=None,
                     help="only time this entry point at --entry-m tokens (for profiling) and exit")
@@ -396,12 +401,15 @@ def main():
         print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 5}))
         return
     H.load_library()
-    op = H.HCGR(H.Config(), 0)
+    table = None if args.heuristic else "shipped"
+    op = H.HCGR(H.Config(), 0, plan_table=table)
     if args.entry:
         r = run_entry(H, op, args.entry, args.entry_m, args.steps, torch.cuda.current_stream().cuda_stream)
         print(json.dumps(r), flush=True)
         return
-    opm = H.HCGR(H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336), 0)
+    opm = H.HCGR(H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336), 0, plan_table=table)
+    plans = "heuristic" if args.heuristic else (os.path.relpath(H.shipped_plan_table(op.cfg), ROOT)
+                                                if H.shipped_plan_table(op.cfg) else "heuristic")
     stream = torch.cuda.current_stream().cuda_stream
 
     M, merged, scale0 = WORKLOADS[args.workload]
@@ -451,7 +459,7 @@ def main():
             "data": "synthetic (seeded SplitMix64/Box-Muller, the study's distributions)",
             "config": {"workload": args.workload, "M": M, "hc": HC, "hs": HS, "r": R_LOW, "eps": 1e-6,
                        "weights": "merged_folded_n336" if merged else "separate",
-                       "buffers": head["cache"], "buffer_sets": head["buffer_sets"]},
+                       "buffers": head["cache"], "buffer_sets": head["buffer_sets"], "plans": plans},
             "us_per_call": head["us_per_call"], "us_per_call_graph": head["us_per_call_graph"],
             "us_per_call_warm": warm["us_per_call"] if warm else None,
             "op_roofline_frac": head["op_roofline_frac"], "op_hbm_frac": head["op_hbm_frac"],

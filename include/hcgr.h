@@ -83,7 +83,9 @@ hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out);
 void hcgr_destroy(hcgr_handle h);
 
 /* Bytes of device workspace that serve hcgr_forward for every token count
- * from 1 to M (0 for M == 0); the value never decreases as M grows, so one
+ * from 1 to M (0 for M == 0), with the handle's tuned table if it has one
+ * (hcgr_set_plan_table: install the table before sizing the workspace);
+ * the value never decreases as M grows, so one
  * workspace sized for the largest M serves all smaller calls. The workspace
  * holds the partial sums of the down/inject contraction (per K chunk at
  * decode sizes, per stream or stream segment at mid sizes), their sums of
@@ -219,6 +221,64 @@ hcgr_status hcgr_workspace_size_for(const hcgr_config* cfg, int64_t M, size_t* b
 /* Writes a one-line description of the kernel plan used for M tokens (tile
  * sizes, split counts, grids) into buf (always NUL-terminated when len > 0). */
 hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, size_t len);
+
+/* ------------------------------------------------------------------------
+ * Tuned plans (the "PR Self-Review" section of the same pull request
+ * describes its op's tuned table: token counts resolve to the nearest key in
+ * log space; below the smallest key, and for entries marked heuristic, the
+ * heuristic plan applies; an entry that cannot tile the actual shape falls
+ * back to the heuristic). A plan choice names a plan family and its
+ * parameters; the library checks every choice before use.
+ * ------------------------------------------------------------------------ */
+#define HCGR_PLAN_HEURISTIC (-1) /* the library's own choice                          */
+#define HCGR_PLAN_SPLIT 0        /* decode plan: K-chunked down kernel, reduction, up */
+#define HCGR_PLAN_TILE 3         /* tile plan: 64-token down tiles, (stream sum), up  */
+#define HCGR_SPLIT_VARIANTS 10   /* down-kernel variants of the decode plan           */
+
+typedef struct hcgr_plan_choice {
+    int64_t tokens;         /* table key (token count >= 1); a candidate carries the M it was made for */
+    int32_t kind;           /* HCGR_PLAN_HEURISTIC, HCGR_PLAN_SPLIT or HCGR_PLAN_TILE                 */
+    int32_t down_variant;   /* SPLIT: 0 .. HCGR_SPLIT_VARIANTS-1 (token tile, row blocks, k waves,
+                               chunk width; hcgr_plan_lookup describes each); serves M <= 256 only  */
+    int32_t streams_per_wg; /* TILE: 1, or 4 with HC = 4                                            */
+    int32_t segments;       /* TILE with 1 stream per workgroup: column segments per stream,
+                               a divisor of HS/128 (1 with 4 streams per workgroup)                  */
+    int32_t up_variant;     /* TILE: 0 staged (HC = 4), 1 sweep (HC = 4, 96 <= r <= 320),
+                               2 stream-generic (HC != 4)                                            */
+    int32_t ranges;         /* TILE with the sweep: channel ranges per token tile, 1 .. HS/32;
+                               1 otherwise                                                           */
+} hcgr_plan_choice;
+
+/* Every plan choice that can run cfg's shape at M tokens (the candidates a
+ * tuner times). Writes min(*count, capacity) choices (tokens = M) to out and
+ * the total number to *count; out may be NULL when capacity is 0. Pure host
+ * code. Errors: HCGR_ERR_INVALID_ARGUMENT (M < 1, NULL count, negative
+ * capacity), config errors as hcgr_create. */
+hcgr_status hcgr_plan_candidates(const hcgr_config* cfg, int64_t M, hcgr_plan_choice* out,
+                                 int32_t capacity, int32_t* count);
+
+/* The plan a table gives M tokens: writes the choice it resolves to (kind
+ * HCGR_PLAN_HEURISTIC when the heuristic applies; tokens = the entry's key or
+ * 0) to *chosen (may be NULL) and a one-line description of the resulting
+ * plan, as hcgr_describe_plan, to buf. n = 0 (table may be NULL) describes
+ * the heuristic. Pure host code. Errors: as hcgr_set_plan_table for a
+ * malformed table; HCGR_ERR_INVALID_ARGUMENT for M < 0. */
+hcgr_status hcgr_plan_lookup(const hcgr_config* cfg, const hcgr_plan_choice* table, int32_t n,
+                             int64_t M, hcgr_plan_choice* chosen, char* buf, size_t len);
+
+/* Workspace bytes that serve every token count from 1 to M with a table (the
+ * table-aware form of hcgr_workspace_size_for). Pure host code. */
+hcgr_status hcgr_workspace_size_table(const hcgr_config* cfg, const hcgr_plan_choice* table, int32_t n,
+                                      int64_t M, size_t* bytes);
+
+/* Installs a copy of a tuned table in the handle (n = 0 clears it; the
+ * caller keeps ownership of `table`). Keys must be >= 1 and strictly
+ * increasing; every non-heuristic entry must be able to run the handle's
+ * shape at its own key; otherwise HCGR_ERR_INVALID_ARGUMENT and the handle's
+ * table is unchanged. Afterwards hcgr_forward, hcgr_forward_timed, hcgr_mix
+ * and hcgr_workspace_size use the table. Calls that may run concurrently on
+ * one handle must not overlap with this one. */
+hcgr_status hcgr_set_plan_table(hcgr_handle h, const hcgr_plan_choice* table, int32_t n);
 
 /* Static name of a status code. */
 const char* hcgr_status_string(hcgr_status s);

@@ -27,6 +27,10 @@ HCGR_ERR_WORKSPACE_TOO_SMALL = 4
 HCGR_ERR_HIP = 5
 HCGR_WEIGHTS_SEPARATE = 0
 HCGR_WEIGHTS_MERGED_FOLDED = 1
+HCGR_PLAN_HEURISTIC = -1
+HCGR_PLAN_SPLIT = 0
+HCGR_PLAN_TILE = 3
+PLAN_FIELDS = ("tokens", "kind", "down_variant", "streams_per_wg", "segments", "up_variant", "ranges")
 
 
 class HcgrError(RuntimeError):
@@ -39,6 +43,26 @@ class hcgr_config(ctypes.Structure):
     _fields_ = [("hc", ctypes.c_int32), ("hs", ctypes.c_int32), ("r", ctypes.c_int32),
                 ("eps", ctypes.c_float), ("wnorm_len", ctypes.c_int32),
                 ("weight_layout", ctypes.c_int32), ("n_pad", ctypes.c_int32)]
+
+
+class hcgr_plan_choice(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("kind", ctypes.c_int32), ("down_variant", ctypes.c_int32),
+                ("streams_per_wg", ctypes.c_int32), ("segments", ctypes.c_int32), ("up_variant", ctypes.c_int32),
+                ("ranges", ctypes.c_int32)]
+
+
+def _choices_in(table):
+    """A table (list of dicts with PLAN_FIELDS keys) as a ctypes array and its length."""
+    table = list(table or [])
+    arr = (hcgr_plan_choice * max(1, len(table)))()
+    for i, e in enumerate(table):
+        for f in PLAN_FIELDS:
+            setattr(arr[i], f, int(e.get(f, 0)))
+    return arr, len(table)
+
+
+def _choice_out(c) -> dict:
+    return {f: int(getattr(c, f)) for f in PLAN_FIELDS}
 
 
 @dataclass(frozen=True)
@@ -92,13 +116,19 @@ def load_library(path: str = LIB_PATH):
     lib.hcgr_validate_combine.argtypes = [CFG, P, P, P, I64, I64, P]
     lib.hcgr_validate_mix.argtypes = [CFG, P, P, P, P, P, I64, P, P, I64, P, P, SZ]
     lib.hcgr_describe_plan.argtypes = [CFG, I64, ctypes.c_char_p, SZ]
+    PC = ctypes.POINTER(hcgr_plan_choice)
+    lib.hcgr_plan_candidates.argtypes = [CFG, I64, PC, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.hcgr_plan_lookup.argtypes = [CFG, PC, ctypes.c_int32, I64, PC, ctypes.c_char_p, SZ]
+    lib.hcgr_workspace_size_table.argtypes = [CFG, PC, ctypes.c_int32, I64, ctypes.POINTER(SZ)]
+    lib.hcgr_set_plan_table.argtypes = [P, PC, ctypes.c_int32]
     lib.hcgr_status_string.argtypes = [ctypes.c_int]
     lib.hcgr_status_string.restype = ctypes.c_char_p
     lib.hcgr_last_error.argtypes = []
     lib.hcgr_last_error.restype = ctypes.c_char_p
     for name in ("hcgr_create", "hcgr_workspace_size", "hcgr_workspace_size_for", "hcgr_forward",
                  "hcgr_forward_timed", "hcgr_combine", "hcgr_mix", "hcgr_validate_combine",
-                 "hcgr_validate_mix", "hcgr_validate", "hcgr_describe_plan"):
+                 "hcgr_validate_mix", "hcgr_validate", "hcgr_describe_plan", "hcgr_plan_candidates",
+                 "hcgr_plan_lookup", "hcgr_workspace_size_table", "hcgr_set_plan_table"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -158,6 +188,62 @@ def hcgr_describe_plan(cfg: Config, M: int) -> str:
     c = cfg.c()
     _check(load_library().hcgr_describe_plan(ctypes.byref(c), int(M), buf, len(buf)), "hcgr_describe_plan")
     return buf.value.decode()
+
+
+def hcgr_plan_candidates(cfg: Config, M: int) -> list:
+    """Every plan choice that can run cfg's shape at M tokens (dicts with PLAN_FIELDS)."""
+    lib, c, n = load_library(), cfg.c(), ctypes.c_int32()
+    _check(lib.hcgr_plan_candidates(ctypes.byref(c), int(M), None, 0, ctypes.byref(n)), "hcgr_plan_candidates")
+    arr = (hcgr_plan_choice * max(1, n.value))()
+    _check(lib.hcgr_plan_candidates(ctypes.byref(c), int(M), arr, n.value, ctypes.byref(n)), "hcgr_plan_candidates")
+    return [_choice_out(arr[i]) for i in range(n.value)]
+
+
+def hcgr_plan_lookup(cfg: Config, table, M: int):
+    """(choice the table resolves M to, description of the resulting plan)."""
+    c, (arr, n) = cfg.c(), _choices_in(table)
+    out, buf = hcgr_plan_choice(), ctypes.create_string_buffer(1024)
+    _check(load_library().hcgr_plan_lookup(ctypes.byref(c), arr, n, int(M), ctypes.byref(out), buf, len(buf)),
+           "hcgr_plan_lookup")
+    return _choice_out(out), buf.value.decode()
+
+
+def hcgr_workspace_size_table(cfg: Config, table, M: int) -> int:
+    c, (arr, n), b = cfg.c(), _choices_in(table), ctypes.c_size_t()
+    _check(load_library().hcgr_workspace_size_table(ctypes.byref(c), arr, n, int(M), ctypes.byref(b)),
+           "hcgr_workspace_size_table")
+    return b.value
+
+
+def hcgr_set_plan_table(handle: int, table) -> None:
+    arr, n = _choices_in(table)
+    _check(load_library().hcgr_set_plan_table(handle, arr, n), "hcgr_set_plan_table")
+
+
+PLANS_DIR = os.path.join(_PKG, "plans")
+
+
+def shipped_plan_table(cfg: Config):
+    """Path of the tuned table shipped with the package for cfg (written by
+    ``skinny_gemm_hcgr_amd.tune`` on an MI355X), or None."""
+    name = f"hc{cfg.hc}_hs{cfg.hs}_r{cfg.r}" + ("_merged" if cfg.merged else "") + \
+        ("_wnfull" if (cfg.wnorm_len or cfg.hs) != cfg.hs else "") + ".json"
+    path = os.path.join(PLANS_DIR, name)
+    return path if os.path.exists(path) else None
+
+
+def load_plan_table(path: str, cfg: Config) -> list:
+    """Entries of a tuned-plan JSON file (written by ``skinny_gemm_hcgr_amd.tune``);
+    raises if the file was tuned for another configuration."""
+    import json
+    with open(path) as f:
+        d = json.load(f)
+    want = {"hc": cfg.hc, "hs": cfg.hs, "r": cfg.r, "wnorm_len": cfg.wnorm_len or cfg.hs,
+            "weight_layout": cfg.weight_layout}
+    got = {k: d.get("config", {}).get(k) for k in want}
+    if got != want:
+        raise ValueError(f"{path} was tuned for {got}, not {want}")
+    return [{f: int(e[f]) for f in PLAN_FIELDS} for e in d["entries"]]
 
 
 def _stream(stream, like):
@@ -248,11 +334,29 @@ def hcgr_validate(cfg: Config, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms
 class HCGR:
     """Handle + torch-allocated outputs/workspace around ``hcgr_forward``."""
 
-    def __init__(self, cfg: Config = Config(), device: int = 0):
+    def __init__(self, cfg: Config = Config(), device: int = 0, plan_table=None):
+        """``plan_table``: a tuned table (list of entries, or the path of a JSON
+        file written by ``skinny_gemm_hcgr_amd.tune``), "shipped" for the table
+        shipped with the package for cfg (the heuristic if there is none), or
+        None for the heuristic."""
         self.cfg = cfg
         self.device = device
         self.handle = hcgr_create(cfg, device)
         self._ws = None
+        if plan_table == "shipped":
+            plan_table = shipped_plan_table(cfg)
+        if plan_table is not None:
+            self.set_plan_table(plan_table)
+
+    def set_plan_table(self, table):
+        if isinstance(table, str):
+            table = load_plan_table(table, self.cfg)
+        hcgr_set_plan_table(self.handle, table)
+        self.table = list(table)
+        self._ws = None  # the workspace bound may change
+
+    def describe(self, M: int) -> str:
+        return hcgr_plan_lookup(self.cfg, getattr(self, "table", []), M)[1]
 
     def close(self):
         if self.handle:

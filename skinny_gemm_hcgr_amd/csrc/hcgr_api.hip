@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "../../include/hcgr.h"
 #include "hcgr_internal.h"
@@ -16,6 +17,7 @@ struct hcgr_op {
   hcgr_config cfg;
   int device;
   int cu_count;
+  std::vector<hcgr::TableEntry> table;  // tuned plans (empty: the heuristic)
 };
 
 namespace {
@@ -97,7 +99,8 @@ hcgr_status check_forward(const hcgr_config* cfg, const hcgr::Shape& s, const ui
                           const uint16_t* inj, int64_t ld_inj, const uint16_t* wnorm, const uint16_t* wd,
                           const uint16_t* wi, const uint16_t* wu, int64_t M, const void* R2, const float* rrms,
                           const void* inj_next, int64_t ld_inj_next, const void* x, const void* ws,
-                          size_t ws_bytes, hcgr::Plan* plan_out, bool mix = false) {
+                          size_t ws_bytes, hcgr::Plan* plan_out, bool mix = false,
+                          const hcgr::TableEntry* table = nullptr, int ntable = 0) {
   if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
   if (M > (int64_t)1 << 31) return fail(HCGR_ERR_UNSUPPORTED, "M=%lld exceeds 2^31", (long long)M);
   if (M == 0) return ok();
@@ -120,7 +123,7 @@ hcgr_status check_forward(const hcgr_config* cfg, const hcgr::Shape& s, const ui
   if (!mix && ld_inj < s.hc) return fail(HCGR_ERR_INVALID_ARGUMENT, "ld_inj=%lld < hc=%d", (long long)ld_inj, s.hc);
   if (ld_inj_next < s.hc)
     return fail(HCGR_ERR_INVALID_ARGUMENT, "ld_inj_next=%lld < hc=%d", (long long)ld_inj_next, s.hc);
-  hcgr::Plan plan = hcgr::make_plan(s, M);
+  hcgr::Plan plan = hcgr::plan_for(s, M, table, ntable);
   if (ws_bytes < plan.ws_bytes)
     return fail(HCGR_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed for M=%lld", ws_bytes,
                 plan.ws_bytes, (long long)M);
@@ -163,6 +166,53 @@ hcgr_status check_forward(const hcgr_config* cfg, const hcgr::Shape& s, const ui
   return ok();
 }
 
+// A C ABI plan choice as the planner's Choice; false for an unknown kind.
+bool to_choice(const hcgr_plan_choice& c, hcgr::Choice* out) {
+  hcgr::Choice x;
+  x.kind = c.kind;
+  x.kd = c.down_variant;
+  x.spw = c.streams_per_wg;
+  x.nseg = c.segments;
+  x.kt = c.up_variant;  // 0 staged, 1 sweep, 2 generic: the planner's KT_* values
+  x.nranges = c.ranges;
+  if (c.kind != HCGR_PLAN_HEURISTIC && c.kind != HCGR_PLAN_SPLIT && c.kind != HCGR_PLAN_TILE) return false;
+  *out = x;
+  return true;
+}
+
+hcgr_plan_choice from_choice(const hcgr::Choice& c, int64_t tokens) {
+  hcgr_plan_choice o;
+  o.tokens = tokens;
+  o.kind = c.kind;
+  o.down_variant = c.kind == HCGR_PLAN_SPLIT ? c.kd : 0;
+  o.streams_per_wg = c.kind == HCGR_PLAN_TILE ? c.spw : 0;
+  o.segments = c.kind == HCGR_PLAN_TILE ? c.nseg : 0;
+  o.up_variant = c.kind == HCGR_PLAN_TILE ? c.kt : 0;
+  o.ranges = c.kind == HCGR_PLAN_TILE ? c.nranges : 0;
+  return o;
+}
+
+// Checks a C ABI table against a shape and converts it.
+hcgr_status check_table(const hcgr::Shape& s, const hcgr_plan_choice* t, int32_t n, std::vector<hcgr::TableEntry>* out) {
+  if (n < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "table length %d is negative", n);
+  if (n > 0 && !t) return fail(HCGR_ERR_INVALID_ARGUMENT, "table is NULL");
+  std::vector<hcgr::TableEntry> v;
+  v.reserve((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    hcgr::Choice c;
+    if (!to_choice(t[i], &c)) return fail(HCGR_ERR_INVALID_ARGUMENT, "table entry %d: unknown kind %d", i, t[i].kind);
+    if (t[i].tokens < 1 || (i > 0 && t[i].tokens <= t[i - 1].tokens))
+      return fail(HCGR_ERR_INVALID_ARGUMENT, "table entry %d: keys must be >= 1 and strictly increasing", i);
+    hcgr::Plan p;
+    if (c.kind != hcgr::kChoiceHeuristic && !hcgr::plan_from_choice(s, t[i].tokens, c, &p))
+      return fail(HCGR_ERR_INVALID_ARGUMENT, "table entry %d (tokens=%lld): the choice cannot run this shape", i,
+                  (long long)t[i].tokens);
+    v.push_back(hcgr::TableEntry{t[i].tokens, c});
+  }
+  *out = std::move(v);
+  return HCGR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,13 +251,7 @@ static long long k2_grid(const hcgr::Shape& s, const hcgr::Plan& p, int64_t M) {
   return (long long)(hcgr::cdiv(hcgr::cdiv(M, t.tm) * (s.hs / 64), 8) * 16);
 }
 
-hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, size_t len) {
-  hcgr::Shape s;
-  hcgr_status st = check_config(cfg, &s);
-  if (st != HCGR_OK) return st;
-  if (!buf && len) return fail(HCGR_ERR_INVALID_ARGUMENT, "buf is NULL");
-  if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
-  hcgr::Plan p = hcgr::make_plan(s, M);
+static void describe(const hcgr::Shape& s, const hcgr::Plan& p, int64_t M, char* buf, size_t len) {
   if (len) {
     if (M == 0) {
       snprintf(buf, len, "M=0: no launch");
@@ -240,6 +284,74 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
                k2_name(p.kt), t.tm, t.cb, p.nranges, k2_grid(s, p, M), p.ws_bytes);
     }
   }
+}
+
+hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, size_t len) {
+  hcgr::Shape s;
+  hcgr_status st = check_config(cfg, &s);
+  if (st != HCGR_OK) return st;
+  if (!buf && len) return fail(HCGR_ERR_INVALID_ARGUMENT, "buf is NULL");
+  if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
+  describe(s, hcgr::make_plan(s, M), M, buf, len);
+  return ok();
+}
+
+hcgr_status hcgr_plan_candidates(const hcgr_config* cfg, int64_t M, hcgr_plan_choice* out, int32_t capacity,
+                                 int32_t* count) {
+  hcgr::Shape s;
+  hcgr_status st = check_config(cfg, &s);
+  if (st != HCGR_OK) return st;
+  if (!count) return fail(HCGR_ERR_INVALID_ARGUMENT, "count is NULL");
+  if (M < 1) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld: candidates need M >= 1", (long long)M);
+  if (capacity < 0 || (capacity > 0 && !out)) return fail(HCGR_ERR_INVALID_ARGUMENT, "bad output capacity");
+  std::vector<hcgr::Choice> v(512);
+  const int n = hcgr::plan_choices(s, M, v.data(), (int)v.size());
+  for (int i = 0; i < n && i < capacity && i < (int)v.size(); ++i) out[i] = from_choice(v[(size_t)i], M);
+  *count = n;
+  return ok();
+}
+
+hcgr_status hcgr_plan_lookup(const hcgr_config* cfg, const hcgr_plan_choice* table, int32_t n, int64_t M,
+                             hcgr_plan_choice* chosen, char* buf, size_t len) {
+  hcgr::Shape s;
+  hcgr_status st = check_config(cfg, &s);
+  if (st != HCGR_OK) return st;
+  if (!buf && len) return fail(HCGR_ERR_INVALID_ARGUMENT, "buf is NULL");
+  if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
+  std::vector<hcgr::TableEntry> t;
+  if ((st = check_table(s, table, n, &t)) != HCGR_OK) return st;
+  const int i = hcgr::table_index(t.data(), (int)t.size(), M);
+  hcgr::Plan p;
+  const bool use = i >= 0 && t[(size_t)i].c.kind != hcgr::kChoiceHeuristic &&
+                   hcgr::plan_from_choice(s, M, t[(size_t)i].c, &p);
+  if (chosen) *chosen = use ? from_choice(t[(size_t)i].c, t[(size_t)i].M) : from_choice(hcgr::Choice(), i >= 0 ? t[(size_t)i].M : 0);
+  if (M == 0) {
+    if (len) snprintf(buf, len, "M=0: no launch");
+  } else {
+    describe(s, use ? p : hcgr::make_plan(s, M), M, buf, len);
+  }
+  return ok();
+}
+
+hcgr_status hcgr_workspace_size_table(const hcgr_config* cfg, const hcgr_plan_choice* table, int32_t n, int64_t M,
+                                      size_t* bytes) {
+  hcgr::Shape s;
+  hcgr_status st = check_config(cfg, &s);
+  if (st != HCGR_OK) return st;
+  if (!bytes) return fail(HCGR_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
+  std::vector<hcgr::TableEntry> t;
+  if ((st = check_table(s, table, n, &t)) != HCGR_OK) return st;
+  *bytes = hcgr::workspace_bound_table(s, M, t.data(), (int)t.size());
+  return ok();
+}
+
+hcgr_status hcgr_set_plan_table(hcgr_handle h, const hcgr_plan_choice* table, int32_t n) {
+  if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
+  std::vector<hcgr::TableEntry> t;
+  hcgr_status st = check_table(h->shape, table, n, &t);
+  if (st != HCGR_OK) return st;
+  h->table = std::move(t);
   return ok();
 }
 
@@ -283,7 +395,10 @@ void hcgr_destroy(hcgr_handle h) { delete h; }
 
 hcgr_status hcgr_workspace_size(hcgr_handle h, int64_t M, size_t* bytes) {
   if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
-  return hcgr_workspace_size_for(&h->cfg, M, bytes);
+  if (!bytes) return fail(HCGR_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (M < 0) return fail(HCGR_ERR_INVALID_ARGUMENT, "M=%lld is negative", (long long)M);
+  *bytes = hcgr::workspace_bound_table(h->shape, M, h->table.data(), (int)h->table.size());
+  return ok();
 }
 
 hcgr_status hcgr_validate(const hcgr_config* cfg, const uint16_t* R, const uint16_t* y, const uint16_t* inj,
@@ -334,7 +449,8 @@ static hcgr_status forward_impl(hcgr_handle h, const uint16_t* R, const uint16_t
   if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
   hcgr::Plan plan;
   hcgr_status st = check_forward(&h->cfg, h->shape, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next,
-                                 ld_inj_next, x, workspace, workspace_bytes, &plan, mix);
+                                 ld_inj_next, x, workspace, workspace_bytes, &plan, mix, h->table.data(),
+                                 (int)h->table.size());
   if (st != HCGR_OK || M == 0) return st;
   int cur = -1;
   if ((st = enter_device(h, stream, &cur)) != HCGR_OK) return st;

@@ -45,6 +45,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <climits>
+
 namespace hcgr {
 
 enum PlanKind { PLAN_SPLIT = 0, PLAN_STREAM = 1, PLAN_FULL = 2, PLAN_TILE = 3 };
@@ -178,6 +180,49 @@ inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
   return true;
 }
 
+// TILE plan with explicit parameters: spw streams per down workgroup (1, or 4
+// with HC = 4), nseg column segments per stream (spw = 1; divides HS/128),
+// up-kernel variant kt (KT_GEN exactly when HC != 4; KT_SWEEP needs
+// 96 <= r <= 320) and nranges channel ranges per token tile (KT_SWEEP only,
+// 1 .. HS/32). False when the parameters cannot run this shape.
+inline bool make_tile(const Shape& s, int64_t M, int spw, int nseg, int kt, int nranges, Plan* out) {
+  const bool generic = s.hc != 4;
+  if (M <= 0) return false;
+  if (spw != 1 && !(spw == 4 && !generic)) return false;
+  if (nseg < 1 || (s.hs / 128) % nseg != 0 || (spw == 4 && nseg != 1)) return false;
+  if (generic != (kt == KT_GEN)) return false;
+  if (kt == KT_SWEEP) {
+    if (!sweep_fits(s.r) || nranges < 1 || nranges > s.hs / kt_shape(KT_SWEEP).cb) return false;
+  } else if (kt != KT_S128 && kt != KT_GEN) {
+    return false;
+  } else if (nranges != 1) {
+    return false;
+  }
+  const size_t np = (size_t)s.np();
+  Plan p;
+  p.M = M;
+  p.kind = PLAN_TILE;
+  p.spw = spw;
+  p.nsplit = (int)cdiv(s.nblk(), kTileMaxBlk);  // row splits of the tile down kernel
+  p.nseg = nseg;
+  p.kt = kt;
+  p.nranges = nranges;
+  p.tm = kTileTm;
+  const int tm2 = kt_shape(kt).tm;
+  p.mpad = cdiv(M, tm2) * tm2;
+  p.mq = cdiv(M, kTileTm) * kTileTm;
+  p.off_h = 0;
+  p.off_q = align256((size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
+  p.ws_bytes = p.off_q;
+  if (spw == 1) {
+    const size_t parts = (size_t)s.hc * (size_t)nseg;
+    p.off_ss = align256(p.off_q + parts * (size_t)p.mq * np * sizeof(float));
+    p.ws_bytes = align256(p.off_ss + parts * (size_t)p.mq * sizeof(float));
+  }
+  *out = p;
+  return true;
+}
+
 // Pure host planning: tile sizes and split counts by token count M.
 inline Plan make_plan(const Shape& s, int64_t M) {
   Plan p;
@@ -198,9 +243,7 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   const int64_t tiles = cdiv(M, kTileTm);
   const int tsplit = (int)cdiv(s.nblk(), kTileMaxBlk);  // row splits of the tile down kernel
   if (M >= kTileMinM || generic) {
-    p.kind = PLAN_TILE;
-    p.spw = tiles * tsplit >= target && !generic ? 4 : 1;
-    p.nsplit = tsplit;
+    const int spw = tiles * tsplit >= target && !generic ? 4 : 1;
     // below one workgroup per CU, split each stream's columns into segments
     // (an even number of 64-column stages each); hcgr_k1_sum then forms rrms.
     // The count minimises a cost fitted to measurements on MI355X (HS = 2560,
@@ -210,7 +253,8 @@ inline Plan make_plan(const Shape& s, int64_t M) {
     // partials. It depends on M only through the token tile count, so every M
     // with the same tile count gets the same plan (the workspace bound below
     // relies on that).
-    if (p.spw == 1) {
+    int nseg = 1;
+    if (spw == 1) {
       const int pairs = s.hs / 128;
       const double mt = (double)(tiles * kTileTm);
       double best = 1e300;
@@ -219,28 +263,17 @@ inline Plan make_plan(const Shape& s, int64_t M) {
         const int64_t rounds = cdiv(tiles * s.hc * tsplit * d, target);
         const int64_t nst = cdiv(2 * pairs / d, 4) * 4;
         const double cost = (double)rounds * (8.5 + 1.3 * (double)nst) + (double)d * (0.4 + 0.0004 * mt);
-        if (cost < best) { best = cost; p.nseg = d; }
+        if (cost < best) { best = cost; nseg = d; }
       }
     }
-    p.kt = generic ? KT_GEN : KT_S128;
+    int kt = generic ? KT_GEN : KT_S128, nranges = 1;
     if (M >= kSweepMinM && sweep_fits(s.r) && !generic) {
-      p.kt = KT_SWEEP;
+      kt = KT_SWEEP;
       const int64_t t2 = cdiv(M, kt_shape(KT_SWEEP).tm);
       const int ng = hs / kt_shape(KT_SWEEP).cb;
-      p.nranges = (int)(t2 >= target ? 1 : cdiv(target, t2) < ng ? cdiv(target, t2) : ng);
+      nranges = (int)(t2 >= target ? 1 : cdiv(target, t2) < ng ? cdiv(target, t2) : ng);
     }
-    p.tm = kTileTm;
-    const int tm2 = kt_shape(p.kt).tm;
-    p.mpad = cdiv(M, tm2) * tm2;
-    p.mq = tiles * kTileTm;
-    p.off_h = 0;
-    p.off_q = align256((size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
-    p.ws_bytes = p.off_q;
-    if (p.spw == 1) {
-      const size_t parts = (size_t)s.hc * (size_t)p.nseg;
-      p.off_ss = align256(p.off_q + parts * (size_t)p.mq * np * sizeof(float));
-      p.ws_bytes = align256(p.off_ss + parts * (size_t)p.mq * sizeof(float));
-    }
+    make_tile(s, M, spw, nseg, kt, nranges, &p);
     return p;
   }
   const KFShape f64 = kf_shape(KF_T64);
@@ -286,6 +319,120 @@ inline size_t workspace_bound(const Shape& s, int64_t M) {
   for (int64_t t = 1; t * kTileTm <= M && t <= 256; ++t) {
     const size_t b = make_plan(s, t * kTileTm).ws_bytes;
     best = best > b ? best : b;
+  }
+  return best;
+}
+
+// ---------------------------------------------------------------------------
+// Tuned plans. A Choice names a plan family and its parameters; a table of
+// (token count, Choice) entries replaces the heuristic near its keys: a token
+// count M resolves to the nearest key in log space (ties to the smaller key);
+// below the smallest key, for an entry marked heuristic, and wherever the
+// entry's choice cannot run the shape at M, make_plan decides.
+constexpr int kChoiceHeuristic = -1;
+constexpr int64_t kSplitChoiceMaxM = 256;  // a decode-plan choice serves token counts up to this
+struct Choice {
+  int kind = kChoiceHeuristic;  // kChoiceHeuristic, PLAN_SPLIT or PLAN_TILE
+  int kd = 0;                   // PLAN_SPLIT: down-kernel variant
+  int spw = 1, nseg = 1, kt = KT_S128, nranges = 1;  // PLAN_TILE: as make_tile
+};
+struct TableEntry {
+  int64_t M;
+  Choice c;
+};
+
+inline bool plan_from_choice(const Shape& s, int64_t M, const Choice& c, Plan* out) {
+  if (c.kind == PLAN_SPLIT)
+    return s.hc == 4 && M >= 1 && M <= kSplitChoiceMaxM && c.kd >= 0 && c.kd < KD_NVAR && make_split(s, M, c.kd, out);
+  if (c.kind == PLAN_TILE) return make_tile(s, M, c.spw, c.nseg, c.kt, c.nranges, out);
+  return false;
+}
+
+// Every choice that can run the shape at M (the candidates a tuner times),
+// written to out[0 .. min(count, cap)); returns the count.
+inline int plan_choices(const Shape& s, int64_t M, Choice* out, int cap) {
+  int n = 0;
+  auto add = [&](const Choice& c) {
+    Plan p;
+    if (!plan_from_choice(s, M, c, &p)) return;
+    if (n < cap) out[n] = c;
+    ++n;
+  };
+  for (int kd = 0; kd < KD_NVAR; ++kd) {
+    Choice c;
+    c.kind = PLAN_SPLIT;
+    c.kd = kd;
+    add(c);
+  }
+  const int ups[3] = {KT_S128, KT_SWEEP, KT_GEN};
+  const int pairs = s.hs / 128;
+  for (int spw : {1, 4})
+    for (int d = 1; d <= pairs; ++d) {
+      if (pairs % d != 0 || (spw == 4 && d != 1)) continue;
+      for (int kt : ups)
+        for (int nr = 1; nr <= (kt == KT_SWEEP ? 8 : 1); nr *= 2) {
+          Choice c;
+          c.kind = PLAN_TILE;
+          c.spw = spw;
+          c.nseg = d;
+          c.kt = kt;
+          c.nranges = nr;
+          add(c);
+        }
+    }
+  return n;
+}
+
+// Index of the table entry that M resolves to, or -1 (below the smallest key).
+inline int table_index(const TableEntry* t, int n, int64_t M) {
+  if (n <= 0 || M < t[0].M) return -1;
+  int i = 0;
+  while (i + 1 < n && t[i + 1].M <= M) ++i;
+  if (i + 1 < n && (double)M * (double)M > (double)t[i].M * (double)t[i + 1].M) ++i;  // nearer in log space
+  return i;
+}
+
+// The plan used for M with a table (n = 0: the heuristic).
+inline Plan plan_for(const Shape& s, int64_t M, const TableEntry* t, int n) {
+  const int i = table_index(t, n, M);
+  Plan p;
+  if (i >= 0 && t[i].c.kind != kChoiceHeuristic && plan_from_choice(s, M, t[i].c, &p)) return p;
+  return make_plan(s, M);
+}
+
+// Workspace that serves every M' <= M with a table. Entry i serves the
+// interval of token counts nearer (in log space) to its key than to its
+// neighbours', which may start below the key; its choice needs the most at
+// the largest M' it serves (a decode-plan choice at the largest M' <= 256),
+// and where the choice cannot run, the heuristic serves, which
+// workspace_bound covers.
+inline size_t workspace_bound_table(const Shape& s, int64_t M, const TableEntry* t, int n) {
+  if (M <= 0) return 0;
+  if (n <= 0) return workspace_bound(s, M);
+  // largest M' that resolves to entry i (entry i + 1 is nearer above it)
+  auto last_of = [&](int i) -> int64_t {
+    if (i + 1 >= n) return INT64_MAX;
+    const double lim = (double)t[i].M * (double)t[i + 1].M;
+    int64_t b = (int64_t)__builtin_sqrt(lim);
+    while ((double)(b + 1) * (double)(b + 1) <= lim) ++b;
+    while ((double)b * (double)b > lim) --b;
+    return b;
+  };
+  size_t best = workspace_bound(s, M < t[0].M ? M : t[0].M);  // heuristic below the first key
+  int64_t lo = t[0].M;
+  for (int i = 0; i < n && lo <= M; ++i) {
+    const int64_t last = last_of(i);
+    const int64_t hi = last < M ? last : M;
+    const size_t h = workspace_bound(s, hi);  // heuristic wherever entry i falls back
+    best = best > h ? best : h;
+    Plan p;
+    if (t[i].c.kind == PLAN_SPLIT) {
+      const int64_t m = hi < kSplitChoiceMaxM ? hi : kSplitChoiceMaxM;
+      if (m >= lo && plan_from_choice(s, m, t[i].c, &p)) best = best > p.ws_bytes ? best : p.ws_bytes;
+    } else if (t[i].c.kind == PLAN_TILE && plan_from_choice(s, hi, t[i].c, &p)) {
+      best = best > p.ws_bytes ? best : p.ws_bytes;
+    }
+    lo = last == INT64_MAX ? INT64_MAX : last + 1;
   }
   return best;
 }

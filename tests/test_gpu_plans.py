@@ -1,0 +1,148 @@
+"""GPU parity of every plan a tuned table may choose, and of the tuner end to
+end: each candidate plan (hcgr_plan_candidates) installed as a one-entry
+table must match the fp64 oracle; a table written by
+skinny_gemm_hcgr_amd.tune must load and give oracle-matching results at and
+between its keys."""
+from __future__ import annotations
+
+import os
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import check_all
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = synth.Shape()
+
+
+@pytest.fixture(scope="module")
+def H():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import skinny_gemm_hcgr_amd as H
+    H.load_library()
+    return H
+
+
+@pytest.fixture(scope="module")
+def weights():
+    return synth.make_weights(SHAPE, seed=0, device="cuda")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def sample_rows(M, n=24, seed=3):
+    rng = np.random.default_rng(seed)
+    rows = {0, M // 2, M - 1} | set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def run_oracle(inp, rows=None):
+    R, y, inj = inp["R"], inp["y"], inp["inj"]
+    if rows is not None:
+        idx = torch.as_tensor(rows, device="cuda")
+        R, y, inj = R[idx], y[idx], inj[idx]
+    return oracle.forward(oracle.OracleConfig(), R.cpu(), y.cpu(), inj.cpu(), inp["wnorm"].cpu(), inp["wd"].cpu(),
+                          inp["wi"].cpu(), inp["wu"].cpu())
+
+
+def check_rows(out, ref, rows):
+    if rows is None:
+        check_all(out, ref)
+    else:
+        idx = torch.as_tensor(rows, device="cuda")
+        check_all({k: out[k][idx] for k in ("R2", "rrms", "inj_next", "x")}, ref)
+
+
+@pytest.mark.parametrize("M", [1, 32, 100, 300, 4100])
+def test_every_candidate_plan(H, weights, M):
+    op = H.HCGR(H.Config(), 0)
+    inp = synth.make_inputs(M, SHAPE, seed=60 + M, device="cuda", weights=weights)
+    rows = None if M <= 300 else sample_rows(M)
+    ref = run_oracle(inp, rows)
+    cands = H.hcgr_plan_candidates(op.cfg, M)
+    _say(f"[plans] M={M}: {len(cands)} candidates")
+    for c in cands:
+        op.set_plan_table([c])
+        desc = op.describe(M)
+        _say(f"[plans]   {desc}")
+        out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"])
+        torch.cuda.synchronize()
+        try:
+            check_rows(out, ref, rows)
+        except AssertionError as e:
+            raise AssertionError(f"{c} ({desc}): {e}") from None
+    op.close()
+
+
+def test_tuner_end_to_end(H, weights):
+    from skinny_gemm_hcgr_amd import tune
+    cfg = H.Config()
+    entries, failures = tune.tune(cfg, [16, 600], reps=3, log=_say)
+    assert len(entries) == 2 and not failures, failures
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "plans.json")
+        tune.write_table(path, cfg, entries)
+        op = H.HCGR(cfg, 0, plan_table=path)
+        with pytest.raises(ValueError):
+            H.load_plan_table(path, H.Config(hs=1024))  # tuned for another shape
+    for M in (16, 100, 600, 2000):
+        _say(f"[plans] tuned table M={M}: {op.describe(M)}")
+        inp = synth.make_inputs(M, SHAPE, seed=70 + M, device="cuda", weights=weights)
+        out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"])
+        torch.cuda.synchronize()
+        rows = None if M <= 600 else sample_rows(M)
+        check_rows(out, run_oracle(inp, rows), rows)
+    op.close()
+
+
+def test_bad_table_leaves_the_handle_unchanged(H, weights):
+    op = H.HCGR(H.Config(), 0)
+    good = [{"tokens": 64, "kind": H.HCGR_PLAN_TILE, "down_variant": 0, "streams_per_wg": 1, "segments": 4,
+             "up_variant": 0, "ranges": 1}]
+    op.set_plan_table(good)
+    before = op.describe(64)
+    with pytest.raises(H.HcgrError):
+        H.hcgr_set_plan_table(op.handle, good + [dict(good[0], tokens=32)])  # keys not increasing
+    assert H.hcgr_plan_lookup(op.cfg, good, 64)[1] == before
+    inp = synth.make_inputs(64, SHAPE, seed=71, device="cuda", weights=weights)
+    out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"])
+    torch.cuda.synchronize()
+    check_all(out, run_oracle(inp))
+    op.close()
+
+
+@pytest.mark.parametrize("merged", [False, True])
+def test_shipped_table_at_every_tuned_key(H, weights, merged):
+    """Every non-heuristic entry of the shipped tables, at its own key, against
+    the oracle (sampled rows above 1024 tokens)."""
+    cfg = H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336) if merged else H.Config()
+    op = H.HCGR(cfg, 0, plan_table="shipped")
+    assert op.table
+    for e in op.table:
+        if e["kind"] == H.HCGR_PLAN_HEURISTIC:
+            continue
+        M = e["tokens"]
+        _say(f"[plans] shipped merged={merged} M={M}: {op.describe(M)}")
+        inp = synth.make_inputs(M, SHAPE, seed=80 + M, device="cuda", weights=weights)
+        wd = synth.fold_merged_weight(inp["wd"], inp["wi"], inp["wnorm"], 336, SHAPE.hs) if merged else inp["wd"]
+        out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], wd, None if merged else inp["wi"], inp["wu"])
+        torch.cuda.synchronize()
+        rows = None if M <= 1024 else sample_rows(M)
+        R, y, inj = inp["R"], inp["y"], inp["inj"]
+        if rows is not None:
+            idx = torch.as_tensor(rows, device="cuda")
+            R, y, inj = R[idx], y[idx], inj[idx]
+        ocfg = oracle.OracleConfig(merged=merged, n_pad=336 if merged else 0)
+        ref = oracle.forward(ocfg, R.cpu(), y.cpu(), inj.cpu(), inp["wnorm"].cpu(), wd.cpu(),
+                             None if merged else inp["wi"].cpu(), inp["wu"].cpu())
+        check_rows(out, ref, rows)
+    op.close()
