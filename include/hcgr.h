@@ -239,7 +239,9 @@ typedef struct hcgr_plan_choice {
     int64_t tokens;         /* table key (token count >= 1); a candidate carries the M it was made for */
     int32_t kind;           /* HCGR_PLAN_HEURISTIC, HCGR_PLAN_SPLIT or HCGR_PLAN_TILE                 */
     int32_t down_variant;   /* SPLIT: 0 .. HCGR_SPLIT_VARIANTS-1 (token tile, row blocks, k waves,
-                               chunk width; hcgr_plan_lookup describes each); serves M <= 256 only  */
+                               chunk width; hcgr_plan_lookup describes each); serves M <= 256 only.
+                               TILE: 0 = 64-token down tiles, 1 = 128-token down tiles (needs
+                               streams_per_wg = 1)                                                   */
     int32_t streams_per_wg; /* TILE: 1, or 4 with HC = 4                                            */
     int32_t segments;       /* TILE with 1 stream per workgroup: column segments per stream,
                                a divisor of HS/128 (1 with 4 streams per workgroup)                  */

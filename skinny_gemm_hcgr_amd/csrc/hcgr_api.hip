@@ -184,7 +184,7 @@ hcgr_plan_choice from_choice(const hcgr::Choice& c, int64_t tokens) {
   hcgr_plan_choice o;
   o.tokens = tokens;
   o.kind = c.kind;
-  o.down_variant = c.kind == HCGR_PLAN_SPLIT ? c.kd : 0;
+  o.down_variant = c.kind == HCGR_PLAN_SPLIT || c.kind == HCGR_PLAN_TILE ? c.kd : 0;
   o.streams_per_wg = c.kind == HCGR_PLAN_TILE ? c.spw : 0;
   o.segments = c.kind == HCGR_PLAN_TILE ? c.nseg : 0;
   o.up_variant = c.kind == HCGR_PLAN_TILE ? c.kt : 0;
@@ -268,10 +268,12 @@ static void describe(const hcgr::Shape& s, const hcgr::Plan& p, int64_t M, char*
     } else if (p.kind == hcgr::PLAN_TILE) {
       hcgr::KTShape t = hcgr::kt_shape(p.kt);
       snprintf(buf, len,
-               "M=%lld plan=tile | k1_tile tm=%d waves=8 stage_k=64 streams/wg=%d row_splits=%d segments=%d grid=%lld%s | "
+               "M=%lld plan=tile | k1_tile tm=%d waves=8 stage_k=64 streams/wg=%d row_splits=%d segments=%d%s grid=%lld%s | "
                "%s tm=%d channels=%d ranges=%d grid=%lld | workspace=%zu",
-               (long long)M, (int)hcgr::kTileTm, p.spw, p.nsplit, p.nseg,
-               (long long)(hcgr::cdiv(M, hcgr::kTileTm) * p.nsplit * (s.hc / p.spw) * p.nseg), p.spw == 1 ? " | k1_sum" : "",
+               (long long)M, p.tm, p.spw, p.nsplit, p.nseg, p.xgroup ? " tile_xcd" : "",
+               (long long)((p.xgroup ? hcgr::cdiv(hcgr::cdiv(M, (int64_t)p.tm), 8) * 8 : hcgr::cdiv(M, (int64_t)p.tm)) *
+                           p.nsplit * (s.hc / p.spw) * p.nseg),
+               p.spw == 1 ? " | k1_sum" : "",
                k2_name(p.kt), t.tm, t.cb, p.nranges, k2_grid(s, p, M), p.ws_bytes);
     } else {
       hcgr::KFShape f = hcgr::kf_shape(p.kf);

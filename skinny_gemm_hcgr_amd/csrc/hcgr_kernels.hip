@@ -828,19 +828,35 @@ struct Tile1Args {
   int NP;
   int nseg;    // column segments per stream (SPW = 1 only); > 1: rrms is formed by hcgr_k1_sum
   float* SSp;  // [HC*nseg][Mq] per-segment sums of squares (nseg > 1)
+  int tiles;   // token tiles
+  int xgroup;  // 1: the workgroups of one token tile share an XCD (grid rounded up to 8 tiles)
 };
 
 template <int N>
 using ic = std::integral_constant<int, N>;
 
-template <int SPW>
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(ic<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// TM: tokens per tile (64, or 128 with one stream per workgroup); D: depth of
+// the R/y/Wnorm prefetch ring in stages (4 for 64 tokens; 3 for 128, whose
+// threads own two tokens' chunks per stage).
+template <int SPW, int TM, int D>
 __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
-  constexpr int TM = (int)kTileTm, NT = 512, BPW = 6, NTB = 2, D = 4;
+  constexpr int NT = 512, BPW = 6, NTB = TM / 32, TPT = TM / 64;  // TPT: tokens per thread per stage
   constexpr int WGRP = 6;  // 8-row weight groups per wave per stage
   constexpr int WBYTES = 8 * WGRP * 1024, ABYTES = TM * 128;
   constexpr int NSET = SPW == 4 ? 1 : 0;  // rrms-scaled total kept in registers
+  constexpr int NL = 2 * TPT + 1;         // prefetch loads per thread per stage: R and y per token, Wnorm
+  constexpr int G = D % 2 ? 2 * D : D;    // iterations per unrolled group: ring slot period D, buffer parity 2
   constexpr uint32_t kOut = 0x80000000u;  // offset past every buffer range
-  static_assert(TM == 64 && 8 * WGRP >= 2 * kTileMaxBlk && (kTileMaxBlk * 3) / 4 + BPW <= 8 * WGRP / 2,
+  static_assert((TM == 64 || (TM == 128 && SPW == 1)) && D >= 2 && D <= 4, "tile shapes");
+  static_assert(8 * WGRP >= 2 * kTileMaxBlk && (kTileMaxBlk * 3) / 4 + BPW <= 8 * WGRP / 2,
                 "tile shape: every wave's blocks (read or not) lie inside the weight buffer");
   __shared__ __attribute__((aligned(1024))) uint8_t w_0[WBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t w_1[WBYTES];
@@ -854,11 +870,26 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
   const int rq = wave & 3, th = wave >> 2;
   const int NG = a.HC / SPW;  // stream groups (SPW = 4 only with HC = 4)
   const int nseg = SPW == 1 ? a.nseg : 1;
-  const int seg = (int)(blockIdx.x % nseg);
-  const int bid = (int)(blockIdx.x / nseg);
-  const int sg = bid % NG;
-  const int split = (bid / NG) % a.nsplit;
-  const int64_t m0 = (int64_t)(bid / (NG * a.nsplit)) * TM;
+  // workgroup -> (token tile, row split, stream group, column segment). With
+  // xgroup, workgroup b serves tile 8 (q / P) + b % 8, q = b / 8, P = the
+  // workgroups of a tile: all of a tile's workgroups share b % 8 and so run
+  // on one XCD (workgroups go round-robin over the 8 XCDs), where y and the
+  // tile's R rows are fetched from HBM once. Otherwise b = ((tile * nsplit +
+  // split) * NG + sg) * nseg + seg.
+  int wq, tile_i;
+  if (a.xgroup) {
+    const int P = a.nsplit * NG * nseg, q = (int)(blockIdx.x >> 3);
+    tile_i = (q / P) * 8 + (int)(blockIdx.x & 7);
+    wq = q % P;
+    if (tile_i >= a.tiles) return;  // grid rounded up to whole octets of tiles
+  } else {
+    tile_i = (int)(blockIdx.x / (nseg * NG * a.nsplit));
+    wq = (int)(blockIdx.x % (nseg * NG * a.nsplit));
+  }
+  const int seg = wq % nseg;
+  const int sg = (wq / nseg) % NG;
+  const int split = wq / (nseg * NG);
+  const int64_t m0 = (int64_t)tile_i * TM;
   const int rows = (int)min((int64_t)TM, a.M - m0);
   const int s_first = sg * SPW;
   const int b0 = split * a.nblk / a.nsplit, b1 = (split + 1) * a.nblk / a.nsplit;
@@ -898,7 +929,8 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
     if (!down) winj |= 1u << j;
   }
   winj = __builtin_amdgcn_readfirstlane(winj);
-  // this thread's chunk of every stage: token tok, LDS slot tid & 7 (chunk swz)
+  // this thread's chunks of every stage: tokens tok + 64 j (j < TPT), LDS slot
+  // tid & 7 (chunk swz) of their rows
   const int tok = tid >> 3;
   const uint32_t offR = (uint32_t)tok * rowb + swz * 16u;
   const uint32_t offY = (uint32_t)tok * (uint32_t)HS * 2u + swz * 16u;
@@ -912,54 +944,74 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds((winj >> j) & 1u ? rW1 : rW0, (lds_void_t*)(wbuf + (wave + 8 * j) * 1024),
                                                16, valid ? woff[j] + kb : kOut, 0, 0, 0);
   };
-  u32x4_t rv[D], yv[D], wv[D];  // prefetch ring: stage j in slot j % D
+  u32x4_t rv[D][TPT], yv[D][TPT], wv[D];  // prefetch ring: stage j in slot j % D
   auto load_ry = [&](auto SL, bool valid, int s, int c0) {
     constexpr int k = decltype(SL)::value;
     const uint32_t col = (uint32_t)c0 * 2u;
-    const uint32_t oR = valid ? offR + (uint32_t)(s * HS) * 2u + col : kOut;
-    const uint32_t oY = valid ? offY + col : kOut;
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const uint32_t oR = valid ? offR + (uint32_t)(j * 64) * rowb + (uint32_t)(s * HS) * 2u + col : kOut;
+      const uint32_t oY = valid ? offY + (uint32_t)(j * 64 * HS) * 2u + col : kOut;
+      rv[k][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rR, (int)oR, 0, 0));
+      yv[k][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rY, (int)oY, 0, 0));
+    }
     const uint32_t oW = valid ? (wnc ? (uint32_t)(s * HS) * 2u : 0u) + col + swz * 16u : kOut;
-    rv[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rR, (int)oR, 0, 0));
-    yv[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rY, (int)oY, 0, 0));
     wv[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rWn, (int)oW, 0, 0));
   };
 
-  float ss = 0.0f, ih = 0.0f, il = 0.0f;
+  float ss[TPT], ih[TPT], il[TPT];
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) ss[j] = ih[j] = il[j] = 0.0f;
   // stages past the last one combine the zeros their prefetch returned and
   // store nothing (out-of-range R2 offset); running them keeps every ring
   // slot consumed on every path
   auto combine = [&](auto SL, bool valid, int s, int c0, uint8_t* abuf) {
     constexpr int k = decltype(SL)::value;
-    uint32_t o2[4], ou[4];
-    float acc = ss;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t rw = rv[k][e], yw = yv[k][e], ww = wv[k][e];
-      const float r0 = fmaf(bf_lo(yw), il, fmaf(bf_lo(yw), ih, bf_lo(rw)));
-      const float r1 = fmaf(bf_hi(yw), il, fmaf(bf_hi(yw), ih, bf_hi(rw)));
-      acc = fmaf(r0, r0, acc);
-      acc = fmaf(r1, r1, acc);
-      o2[e] = pack_bf2(r0, r1);
-      ou[e] = pack_bf2(r0 * (1.0f + bf_lo(ww)), r1 * (1.0f + bf_hi(ww)));
-    }
-    ss = acc;
-    bst16(rR2, valid ? offR + (uint32_t)(s * HS + c0) * 2u : kOut, make_uint4(o2[0], o2[1], o2[2], o2[3]));
-    *reinterpret_cast<u32x4_t*>(abuf + la_off) = u32x4_t{ou[0], ou[1], ou[2], ou[3]};
-  };
-  // (N) the stream's sum of squares -> rrms of this thread's token
-  auto stream_rrms = [&](int sl) {
-    float v = ss;
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    ss = 0.0f;
-    if ((tid & 7) == 0) {
-      if (nseg == 1) {
-        rrs[sl][tok] = 1.0f / sqrtf(v * a.inv_hs + a.eps);
-      } else {  // a segment of the stream: its sum of squares goes out, the partial stays unscaled
-        rrs[sl][tok] = 1.0f;
-        if (lead && tok < rows) a.SSp[(int64_t)(s_first * nseg + seg) * a.Mq + m0 + tok] = v;
+    for (int j = 0; j < TPT; ++j) {
+      uint32_t o2[4], ou[4];
+      float acc = ss[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t rw = rv[k][j][e], yw = yv[k][j][e], ww = wv[k][e];
+        const float r0 = fmaf(bf_lo(yw), il[j], fmaf(bf_lo(yw), ih[j], bf_lo(rw)));
+        const float r1 = fmaf(bf_hi(yw), il[j], fmaf(bf_hi(yw), ih[j], bf_hi(rw)));
+        acc = fmaf(r0, r0, acc);
+        acc = fmaf(r1, r1, acc);
+        o2[e] = pack_bf2(r0, r1);
+        ou[e] = pack_bf2(r0 * (1.0f + bf_lo(ww)), r1 * (1.0f + bf_hi(ww)));
       }
+      ss[j] = acc;
+      bst16(rR2, valid ? offR + (uint32_t)(j * 64) * rowb + (uint32_t)(s * HS + c0) * 2u : kOut,
+            make_uint4(o2[0], o2[1], o2[2], o2[3]));
+      *reinterpret_cast<u32x4_t*>(abuf + la_off + j * 64 * 128) = u32x4_t{ou[0], ou[1], ou[2], ou[3]};
+    }
+  };
+  // (N) the stream's sum of squares -> rrms of this thread's tokens
+  auto stream_rrms = [&](int sl) {
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      float v = ss[j];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      ss[j] = 0.0f;
+      const int t = tok + 64 * j;
+      if ((tid & 7) == 0) {
+        if (nseg == 1) {
+          rrs[sl][t] = 1.0f / sqrtf(v * a.inv_hs + a.eps);
+        } else {  // a segment of the stream: its sum of squares goes out, the partial stays unscaled
+          rrs[sl][t] = 1.0f;
+          if (lead && t < rows) a.SSp[(int64_t)(s_first * nseg + seg) * a.Mq + m0 + t] = v;
+        }
+      }
+    }
+  };
+  auto set_iw = [&](int sl) {  // injection weights of stream s_first + sl for this thread's tokens
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      ih[j] = iwh[sl][tok + 64 * j];
+      il[j] = iwl[sl][tok + 64 * j];
     }
   };
 
@@ -1042,15 +1094,10 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
 
   // prologue: weights of stage 0, R/y/Wnorm of stages 0 .. D-1
   issue_w(true, s0, c0, w_0);
-  load_ry(ic<0>{}, true, sD, cD);
-  advance(sD, cD);
-  load_ry(ic<1>{}, 1 < nst, sD, cD);
-  advance(sD, cD);
-  load_ry(ic<2>{}, 2 < nst, sD, cD);
-  advance(sD, cD);
-  load_ry(ic<3>{}, 3 < nst, sD, cD);
-  advance(sD, cD);
-  static_assert(D == 4, "prologue and loop body above are written for a ring of four");
+  static_for<0, D>([&](auto J) {
+    load_ry(J, decltype(J)::value < nst, sD, cD);
+    advance(sD, cD);
+  });
   // (COMBINE) iw = 2*sigmoid(inj/HC) in fp64, kept as fp32 hi + lo
   if (tid < SPW * TM) {
     const double v = it < rows ? 2.0 / (1.0 + exp(-(double)bf1(injb) / (double)a.HC)) : 0.0;
@@ -1059,37 +1106,39 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
     iwl[isl][it] = (float)(v - (double)hi);
   }
   lds_sync();
-  ih = iwh[0][tok];
-  il = iwl[0][tok];
-  asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // weights and R/y of stage 0
+  set_iw(0);
+  // weights and R/y/Wnorm of stage 0: the NL loads of each of stages 1 .. D-1 stay in flight
+  if constexpr (D == 4 && NL == 3) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else if constexpr (D == 3 && NL == 5) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else static_assert(D == 4 && NL == 3, "prologue wait written for these two shapes");
   combine(ic<0>{}, true, s0, c0, act_0);
   if (c0 + 64 == c_end) stream_rrms(0);
 
-  // Iteration st (slot k = st % D). On entry the newest memory operations of
-  // this thread are, in issue order: the weights of stage st, the R2 store
-  // (and, closing a column segment, a sum-of-squares store), then the
-  // R/y/Wnorm loads of stage st+D-1. The vector memory counter covers loads
-  // and stores; with the stores issued before the prefetch, vmcnt(3) leaves
-  // exactly those three prefetch loads in flight whether or not a store may
+  // Iteration st (position p = st % G in its group: ring slot k = p % D,
+  // buffer parity p % 2). On entry the newest memory operations of this
+  // thread are, in issue order: the weights of stage st, the R2 stores (and,
+  // closing a column segment, sum-of-squares stores), then the NL R/y/Wnorm
+  // loads of stage st+D-1. The vector memory counter covers loads and
+  // stores; with the stores issued before the prefetch, vmcnt(NL) leaves
+  // exactly those prefetch loads in flight whether or not a store may
   // complete ahead of earlier loads. Everything it waits for includes
   // R/y/Wnorm of stage st+1 (issued D-1 iterations back).
-  auto iteration = [&](auto K, int st) {
-    constexpr int k = decltype(K)::value;
-    asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  auto iteration = [&](auto P, int st) {
+    constexpr int p = decltype(P)::value, k = p % D;
+    if constexpr (NL == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else if constexpr (NL == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else static_assert(NL == 3, "iteration wait written for one or two tokens per thread");
     lds_sync();  // weights of stage st landed for every wave; iteration st-1 fully done
-    uint8_t* wcur = (k & 1) ? w_1 : w_0;
-    uint8_t* wnxt = (k & 1) ? w_0 : w_1;
-    uint8_t* acur = (k & 1) ? act_1 : act_0;
-    uint8_t* anxt = (k & 1) ? act_0 : act_1;
+    uint8_t* wcur = (p & 1) ? w_1 : w_0;
+    uint8_t* wnxt = (p & 1) ? w_0 : w_1;
+    uint8_t* acur = (p & 1) ? act_1 : act_0;
+    uint8_t* anxt = (p & 1) ? act_0 : act_1;
     const bool v1 = st + 1 < nst;
     issue_w(v1, s1, c1, wnxt);
-    if (v1 && c1 == c_begin) {  // stage st+1 opens stream s1
-      ih = iwh[s1 - s_first][tok];
-      il = iwl[s1 - s_first][tok];
-    }
+    if (v1 && c1 == c_begin) set_iw(s1 - s_first);  // stage st+1 opens stream s1
     combine(ic<(k + 1) % D>{}, v1, s1, c1, anxt);
     if (v1 && c1 + 64 == c_end) stream_rrms(s1 - s_first);  // stage st+1 closes stream s1
-    load_ry(K, st + D < nst, sD, cD);  // slot k held stage st, combined in iteration st-1
+    load_ry(ic<k>{}, st + D < nst, sD, cD);  // slot k held stage st, combined in iteration st-1
     if (st < nst) {
       contract(wcur, acur);
       if (c0 + 64 == c_end) fold(s0 - s_first);  // stage st closed stream s0 (its rrms is visible since the barrier)
@@ -1098,14 +1147,9 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
     advance(s1, c1);
     advance(sD, cD);
   };
-  // groups of four iterations (slots and buffers by position in the group);
+  // groups of G iterations (slots and buffers by position in the group);
   // iterations past the last stage only keep the ring in step
-  for (int st = 0; st < nst; st += D) {
-    iteration(ic<0>{}, st);
-    iteration(ic<1>{}, st + 1);
-    iteration(ic<2>{}, st + 2);
-    iteration(ic<3>{}, st + 3);
-  }
+  for (int st = 0; st < nst; st += G) static_for<0, G>([&](auto P) { iteration(P, st + decltype(P)::value); });
   // the loads issued past the last stage must land before the LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -2094,9 +2138,13 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     a.R2 = f.R2; a.rrms = f.rrms; a.h = H; a.inj_next = f.inj_next; a.ld_inj_next = f.ld_inj_next;
     a.Q = Q; a.Mq = p.mq; a.NP = s.np();
     a.nseg = p.nseg; a.SSp = reinterpret_cast<float*>(ws + p.off_ss);
-    const dim3 g1((unsigned)(cdiv(f.M, kTileTm) * p.nsplit * (s.hc / p.spw) * p.nseg));
-    if (p.spw == 4) klaunch(hcgr_k1_tile<4>, g1, dim3(512), 0, st, tm.stage(0), a);
-    else klaunch(hcgr_k1_tile<1>, g1, dim3(512), 0, st, tm.stage(0), a);
+    a.tiles = (int)cdiv(f.M, (int64_t)p.tm);
+    a.xgroup = p.xgroup;
+    const int64_t tiles_g = p.xgroup ? cdiv((int64_t)a.tiles, 8) * 8 : a.tiles;
+    const dim3 g1((unsigned)(tiles_g * p.nsplit * (s.hc / p.spw) * p.nseg));
+    if (p.spw == 4) klaunch(hcgr_k1_tile<4, 64, 4>, g1, dim3(512), 0, st, tm.stage(0), a);
+    else if (p.tm == 128) klaunch(hcgr_k1_tile<1, 128, 3>, g1, dim3(512), 0, st, tm.stage(0), a);
+    else klaunch(hcgr_k1_tile<1, 64, 4>, g1, dim3(512), 0, st, tm.stage(0), a);
   } else {
   FullArgs a;
   a.R = f.R; a.y = f.y; a.inj = f.inj; a.ld_inj = f.ld_inj;

@@ -146,3 +146,54 @@ def test_shipped_table_at_every_tuned_key(H, weights, merged):
                              None if merged else inp["wi"].cpu(), inp["wu"].cpu())
         check_rows(out, ref, rows)
     op.close()
+
+
+def _tile128(M, seg, up, ranges=1):
+    import skinny_gemm_hcgr_amd as H
+    return {"tokens": M, "kind": H.HCGR_PLAN_TILE, "down_variant": 1, "streams_per_wg": 1, "segments": seg,
+            "up_variant": up, "ranges": ranges}
+
+
+@pytest.mark.parametrize("hc,hs,r,M,seg,up,extra", [
+    (4, 2560, 320, 129, 4, 0, ""), (4, 2560, 320, 16400, 1, 1, ""), (4, 640, 64, 1000, 5, 0, ""),
+    (4, 1024, 512, 700, 2, 0, ""),          # two row splits of the down rows
+    (2, 1024, 320, 300, 8, 2, ""), (8, 512, 96, 257, 1, 2, ""), (1, 2560, 64, 90, 10, 2, ""),
+    (4, 1280, 160, 500, 2, 1, "wnfull"), (4, 2560, 320, 384, 1, 0, "merged"), (4, 2560, 320, 200, 2, 0, "mix"),
+])
+def test_tile128_shapes(H, hc, hs, r, M, seg, up, extra):
+    """The 128-token down tile (two tokens per thread, a prefetch ring of
+    three stages, groups of six iterations) across shapes: partial last tiles,
+    column segments, row splits, other stream counts, full-width Wnorm, merged
+    weights and the mix entry point."""
+    shape = synth.Shape(hc=hc, hs=hs, r=r)
+    merged = extra == "merged"
+    n_pad = (r + hc + 15) // 16 * 16
+    cfg = H.Config(hc=hc, hs=hs, r=r, wnorm_len=hc * hs if extra == "wnfull" else 0,
+                   weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED if merged else H.HCGR_WEIGHTS_SEPARATE,
+                   n_pad=n_pad if merged else 0)
+    op = H.HCGR(cfg, 0, plan_table=[_tile128(M, seg, up)])
+    desc = op.describe(M)
+    _say(f"[plans] tile128 {extra} hc={hc} hs={hs} r={r} M={M}: {desc}")
+    assert "k1_tile tm=128" in desc
+    inp = synth.make_inputs(M, shape, seed=90 + M, device="cuda", wnorm_full=extra == "wnfull")
+    wd = synth.fold_merged_weight(inp["wd"], inp["wi"], inp["wnorm"], n_pad, hs) if merged else inp["wd"]
+    wi = None if merged else inp["wi"]
+    ocfg = oracle.OracleConfig(hc=hc, hs=hs, r=r, wnorm_full=extra == "wnfull", merged=merged,
+                               n_pad=n_pad if merged else 0)
+    rows = None if M <= 1000 else sample_rows(M)
+    sel = (lambda t: t) if rows is None else (lambda t: t[torch.as_tensor(rows, device="cuda")])
+    if extra == "mix":
+        out = op.mix(inp["R"], inp["wnorm"], wd, wi, inp["wu"])
+        torch.cuda.synchronize()
+        ref = oracle.mix(ocfg, sel(inp["R"]).cpu(), inp["wnorm"].cpu(), wd.cpu(), wi.cpu(), inp["wu"].cpu())
+        from parity import check_rrms, check_tol
+        check_rrms(sel(out["rrms"]), ref["rrms"])
+        check_tol(sel(out["inj_next"]), ref["inj_next"], "inj_next")
+        check_tol(sel(out["x"]), ref["x"], "x")
+    else:
+        out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], wd, wi, inp["wu"])
+        torch.cuda.synchronize()
+        ref = oracle.forward(ocfg, sel(inp["R"]).cpu(), sel(inp["y"]).cpu(), sel(inp["inj"]).cpu(),
+                             inp["wnorm"].cpu(), wd.cpu(), None if merged else wi.cpu(), inp["wu"].cpu())
+        check_rows(out, ref, rows)
+    op.close()
