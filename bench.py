@@ -225,6 +225,26 @@ def time_graph(H, op, sets, replays, stream):
     return us
 
 
+def measure_copy_gbs(torch, nbytes=1 << 30, reps=10):
+    """Achievable HBM bandwidth on this machine: read + write bytes per second of a
+    plain device-to-device copy of nbytes (median of reps)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / sorted(times)[len(times) // 2] / 1e9
+
+
 def kernel_source_digest():
     """Digest of the kernel sources; a counter summary taken on other sources no longer applies."""
     import glob
@@ -453,6 +473,8 @@ def main():
 
     dom = max(head["kernels_us"], key=lambda k: head["kernels_us"][k])
     roof = roofline_entry(dom, M, head["kernels_us"][dom], merged, head["plan"], args.workload)
+    copy_gbs = measure_copy_gbs(torch)
+    roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbs, 4)
     line = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["us_per_call"] / 1e3, 6),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -464,6 +486,9 @@ def main():
             "us_per_call_warm": warm["us_per_call"] if warm else None,
             "op_roofline_frac": head["op_roofline_frac"], "op_hbm_frac": head["op_hbm_frac"],
             "kernels_us": head["kernels_us"], "roofline": roof,
+            "measured_peaks": {"hbm_copy_gbs": round(copy_gbs, 1),
+                               "note": "read + write bytes per second of a 1 GiB device copy on this box; "
+                                       "op_hbm_frac and roofline.frac use the published 8 TB/s"},
             "context": {"pages_two_stage_graph_us": {"1": 21.0, "32": 28.8, "1024": 76.3, "8192": 339.2,
                                                      "65536": 2636.4},
                         "note": "page numbers: MI355X, merged/folded weights, graph replay; context only"}}
