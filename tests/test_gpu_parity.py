@@ -93,6 +93,26 @@ def test_token_sweep_sampled_rows(op, weights, M):
     check_all(out, run_oracle(inp, rows), rows)
 
 
+def test_beyond_4gib(op, weights):
+    """R and R2 past 4 GiB (215000 tokens x 20480 bytes): every address the
+    kernels form is 64-bit. Rows on both sides of the 4 GiB mark and the
+    ragged last tile match the oracle, and the combine entry point gives the
+    same R2 bit for bit."""
+    M = 215000
+    row_bytes = SHAPE.k * 2
+    assert M * row_bytes > 1 << 32
+    _say(f"[parity] beyond 4 GiB M={M}")
+    inp = synth.make_inputs(M, SHAPE, seed=7, device="cuda", weights=weights)
+    out = gpu_forward(op, inp)
+    edge = (1 << 32) // row_bytes  # the row that straddles the 4 GiB mark
+    rows = np.array(sorted(set(sample_rows(M, n=24).tolist()) | {edge - 1, edge, edge + 1, M - 1}))
+    check_all(out, run_oracle(inp, rows), rows)
+    R2 = op.combine(inp["R"], inp["y"], inp["inj"])
+    torch.cuda.synchronize()
+    idx = torch.as_tensor(rows, device="cuda")
+    assert torch.equal(R2[idx], out["R2"][idx])
+
+
 def test_decode_m1(op, weights):
     inp = synth.make_inputs(1, SHAPE, seed=0, device="cuda", weights=weights)
     check_all(gpu_forward(op, inp), run_oracle(inp))
