@@ -475,6 +475,7 @@ struct CombineArgs {
   int64_t ld_inj, M;
   int HS, HC;
   uint16_t* R2;
+  int nt = 0;  // set by launch_combine: R read and R2 written with the non-temporal policy
 };
 // Enqueues the combine-only kernel (R2 = R + y*iw) on `stream`; returns the
 // hipError_t of the launch.

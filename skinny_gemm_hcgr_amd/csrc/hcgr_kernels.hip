@@ -62,6 +62,22 @@ __device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void bst16(rsrc_t r, uint32_t off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, 0);
 }
+// Non-temporal (streaming) cache policy, for data a kernel reads or writes
+// once: R in and R2 out of the combine pass, when R2 is too large for the
+// caches to keep it until the up kernel reads it back. Measured on MI355X
+// (HC = 4, HS = 2560): the large-token down kernel 17% faster at M = 8192 and
+// 65536 with R read and R2 written this way (the whole call 7-9% faster from
+// M = 8192), the combine-only kernel 11-20% faster at M = 8192; but the
+// staged up kernel 10-20% slower at M = 256 .. 2048, where R2 stays in the
+// 256 MB Infinity Cache for it. y (read once per stream) keeps the default.
+constexpr int kNonTemporal = 2;
+constexpr double kStreamBytes = 256.0 * 1024 * 1024;  // Infinity Cache
+__device__ __forceinline__ uint4 bld16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal));
+}
+__device__ __forceinline__ void bst16_nt(rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, kNonTemporal);
+}
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 bld8(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
@@ -830,6 +846,7 @@ struct Tile1Args {
   float* SSp;  // [HC*nseg][Mq] per-segment sums of squares (nseg > 1)
   int tiles;   // token tiles
   int xgroup;  // 1: the workgroups of one token tile share an XCD (grid rounded up to 8 tiles)
+  int nt;      // 1: R read and R2 written with the non-temporal policy
 };
 
 template <int N>
@@ -952,7 +969,8 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
     for (int j = 0; j < TPT; ++j) {
       const uint32_t oR = valid ? offR + (uint32_t)(j * 64) * rowb + (uint32_t)(s * HS) * 2u + col : kOut;
       const uint32_t oY = valid ? offY + (uint32_t)(j * 64 * HS) * 2u + col : kOut;
-      rv[k][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rR, (int)oR, 0, 0));
+      rv[k][j] = __builtin_bit_cast(u32x4_t, a.nt ? __builtin_amdgcn_raw_buffer_load_b128(rR, (int)oR, 0, kNonTemporal)
+                                                 : __builtin_amdgcn_raw_buffer_load_b128(rR, (int)oR, 0, 0));
       yv[k][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rY, (int)oY, 0, 0));
     }
     const uint32_t oW = valid ? (wnc ? (uint32_t)(s * HS) * 2u : 0u) + col + swz * 16u : kOut;
@@ -982,8 +1000,9 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
         ou[e] = pack_bf2(r0 * (1.0f + bf_lo(ww)), r1 * (1.0f + bf_hi(ww)));
       }
       ss[j] = acc;
-      bst16(rR2, valid ? offR + (uint32_t)(j * 64) * rowb + (uint32_t)(s * HS + c0) * 2u : kOut,
-            make_uint4(o2[0], o2[1], o2[2], o2[3]));
+      const uint32_t o2off = valid ? offR + (uint32_t)(j * 64) * rowb + (uint32_t)(s * HS + c0) * 2u : kOut;
+      if (a.nt) bst16_nt(rR2, o2off, make_uint4(o2[0], o2[1], o2[2], o2[3]));
+      else bst16(rR2, o2off, make_uint4(o2[0], o2[1], o2[2], o2[3]));
       *reinterpret_cast<u32x4_t*>(abuf + la_off + j * 64 * 128) = u32x4_t{ou[0], ou[1], ou[2], ou[3]};
     }
   };
@@ -1965,7 +1984,7 @@ __global__ __launch_bounds__(kCombineThreads) void hcgr_combine_k(CombineArgs a)
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {  // chunks past the row read as zero
       const uint32_t off = (uint32_t)(c0 + tid + j * kCombineThreads) * 16u;
-      rv[j] = bld16(rR, off);
+      rv[j] = a.nt ? bld16_nt(rR, off) : bld16(rR, off);
       yv[j] = bld16(rY, off);
     }
     if (c0 == 0) {
@@ -1993,12 +2012,17 @@ __global__ __launch_bounds__(kCombineThreads) void hcgr_combine_k(CombineArgs a)
         const float r1 = fmaf(bf_hi(yw[e]), il, fmaf(bf_hi(yw[e]), ih, bf_hi(rw[e])));
         o[e] = pack_bf2(r0, r1);
       }
-      bst16(rO, (uint32_t)c * 16u, make_uint4(o[0], o[1], o[2], o[3]));
+      if (a.nt) bst16_nt(rO, (uint32_t)c * 16u, make_uint4(o[0], o[1], o[2], o[3]));
+      else bst16(rO, (uint32_t)c * 16u, make_uint4(o[0], o[1], o[2], o[3]));
     }
   }
 }
 
-int launch_combine(const CombineArgs& a, void* stream) {
+int launch_combine(const CombineArgs& args, void* stream) {
+  CombineArgs a = args;
+  // streaming policy once R2 outgrows the L2s (8 x 4 MB): 73% -> 81% of HBM
+  // peak at M = 8192 (HC = 4, HS = 2560) on MI355X
+  a.nt = (double)a.M * a.HC * a.HS * 2.0 > 32.0 * 1024 * 1024 ? 1 : 0;
   const int64_t groups = cdiv(a.M, 8) * 8 * a.HC;  // token octets x streams x 8
   const int passes = (int)cdiv(a.HS / 8, kCombineThreads);  // chunks per thread in one pass
   const dim3 g((unsigned)groups), blk(kCombineThreads);
@@ -2140,6 +2164,10 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     a.nseg = p.nseg; a.SSp = reinterpret_cast<float*>(ws + p.off_ss);
     a.tiles = (int)cdiv(f.M, (int64_t)p.tm);
     a.xgroup = p.xgroup;
+    // streaming policy for R and R2 when the up kernel cannot find R2 in the
+    // caches anyway: the sweep (large M), or R2 beyond the Infinity Cache;
+    // not for the mix entry point, whose up kernel reads R itself again
+    a.nt = f.R2 && (p.kt == KT_SWEEP || (double)f.M * K * 2.0 > kStreamBytes) ? 1 : 0;
     const int64_t tiles_g = p.xgroup ? cdiv((int64_t)a.tiles, 8) * 8 : a.tiles;
     const dim3 g1((unsigned)(tiles_g * p.nsplit * (s.hc / p.spw) * p.nseg));
     if (p.spw == 4) klaunch(hcgr_k1_tile<4, 64, 4>, g1, dim3(512), 0, st, tm.stage(0), a);
