@@ -1237,7 +1237,11 @@ struct SumArgs {
   float eps, inv_hs;
 };
 
-template <int HC>
+// ONE: a single segment per stream (the large-M plans), straight-line with
+// both loads of a lane issued together (measured on MI355X at M = 65536 and
+// 8192: 8-13% faster than the segment loop); the segment loop keeps its own
+// register budget (eight waves per SIMD).
+template <int HC, bool ONE>
 __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
   // lane = (token m, chunk c of 8 rows, stream s); s is the fastest index, so
   // the HC streams of a (token, chunk) sit in adjacent lanes (HC = 1, 2, 4, 8)
@@ -1252,7 +1256,7 @@ __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
   const bool live = mc / nch < a.M;
   const int n = c * 8;
   float rr = 1.0f;  // partials arrive rrms-scaled unless the streams were split into segments
-  if (a.nseg > 1) {  // (N) rrms of stream s from its segments' sums of squares
+  if (!ONE && a.nseg > 1) {  // (N) rrms of stream s from its segments' sums of squares
     float sq = 0.0f;
     for (int g = 0; g < a.nseg; ++g) sq += a.SSp[(int64_t)(s * a.nseg + g) * a.Mq + m];
     rr = 1.0f / sqrtf(sq * a.inv_hs + a.eps);
@@ -1263,7 +1267,15 @@ __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
   for (int e = 0; e < 8; ++e) u[e] = 0.0f;
   const float* p = a.Q + ((int64_t)s * a.nseg * a.Mq + m) * a.NP + n;
   const int64_t gstride = a.Mq * a.NP;
-  int g = 0;
+  if constexpr (ONE) {
+    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(p), hi = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u[e] = lo[e];
+      u[e + 4] = hi[e];
+    }
+  }
+  int g = ONE ? a.nseg : 0;
   for (; g + 4 <= a.nseg; g += 4) {  // four segments' loads in flight at once
     f32x4_t lo[4], hi[4];
 #pragma unroll
@@ -2200,10 +2212,22 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     const int64_t threads = f.M * (s.r / 8 + 1) * s.hc;
     const dim3 gs((unsigned)cdiv(threads, 256)), bs(256);
     switch (s.hc) {
-      case 1: klaunch(hcgr_k1_sum<1>, gs, bs, 0, st, tm.stage(1), sa); break;
-      case 2: klaunch(hcgr_k1_sum<2>, gs, bs, 0, st, tm.stage(1), sa); break;
-      case 8: klaunch(hcgr_k1_sum<8>, gs, bs, 0, st, tm.stage(1), sa); break;
-      default: klaunch(hcgr_k1_sum<4>, gs, bs, 0, st, tm.stage(1), sa); break;
+      case 1:
+        if (sa.nseg == 1) klaunch(hcgr_k1_sum<1, true>, gs, bs, 0, st, tm.stage(1), sa);
+        else klaunch(hcgr_k1_sum<1, false>, gs, bs, 0, st, tm.stage(1), sa);
+        break;
+      case 2:
+        if (sa.nseg == 1) klaunch(hcgr_k1_sum<2, true>, gs, bs, 0, st, tm.stage(1), sa);
+        else klaunch(hcgr_k1_sum<2, false>, gs, bs, 0, st, tm.stage(1), sa);
+        break;
+      case 8:
+        if (sa.nseg == 1) klaunch(hcgr_k1_sum<8, true>, gs, bs, 0, st, tm.stage(1), sa);
+        else klaunch(hcgr_k1_sum<8, false>, gs, bs, 0, st, tm.stage(1), sa);
+        break;
+      default:
+        if (sa.nseg == 1) klaunch(hcgr_k1_sum<4, true>, gs, bs, 0, st, tm.stage(1), sa);
+        else klaunch(hcgr_k1_sum<4, false>, gs, bs, 0, st, tm.stage(1), sa);
+        break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   } else if ((e = tm.skip(1, st)) != hipSuccess) {
