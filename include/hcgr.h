@@ -233,7 +233,7 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
 #define HCGR_PLAN_HEURISTIC (-1) /* the library's own choice                          */
 #define HCGR_PLAN_SPLIT 0        /* decode plan: K-chunked down kernel, reduction, up */
 #define HCGR_PLAN_TILE 3         /* tile plan: 64-token down tiles, (stream sum), up  */
-#define HCGR_SPLIT_VARIANTS 10   /* down-kernel variants of the decode plan           */
+#define HCGR_SPLIT_VARIANTS 11   /* down-kernel variants of the decode plan           */
 
 typedef struct hcgr_plan_choice {
     int64_t tokens;         /* table key (token count >= 1); a candidate carries the M it was made for */

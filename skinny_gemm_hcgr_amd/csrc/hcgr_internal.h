@@ -56,13 +56,13 @@ enum PlanKind { PLAN_SPLIT = 0, PLAN_STREAM = 1, PLAN_FULL = 2, PLAN_TILE = 3 };
 enum KDVariant {
   KD_T16_R7_K1_C128 = 0, KD_T16_R1_K4_C512, KD_T16_R3_K1_C256, KD_T16_R3_K2_C512,
   KD_T32_R7_K1_C128, KD_T32_R1_K4_C512, KD_T32_R3_K1_C256, KD_T32_R3_K2_C512,
-  KD_T64_R7_K1_C128, KD_T64_R3_K1_C256, KD_NVAR
+  KD_T64_R7_K1_C128, KD_T64_R3_K1_C256, KD_T128_R7_K1_C128, KD_NVAR
 };
 struct KDShape { int tm, rb, kw, kc; };
 inline KDShape kd_shape(int v) {
   static const KDShape t[KD_NVAR] = {{16, 7, 1, 128}, {16, 1, 4, 512}, {16, 3, 1, 256}, {16, 3, 2, 512},
                                      {32, 7, 1, 128}, {32, 1, 4, 512}, {32, 3, 1, 256}, {32, 3, 2, 512},
-                                     {64, 7, 1, 128}, {64, 3, 1, 256}};
+                                     {64, 7, 1, 128}, {64, 3, 1, 256}, {128, 7, 1, 128}};
   return t[v];
 }
 // SPLIT-plan up kernel variants: token tile; kDecUpWaves waves of 4
@@ -74,6 +74,14 @@ inline K2Shape k2_shape(int v) {
   static const K2Shape t[K2_NVAR] = {{16, kDecUpWaves, 1}, {32, kDecUpWaves, 1}, {64, kDecUpWaves, 1}};
   return t[v];
 }
+// Dynamic LDS of the SPLIT-plan up kernel for a token tile of tm and rank r:
+// the workgroup's Wu rows and the h tile, the tile's R2 rows of its
+// channels, rrms and Wnorm; it must fit the 160 KB of one CU.
+inline size_t k2_dec_lds(int tm, int r) {
+  return (size_t)(kDecUpWaves * 16 + tm) * (size_t)r * 2u + (size_t)tm * 4 * (kDecUpWaves * 4) * 2u +
+         (size_t)(tm > 64 ? tm : 64) * 16 + 1024;
+}
+constexpr size_t kLdsPerCu = 160 * 1024;
 // The reduction kernel gives each of a wave's 4 lane groups up to kRedMaxCpl
 // chunks per stream (instantiated: 1, 2, 3, 5, 8).
 constexpr int kRedMaxCpl = 8;
@@ -159,12 +167,17 @@ constexpr int64_t kTileMinM = 65;
 // not split into chunks of the variant (the caller then takes another plan).
 inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
   const KDShape d = kd_shape(kd);
-  if (s.hs % d.kc != 0 || s.hs / d.kc > 4 * kRedMaxCpl) return false;
+  // the up kernel's token tile: the down kernel's, except 32 under 128-token
+  // down tiles (measured on MI355X at M = 128: the 128-token up tile, one
+  // workgroup per CU for its LDS, is 1 us slower than four 32-token ones,
+  // while the 128-token down tile is 1.2 us faster than four 32-token ones)
+  const int k2 = d.tm == 16 ? K2_T16 : d.tm == 64 ? K2_T64S : K2_T32;
+  if (s.hs % d.kc != 0 || s.hs / d.kc > 4 * kRedMaxCpl || k2_dec_lds(k2_shape(k2).tm, s.r) > kLdsPerCu) return false;
   Plan p;
   p.M = M;
   p.kind = PLAN_SPLIT;
   p.k1 = kd;
-  p.k2 = d.tm == 16 ? K2_T16 : d.tm == 32 ? K2_T32 : K2_T64S;
+  p.k2 = k2;
   p.tm = d.tm;
   p.kc = d.kc;
   p.kcps = s.hs / d.kc;

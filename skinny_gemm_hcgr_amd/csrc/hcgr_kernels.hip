@@ -2070,6 +2070,7 @@ static void launch_kd_variant(int v, const DownArgs& d, dim3 grid, hipStream_t s
     case KD_T32_R3_K1_C256: launch_kd<32, 3, 1, 256>(d, grid, st, ev); break;
     case KD_T32_R3_K2_C512: launch_kd<32, 3, 2, 512>(d, grid, st, ev); break;
     case KD_T64_R7_K1_C128: launch_kd<64, 7, 1, 128>(d, grid, st, ev); break;
+    case KD_T128_R7_K1_C128: launch_kd<128, 7, 1, 128>(d, grid, st, ev); break;
     default: launch_kd<64, 3, 1, 256>(d, grid, st, ev); break;
   }
 }
@@ -2087,7 +2088,7 @@ static void launch_kf(const FullArgs& f, dim3 grid, hipStream_t st, const hipEve
   klaunch(hcgr_k1_full<TM, NW, BPW, KS>, grid, dim3(NW * 64), 0, st, ev, f);
 }
 int configure_kernels() {
-  const int lim = 160 * 1024;  // (64 + 64) rows of r <= 512 values, plus the epilogue operands
+  const int lim = (int)kLdsPerCu;  // make_split keeps k2_dec_lds within it
   hipError_t e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<16, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<32, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
@@ -2143,10 +2144,11 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   u.h = H; u.Mpad = p.mpad; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = K;
   u.wu = f.wu; u.R2 = f.res; u.rrms = f.rrms; u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0;
   u.x = f.x;
-  const size_t lds = (size_t)(kDecUpWaves * 16 + p.tm) * (size_t)s.r * sizeof(uint16_t)  // Wu rows, h tile
-                    + (size_t)p.tm * 4 * (kDecUpWaves * 4) * sizeof(uint16_t)             // R2 rows
-                    + (size_t)(p.tm > 64 ? p.tm : 64) * 16 + 1024;                          // rrms, Wnorm
-  const dim3 g2((unsigned)(s.hs / p.cb), (unsigned)(p.mpad / p.tm));
+  // the up kernel's token tiles: every one starts below M (with a smaller
+  // tile than the down kernel's, p.mpad / tm2 tiles would not)
+  const int tm2 = k2_shape(p.k2).tm;
+  const size_t lds = k2_dec_lds(tm2, s.r);
+  const dim3 g2((unsigned)(s.hs / p.cb), (unsigned)cdiv(f.M, (int64_t)tm2));
   const dim3 b2(kDecUpWaves * 64);
   switch (p.k2) {
     case K2_T16: klaunch(hcgr_k2_dec<16, kDecUpWaves>, g2, b2, lds, st, tm.stage(2), u); break;

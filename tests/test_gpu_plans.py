@@ -197,3 +197,21 @@ def test_tile128_shapes(H, hc, hs, r, M, seg, up, extra):
                              inp["wnorm"].cpu(), wd.cpu(), None if merged else wi.cpu(), inp["wu"].cpu())
         check_rows(out, ref, rows)
     op.close()
+
+
+@pytest.mark.parametrize("M", [97, 129, 200, 256])
+def test_split128_up_tiles(H, weights, M):
+    """The decode plan with 128-token down tiles and 32-token up tiles: the up
+    grid covers M, not the down kernel's padded count, so a last down tile
+    that is mostly padding leaves no up tile wholly past M."""
+    table = [{"tokens": M, "kind": H.HCGR_PLAN_SPLIT, "down_variant": 10, "streams_per_wg": 0, "segments": 0,
+              "up_variant": 0, "ranges": 0}]
+    op = H.HCGR(H.Config(), 0, plan_table=table)
+    desc = op.describe(M)
+    _say(f"[plans] split128 M={M}: {desc}")
+    assert "k1_dec tm=128" in desc and "k2_dec tm=32" in desc and f"grid=160x{(M + 31) // 32}" in desc
+    inp = synth.make_inputs(M, SHAPE, seed=700 + M, device="cuda", weights=weights)
+    out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"])
+    torch.cuda.synchronize()
+    check_rows(out, run_oracle(inp), None)
+    op.close()
