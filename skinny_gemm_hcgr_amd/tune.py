@@ -31,7 +31,7 @@ import sys
 import time
 
 MARGIN = 1.04  # a candidate must beat the heuristic by 4%: run-to-run spread on the box is 2-4%
-DEFAULT_TOKENS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536]
+DEFAULT_TOKENS = [1, 2, 4, 8, 16, 32, 64, 96, 128, 192, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536]
 CACHE_BYTES = 256 << 20
 
 
