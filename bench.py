@@ -92,7 +92,7 @@ def stage_names(plan: str):
     a plan has no kernel between two marks)."""
     if "plan=split" in plan:
         return ("hcgr_k1_dec", "hcgr_k1_reduce", "hcgr_k2_dec")
-    up = "hcgr_k2_sweep" if "k2_sweep" in plan else "hcgr_k2_stage"
+    up = "hcgr_k2_sweep" if "k2_sweep" in plan else "hcgr_k2_gen" if "k2_gen" in plan else "hcgr_k2_stage"
     if "plan=tile" in plan:
         return ("hcgr_k1_tile", "hcgr_k1_sum" if "streams/wg=1" in plan else None, up)
     if "plan=stream" in plan:

@@ -1865,8 +1865,16 @@ template <int HC>
 __global__ __launch_bounds__(256) void hcgr_k2_gen(GenUpArgs a) {
   constexpr int TM = kGenTm, CG = kGenCg, NTB = 2;
   constexpr int HB = TM * 128, WB = HC * CG * 128;  // LDS bytes of one stage of h and of Wu
-  __shared__ __attribute__((aligned(1024))) uint8_t hb[HB];
-  __shared__ __attribute__((aligned(1024))) uint8_t wb[WB];
+  constexpr int NL = TM / 32 + HC;                  // loads per thread per stage
+  // vmcnt(NL): the newest stage's loads stay in flight (expcnt and lgkmcnt left open)
+  constexpr int kWaitNewest = (NL & 15) | ((NL >> 4) << 14) | (7 << 4) | (15 << 8);
+  // two stage buffers, separate arrays picked at compile time (stage parity
+  // P): stage s + 1 loads while stage s contracts, and the compiler can tell
+  // that the reads of one buffer do not wait for the loads into the other
+  __shared__ __attribute__((aligned(1024))) uint8_t hb0[HB];
+  __shared__ __attribute__((aligned(1024))) uint8_t hb1[HB];
+  __shared__ __attribute__((aligned(1024))) uint8_t wb0[WB];
+  __shared__ __attribute__((aligned(1024))) uint8_t wb1[WB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1886,8 +1894,10 @@ __global__ __launch_bounds__(256) void hcgr_k2_gen(GenUpArgs a) {
 
   // one wave instruction moves 8 rows x 128 bytes: lane -> row lane >> 3, chunk swz
   const uint32_t swz = (uint32_t)((lane & 7) ^ (lane >> 3));
-  auto issue = [&](int stg) {
+  auto issue = [&](auto P, int stg) {
     const uint32_t kb = (uint32_t)stg * 128u;
+    uint8_t* hb = decltype(P)::value ? hb1 : hb0;
+    uint8_t* wb = decltype(P)::value ? wb1 : wb0;
 #pragma unroll
     for (int i = 0; i < TM / 32; ++i) {  // h: TM / 8 groups of 8 rows over 4 waves
       const int g = wave + 4 * i;
@@ -1912,25 +1922,67 @@ __global__ __launch_bounds__(256) void hcgr_k2_gen(GenUpArgs a) {
     for (int tb = 0; tb < NTB; ++tb) acc[s][tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int fr = lane & 15;  // fragment row inside a 16-row block (row & 7 == lane & 7)
-  for (int stg = 0; stg < nstage; ++stg) {
-    issue(stg);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // every wave's part of the stage has landed
+  auto step = [&](auto P, int stg) {
+    constexpr int par = decltype(P)::value;
+    // every thread issues NL loads per stage, so with the next stage issued
+    // the wait leaves exactly its loads in flight
+    if (stg + 1 < nstage) {
+      issue(ic<par ^ 1>{}, stg + 1);
+      __builtin_amdgcn_s_waitcnt(kWaitNewest);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    }
+    lds_sync();  // every wave's part of stage stg has landed (a barrier that leaves the next stage in flight)
+    const uint8_t* hb = par ? hb1 : hb0;
+    const uint8_t* wb = par ? wb1 : wb0;
     const int nks = 64 * stg + 64 <= a.r ? 2 : 1;
     for (int ks = 0; ks < nks; ++ks) {
       const int slot = ((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
-      uint4 bq[NTB];
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb)
-        bq[tb] = *reinterpret_cast<const uint4*>(hb + (th * 32 + tb * 16 + fr) * 128 + slot);
-#pragma unroll
-      for (int s = 0; s < HC; ++s) {
-        const uint4 af = *reinterpret_cast<const uint4*>(wb + (s * CG + ch * 16 + fr) * 128 + slot);
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) acc[s][tb] = mfma16(af, bq[tb], acc[s][tb]);
+      // the fragments of this k step, read in one asm block with its own
+      // wait: the compiler would otherwise wait for every load in flight
+      // (the next stage's included) before reading LDS filled by such loads
+      const uint32_t ha = (uint32_t)(uintptr_t)(lds_u8_t*)hb + (uint32_t)((th * 32 + fr) * 128 + slot);
+      const uint32_t wa = (uint32_t)(uintptr_t)(lds_u8_t*)wb + (uint32_t)((ch * 16 + fr) * 128 + slot);
+      u32x4_t bq[NTB], af[HC];
+      static_assert(NTB == 2 && CG * 128 == 4096, "offsets below: column block 1 16 rows on, stream s CG rows on");
+      if constexpr (HC == 1) {
+        asm volatile(
+            "ds_read_b128 %0, %3\n\tds_read_b128 %1, %3 offset:2048\n\tds_read_b128 %2, %4\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(bq[0]), "=&v"(bq[1]), "=&v"(af[0])
+            : "v"(ha), "v"(wa)
+            : "memory");
+      } else if constexpr (HC == 2) {
+        asm volatile(
+            "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:2048\n\tds_read_b128 %2, %5\n\t"
+            "ds_read_b128 %3, %5 offset:4096\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(bq[0]), "=&v"(bq[1]), "=&v"(af[0]), "=&v"(af[1])
+            : "v"(ha), "v"(wa)
+            : "memory");
+      } else {
+        static_assert(HC == 8, "stream counts 1, 2 and 8 take this kernel");
+        asm volatile(
+            "ds_read_b128 %0, %10\n\tds_read_b128 %1, %10 offset:2048\n\t"
+            "ds_read_b128 %2, %11\n\tds_read_b128 %3, %11 offset:4096\n\t"
+            "ds_read_b128 %4, %11 offset:8192\n\tds_read_b128 %5, %11 offset:12288\n\t"
+            "ds_read_b128 %6, %11 offset:16384\n\tds_read_b128 %7, %11 offset:20480\n\t"
+            "ds_read_b128 %8, %11 offset:24576\n\tds_read_b128 %9, %11 offset:28672\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(bq[0]), "=&v"(bq[1]), "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]),
+              "=&v"(af[5]), "=&v"(af[6]), "=&v"(af[7])
+            : "v"(ha), "v"(wa)
+            : "memory");
       }
+#pragma unroll
+      for (int s = 0; s < HC; ++s)
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+          acc[s][tb] = mfma16(__builtin_bit_cast(uint4, af[s]), __builtin_bit_cast(uint4, bq[tb]), acc[s][tb]);
     }
-    __syncthreads();  // every wave is done with the stage before it is refilled
+    lds_sync();  // every wave is done with buffer par before stage stg + 2 refills it
+  };
+  issue(ic<0>{}, 0);
+  for (int stg = 0; stg < nstage; stg += 2) {
+    step(ic<0>{}, stg);
+    if (stg + 1 < nstage) step(ic<1>{}, stg + 1);
   }
 
   // (G2) sigmoid and (MIX): lane holds channels cl..cl+3 of token t for every stream
