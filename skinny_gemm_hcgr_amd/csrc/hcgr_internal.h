@@ -104,12 +104,15 @@ inline KFShape kf_shape(int v) {
 // workgroup sweeps a range of 32-channel groups).
 // KT_GEN: hcgr_k2_gen, for stream counts other than 4 (64 tokens x 32
 // channels x HC streams per workgroup).
-enum KTVariant { KT_S128 = 0, KT_SWEEP = 1, KT_GEN = 2, KT_NVAR };
+// KT_GEN128: hcgr_k2_gen over 128-token tiles (HC = 2 or 8: each Wu row read
+// once per 128 tokens instead of 64).
+enum KTVariant { KT_S128 = 0, KT_SWEEP = 1, KT_GEN = 2, KT_GEN128 = 3, KT_NVAR };
 struct KTShape { int tm, cb; };
 inline KTShape kt_shape(int v) {
-  static const KTShape t[KT_NVAR] = {{128, 32}, {128, 32}, {64, 32}};
+  static const KTShape t[KT_NVAR] = {{128, 32}, {128, 32}, {64, 32}, {128, 32}};
   return t[v];
 }
+inline bool is_gen(int kt) { return kt == KT_GEN || kt == KT_GEN128; }
 // hcgr_k2_sweep serves 96 <= r <= 320 (2 to 5 k stages of 64) from
 // kSweepMinM tokens, with enough channel ranges per token tile to give
 // every CU a workgroup.
@@ -207,10 +210,10 @@ inline bool make_tile(const Shape& s, int64_t M, int spw, int nseg, int kt, int 
   if (tm != 64 && !(tm == 128 && spw == 1)) return false;
   if (spw != 1 && !(spw == 4 && !generic)) return false;
   if (nseg < 1 || (s.hs / 128) % nseg != 0 || (spw == 4 && nseg != 1)) return false;
-  if (generic != (kt == KT_GEN)) return false;
+  if (generic != is_gen(kt) || (kt == KT_GEN128 && s.hc != 2 && s.hc != 8)) return false;
   if (kt == KT_SWEEP) {
     if (!sweep_fits(s.r) || nranges < 1 || nranges > s.hs / kt_shape(KT_SWEEP).cb) return false;
-  } else if (kt != KT_S128 && kt != KT_GEN) {
+  } else if (kt != KT_S128 && !is_gen(kt)) {
     return false;
   } else if (nranges != 1) {
     return false;
@@ -265,6 +268,10 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   const int tsplit = (int)cdiv(s.nblk(), kTileMaxBlk);  // row splits of the tile down kernel
   if (M >= kTileMinM || generic) {
     int kt = generic ? KT_GEN : KT_S128, nranges = 1;
+    // two streams from 1024 tokens: the 128-token generic up tile (measured on
+    // MI355X at HS = 2560, r = 320: 4-6% faster up kernel at M = 1024..32768;
+    // with eight streams it was 7-18% slower, one workgroup per CU)
+    if (generic && s.hc == 2 && M >= 1024) kt = KT_GEN128;
     if (M >= kSweepMinM && sweep_fits(s.r) && !generic) {
       kt = KT_SWEEP;
       const int64_t t2 = cdiv(M, kt_shape(KT_SWEEP).tm);
@@ -395,7 +402,7 @@ inline int plan_choices(const Shape& s, int64_t M, Choice* out, int cap) {
     c.kd = kd;
     add(c);
   }
-  const int ups[3] = {KT_S128, KT_SWEEP, KT_GEN};
+  const int ups[4] = {KT_S128, KT_SWEEP, KT_GEN, KT_GEN128};
   const int pairs = s.hs / 128;
   for (int big = 0; big < 2; ++big)
     for (int spw : {1, 4})

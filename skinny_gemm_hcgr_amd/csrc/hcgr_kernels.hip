@@ -1836,15 +1836,17 @@ __global__ __launch_bounds__(512) void hcgr_k2_sweep(SweepArgs a) {
 
 // ---------------------------------------------------------------------------
 // hcgr_k2_gen (stream counts other than 4): (G2) gate = h . Wu^T, G =
-// sigmoid(gate), (MIX) x[c] = 1/HC sum_s G[s,c] xn[s,c], for a tile of 64
-// tokens x 32 channels x HC streams, 4 waves. Wave (ch, th) owns channels
+// sigmoid(gate), (MIX) x[c] = 1/HC sum_s G[s,c] xn[s,c], for a tile of TM =
+// 64 or 128 tokens x 32 channels x HC streams, TM / 16 waves (the 128-token
+// tile reads each Wu row once per 128 tokens). Wave (ch, th) owns channels
 // 16ch.. of the tile and tokens 32th..: for each stream s one 16-row MFMA
 // block whose row i is Wu row s*HS + c0 + 16ch + i, so lane l ends with the
 // same four channels 4(l/16).. of token l%16 for every stream and the MIX sum
-// over streams is lane-local. h (64 rows) and the tile's Wu rows (32 HC rows)
-// pass through LDS in stages of 64 k by direct global->LDS loads, 16-byte
-// chunk c of LDS row t in slot c ^ (t & 7); a half last stage (r % 64 == 32)
-// contracts its first 32 k only.
+// over streams is lane-local. h (TM rows) and the tile's Wu rows (32 HC rows)
+// pass through two LDS stage buffers of 64 k by direct global->LDS loads
+// (stage s + 1 loads while stage s contracts), 16-byte chunk c of LDS row t
+// in slot c ^ (t & 7); a half last stage (r % 64 == 32) contracts its first
+// 32 k only.
 // ---------------------------------------------------------------------------
 struct GenUpArgs {
   const uint16_t* h;  // [>= M, r]
@@ -1859,13 +1861,17 @@ struct GenUpArgs {
   int ngroups;  // HS / 32
 };
 
-constexpr int kGenTm = 64, kGenCg = 32;
+constexpr int kGenCg = 32;
 
-template <int HC>
-__global__ __launch_bounds__(256) void hcgr_k2_gen(GenUpArgs a) {
-  constexpr int TM = kGenTm, CG = kGenCg, NTB = 2;
+// TM: 64 tokens (4 waves) or 128 (8 waves, HC = 2 or 8); a wave always owns
+// 16 channels x 32 tokens of every stream.
+template <int HC, int TM>
+__global__ __launch_bounds__(TM * 4) void hcgr_k2_gen(GenUpArgs a) {
+  constexpr int CG = kGenCg, NTB = 2, NW = TM / 16;
+  static_assert((TM == 64 || (TM == 128 && HC % 2 == 0)) && (4 * HC) % NW == 0, "whole Wu loads per wave");
   constexpr int HB = TM * 128, WB = HC * CG * 128;  // LDS bytes of one stage of h and of Wu
-  constexpr int NL = TM / 32 + HC;                  // loads per thread per stage
+  constexpr int NH = TM / 8 / NW, NWU = 4 * HC / NW;  // h and Wu loads per wave per stage
+  constexpr int NL = NH + NWU;                        // loads per thread per stage
   // vmcnt(NL): the newest stage's loads stay in flight (expcnt and lgkmcnt left open)
   constexpr int kWaitNewest = (NL & 15) | ((NL >> 4) << 14) | (7 << 4) | (15 << 8);
   // two stage buffers, separate arrays picked at compile time (stage parity
@@ -1899,15 +1905,15 @@ __global__ __launch_bounds__(256) void hcgr_k2_gen(GenUpArgs a) {
     uint8_t* hb = decltype(P)::value ? hb1 : hb0;
     uint8_t* wb = decltype(P)::value ? wb1 : wb0;
 #pragma unroll
-    for (int i = 0; i < TM / 32; ++i) {  // h: TM / 8 groups of 8 rows over 4 waves
-      const int g = wave + 4 * i;
+    for (int i = 0; i < NH; ++i) {  // h: TM / 8 groups of 8 rows over NW waves
+      const int g = wave + NW * i;
       const uint32_t row = (uint32_t)(g * 8 + (lane >> 3));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rH, (lds_void_t*)(hb + g * 1024), 16, row * hrow + swz * 16u + kb, 0,
                                                0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < HC; ++i) {  // Wu: HC * CG / 8 groups of 8 rows over 4 waves
-      const int g = wave + 4 * i;
+    for (int i = 0; i < NWU; ++i) {  // Wu: HC * CG / 8 groups of 8 rows over NW waves
+      const int g = wave + NW * i;
       const int rl = g * 8 + (lane >> 3);  // LDS row: stream rl / CG, channel c0 + rl % CG
       const uint32_t grow = (uint32_t)((rl / CG) * a.HS + c0 + rl % CG);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rWu, (lds_void_t*)(wb + g * 1024), 16, grow * hrow + swz * 16u + kb, 0,
@@ -2289,15 +2295,22 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   }
 
   const KTShape ts = kt_shape(p.kt);
-  if (p.kt == KT_GEN) {
+  if (is_gen(p.kt)) {
     GenUpArgs ga;
     ga.h = H; ga.M = f.M; ga.r = s.r; ga.HS = s.hs; ga.K = K; ga.wu = f.wu; ga.R2 = f.res; ga.rrms = f.rrms;
     ga.wn = f.wnorm; ga.wn_len = s.wn_full ? K : s.hs; ga.x = f.x; ga.ngroups = s.hs / kGenCg;
-    const dim3 g2((unsigned)(cdiv(f.M, (int64_t)kGenTm) * ga.ngroups)), b2(256);
+    const dim3 g2((unsigned)(cdiv(f.M, (int64_t)ts.tm) * ga.ngroups)), b2((unsigned)(ts.tm * 4));
+    const bool big = p.kt == KT_GEN128;
     switch (s.hc) {
-      case 1: klaunch(hcgr_k2_gen<1>, g2, b2, 0, st, tm.stage(2), ga); break;
-      case 2: klaunch(hcgr_k2_gen<2>, g2, b2, 0, st, tm.stage(2), ga); break;
-      case 8: klaunch(hcgr_k2_gen<8>, g2, b2, 0, st, tm.stage(2), ga); break;
+      case 1: klaunch(hcgr_k2_gen<1, 64>, g2, b2, 0, st, tm.stage(2), ga); break;
+      case 2:
+        if (big) klaunch(hcgr_k2_gen<2, 128>, g2, b2, 0, st, tm.stage(2), ga);
+        else klaunch(hcgr_k2_gen<2, 64>, g2, b2, 0, st, tm.stage(2), ga);
+        break;
+      case 8:
+        if (big) klaunch(hcgr_k2_gen<8, 128>, g2, b2, 0, st, tm.stage(2), ga);
+        else klaunch(hcgr_k2_gen<8, 64>, g2, b2, 0, st, tm.stage(2), ga);
+        break;
       default: return (int)hipErrorInvalidValue;  // make_plan takes this kernel for HC = 1, 2, 8 only
     }
   } else if (p.kt == KT_SWEEP) {

@@ -159,6 +159,9 @@ def _tile128(M, seg, up, ranges=1):
     (4, 1024, 512, 700, 2, 0, ""),          # two row splits of the down rows
     (2, 1024, 320, 300, 8, 2, ""), (8, 512, 96, 257, 1, 2, ""), (1, 2560, 64, 90, 10, 2, ""),
     (4, 1280, 160, 500, 2, 1, "wnfull"), (4, 2560, 320, 384, 1, 0, "merged"), (4, 2560, 320, 200, 2, 0, "mix"),
+    # the stream-generic up kernel over 128-token tiles: partial last tiles, a half last k stage
+    (2, 1024, 320, 300, 8, 3, ""), (8, 512, 96, 257, 1, 3, ""), (2, 1280, 160, 500, 2, 3, "wnfull"),
+    (8, 1024, 320, 1000, 1, 3, "mix"),
 ])
 def test_tile128_shapes(H, hc, hs, r, M, seg, up, extra):
     """The 128-token down tile (two tokens per thread, a prefetch ring of
