@@ -155,8 +155,20 @@ struct Plan {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Largest M served by the SPLIT plan.
-constexpr int64_t kSplitMaxM = 128;
+// Largest M the heuristic serves with the SPLIT plan, for any shape.
+constexpr int64_t kSplitMaxM = 256;
+// The split plan's cost grows with M (chunk partials, weights re-read per
+// 32-token tile) while the tile plan's stays nearly flat up to a few hundred
+// tokens, so the crossover falls as the weights grow: the heuristic takes the
+// split plan while M times the down weight's elements (K x padded rows) stays
+// under 6.5e8, between 64 and kSplitMaxM tokens (measured on MI355X, HC = 4:
+// crossover near 190 tokens at HS, r = 2560, 320, near 145 at 4096, 256,
+// beyond 256 at 1536, 192; at 7168, 512 the tile plan was 35% faster
+// already at 144 tokens).
+inline int64_t split_max(int64_t k, int np) {
+  const int64_t m = (int64_t)(6.5e8 / ((double)k * (double)np));
+  return m < 64 ? 64 : m > kSplitMaxM ? kSplitMaxM : m;
+}
 // TILE plan: 64-token down kernel (hcgr_k1_tile) with at most 22 16-row
 // blocks per workgroup (4 row quarters of at most 6); taken from kTileMinM
 // tokens: one stream per workgroup (split into column segments while that
@@ -257,7 +269,7 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   // stream counts other than 4 (1, 2 or 8) take the tile plan at every M:
   // one stream per down workgroup, the stream sum, and hcgr_k2_gen
   const bool generic = s.hc != 4;
-  if (M <= kSplitMaxM && !generic) {
+  if (M <= split_max(s.k(), s.np()) && !generic) {
     // above 32 tokens: 32-token down tiles (they pad M to 32, not 64), with
     // 3-row blocks where those leave fewer padded 16-row blocks than 7-row
     // ones (measured on MI355X at M = 40..128 over HS, r = 1536, 192;
