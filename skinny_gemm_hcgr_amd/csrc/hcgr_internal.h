@@ -270,15 +270,18 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   // one stream per down workgroup, the stream sum, and hcgr_k2_gen
   const bool generic = s.hc != 4;
   if (M <= split_max(s.k(), s.np()) && !generic) {
-    // above 32 tokens: 32-token down tiles (they pad M to 32, not 64), with
-    // 3-row blocks where those leave fewer padded 16-row blocks than 7-row
-    // ones (measured on MI355X at M = 40..128 over HS, r = 1536, 192;
+    // above 16 tokens: 32-token down tiles (they pad M to 32, not 64); at
+    // every M, 3-row blocks where those leave fewer padded 16-row blocks than
+    // 7-row ones (measured on MI355X at M = 40..128 over HS, r = 1536, 192;
     // 2560, 320; 4096, 256 and 7168, 512: within 4% of the fastest split
     // variant except HS = 7168 from 112 tokens, 5%; 64-token tiles were up
-    // to 30% slower at M = 80..96)
+    // to 30% slower at M = 80..96. At M = 1..32 and HS, r = 4096, 256 the
+    // 3-row blocks were 13-17% faster than 7-row ones)
     const int nb = s.nblk();
     const bool rb3 = cdiv(nb, 3) * 3 - nb < cdiv(nb, 7) * 7 - nb;
-    const int kd = M <= 16 ? KD_T16_R7_K1_C128 : M <= 32 ? KD_T32_R7_K1_C128 : rb3 ? KD_T32_R3_K1_C256 : KD_T32_R7_K1_C128;
+    const int kd = M <= 16 ? (rb3 ? KD_T16_R3_K2_C512 : KD_T16_R7_K1_C128)
+                 : M <= 32 ? (rb3 ? KD_T32_R3_K2_C512 : KD_T32_R7_K1_C128)
+                 : rb3 ? KD_T32_R3_K1_C256 : KD_T32_R7_K1_C128;
     const int kd_wide = M <= 16 ? KD_T16_R3_K2_C512 : KD_T32_R3_K2_C512;
     if (make_split(s, M, kd, &p) || make_split(s, M, kd_wide, &p)) return p;
   }

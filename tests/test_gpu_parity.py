@@ -260,6 +260,32 @@ def test_shape_grid(H, hs, r, M):
     o.close()
 
 
+@pytest.mark.parametrize("hs,r,M,kind", [(4096, 256, 1, "split"), (4096, 256, 32, "split"), (4096, 256, 100, "split"),
+                                          (4096, 256, 145, "split"), (4096, 256, 146, "tile"), (1536, 192, 256, "split"),
+                                          (7168, 512, 64, "split"), (7168, 512, 80, "tile")])
+def test_split_limit_shapes(H, hs, r, M, kind):
+    """The heuristic's shape-dependent plan choice: 3-row down blocks where
+    they pad fewer 16-row blocks (r = 256, 512), and the split plan's token
+    limit on both sides of it (145 tokens at HS = 4096, r = 256; 256 at
+    HS = 1536; 64 at HS = 7168). Oracle on sampled rows."""
+    shape = synth.Shape(hs=hs, r=r)
+    o = H.HCGR(H.Config(hs=hs, r=r), 0)
+    plan = H.hcgr_describe_plan(o.cfg, M)
+    _say(f"[parity] split limit hs={hs} r={r} M={M}: {plan}")
+    assert f"plan={kind}" in plan
+    if kind == "split" and r in (256, 512):
+        assert "row_blocks=3" in plan
+    inp = synth.make_inputs(M, shape, seed=hs + r + M, device="cuda")
+    out = gpu_forward(o, inp)
+    rows = sample_rows(M, 24)
+    cfg = oracle.OracleConfig(hs=hs, r=r)
+    idx = torch.as_tensor(rows, device="cuda")
+    ref = oracle.forward(cfg, inp["R"][idx].cpu(), inp["y"][idx].cpu(), inp["inj"][idx].cpu(), inp["wnorm"].cpu(),
+                         inp["wd"].cpu(), inp["wi"].cpu(), inp["wu"].cpu())
+    check_all(out, ref, rows)
+    o.close()
+
+
 def test_full_width_wnorm_large(H):
     """Wnorm indexed by k (length HC*HS) on the large-M path."""
     o = H.HCGR(H.Config(wnorm_len=SHAPE.k), 0)
