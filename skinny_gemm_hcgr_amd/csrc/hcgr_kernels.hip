@@ -1241,16 +1241,24 @@ struct SumArgs {
 // both loads of a lane issued together (measured on MI355X at M = 65536 and
 // 8192: 8-13% faster than the segment loop); the segment loop keeps its own
 // register budget (eight waves per SIMD).
-template <int HC, bool ONE>
+// SG: lanes sharing one (token, chunk, stream), lane j summing segments
+// j, j + SG, ..., for grids smaller than the CU count, where a lane's
+// dependent rounds of loads set the time (HC = 2, M = 32, HS = 2560,
+// r = 320, 20 segments: 11 workgroups of 256 lanes become 41).
+template <int HC, bool ONE, int SG>
 __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
-  // lane = (token m, chunk c of 8 rows, stream s); s is the fastest index, so
-  // the HC streams of a (token, chunk) sit in adjacent lanes (HC = 1, 2, 4, 8)
+  // lane = (token m, chunk c of 8 rows, segment lane j, stream s); s is the
+  // fastest index and j the next, so the HC*SG lanes of a (token, chunk)
+  // form an aligned group (HC = 1, 2, 4, 8; SG = 1, 4)
   static_assert(HC == 1 || HC == 2 || HC == 4 || HC == 8, "stream lanes form an aligned group");
+  static_assert((SG == 1 || SG == 4) && !(ONE && SG != 1), "segment lanes: 1, or 4 in the segment loop");
   constexpr int LG = HC == 1 ? 0 : HC == 2 ? 1 : HC == 4 ? 2 : 3;
+  constexpr int LS = SG == 1 ? 0 : 2;
   const int nch = a.r / 8 + (HC + 7) / 8;  // r/8 chunks of h, then the chunk(s) holding the inject rows
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int s = (int)(idx & (HC - 1));
-  const int64_t mc = idx >> LG;
+  const int j = (int)((idx >> LG) & (SG - 1));
+  const int64_t mc = idx >> (LG + LS);
   const int64_t m = min(mc / nch, a.M - 1);  // lanes past M recompute the last token and store nothing
   const int c = (int)(mc % nch);
   const bool live = mc / nch < a.M;
@@ -1258,15 +1266,18 @@ __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
   float rr = 1.0f;  // partials arrive rrms-scaled unless the streams were split into segments
   if (!ONE && a.nseg > 1) {  // (N) rrms of stream s from its segments' sums of squares
     float sq = 0.0f;
-    for (int g = 0; g < a.nseg; ++g) sq += a.SSp[(int64_t)(s * a.nseg + g) * a.Mq + m];
+    for (int g = j; g < a.nseg; g += SG) sq += a.SSp[(int64_t)(s * a.nseg + g) * a.Mq + m];
+#pragma unroll
+    for (int d = HC; d < HC * SG; d <<= 1) sq += __shfl_xor(sq, d, 64);
     rr = 1.0f / sqrtf(sq * a.inv_hs + a.eps);
-    if (live && c == 0) a.rrms[m * HC + s] = rr;
+    if (live && c == 0 && j == 0) a.rrms[m * HC + s] = rr;
   }
   float u[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) u[e] = 0.0f;
-  const float* p = a.Q + ((int64_t)s * a.nseg * a.Mq + m) * a.NP + n;
-  const int64_t gstride = a.Mq * a.NP;
+  const int64_t gstride = a.Mq * a.NP * SG;  // between this lane's segments
+  const float* p = a.Q + ((int64_t)(s * a.nseg + j) * a.Mq + m) * a.NP + n;
+  const int nmine = ONE ? 1 : (a.nseg - j + SG - 1) / SG;  // segments of this lane
   if constexpr (ONE) {
     const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(p), hi = *reinterpret_cast<const f32x4_t*>(p + 4);
 #pragma unroll
@@ -1275,8 +1286,8 @@ __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
       u[e + 4] = hi[e];
     }
   }
-  int g = ONE ? a.nseg : 0;
-  for (; g + 4 <= a.nseg; g += 4) {  // four segments' loads in flight at once
+  int g = ONE ? nmine : 0;
+  for (; g + 4 <= nmine; g += 4) {  // four segments' loads in flight at once
     f32x4_t lo[4], hi[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1291,7 +1302,7 @@ __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
         u[e + 4] += hi[j][e];
       }
   }
-  for (; g < a.nseg; ++g) {
+  for (; g < nmine; ++g) {
     const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(p + g * gstride);
     const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(p + g * gstride + 4);
 #pragma unroll
@@ -1302,12 +1313,14 @@ __global__ __launch_bounds__(256) void hcgr_k1_sum(SumArgs a) {
   }
   float v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {  // sum over the HC stream lanes
+  for (int e = 0; e < 8; ++e) {  // sum over the segment lanes, then the HC stream lanes
+#pragma unroll
+    for (int d = HC; d < HC * SG; d <<= 1) u[e] += __shfl_xor(u[e], d, 64);
     v[e] = rr * u[e];
 #pragma unroll
     for (int d = 1; d < HC; d <<= 1) v[e] += __shfl_xor(v[e], d, 64);
   }
-  if (!live || s != 0) return;
+  if (!live || s != 0 || j != 0) return;
   if (n < a.r) {
     uint32_t o[4];
 #pragma unroll
@@ -2300,23 +2313,32 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     sa.nseg = p.kind == PLAN_TILE ? p.nseg : 1; sa.SSp = reinterpret_cast<const float*>(ws + p.off_ss);
     sa.rrms = f.rrms; sa.eps = s.eps; sa.inv_hs = 1.0f / (float)s.hs;
     const int64_t threads = f.M * (s.r / 8 + 1) * s.hc;
-    const dim3 gs((unsigned)cdiv(threads, 256)), bs(256);
+    // four lanes per (token, chunk, stream) while one lane each would leave
+    // CUs without a workgroup and each lane has a segment (measured on MI355X
+    // at HS = 2560, r = 320: 7.4 -> 4.9 us at HC = 2, M = 32, 9.0 -> 7.6 at
+    // HC = 4, M = 256; 1.6-2.2 us slower at 328 workgroups of one lane each)
+    const int sg = sa.nseg >= 4 && threads <= 256 * 256 ? 4 : 1;
+    const dim3 gs((unsigned)cdiv(threads * sg, 256)), bs(256);
     switch (s.hc) {
       case 1:
-        if (sa.nseg == 1) klaunch(hcgr_k1_sum<1, true>, gs, bs, 0, st, tm.stage(1), sa);
-        else klaunch(hcgr_k1_sum<1, false>, gs, bs, 0, st, tm.stage(1), sa);
+        if (sa.nseg == 1) klaunch(hcgr_k1_sum<1, true, 1>, gs, bs, 0, st, tm.stage(1), sa);
+        else if (sg == 4) klaunch(hcgr_k1_sum<1, false, 4>, gs, bs, 0, st, tm.stage(1), sa);
+        else klaunch(hcgr_k1_sum<1, false, 1>, gs, bs, 0, st, tm.stage(1), sa);
         break;
       case 2:
-        if (sa.nseg == 1) klaunch(hcgr_k1_sum<2, true>, gs, bs, 0, st, tm.stage(1), sa);
-        else klaunch(hcgr_k1_sum<2, false>, gs, bs, 0, st, tm.stage(1), sa);
+        if (sa.nseg == 1) klaunch(hcgr_k1_sum<2, true, 1>, gs, bs, 0, st, tm.stage(1), sa);
+        else if (sg == 4) klaunch(hcgr_k1_sum<2, false, 4>, gs, bs, 0, st, tm.stage(1), sa);
+        else klaunch(hcgr_k1_sum<2, false, 1>, gs, bs, 0, st, tm.stage(1), sa);
         break;
       case 8:
-        if (sa.nseg == 1) klaunch(hcgr_k1_sum<8, true>, gs, bs, 0, st, tm.stage(1), sa);
-        else klaunch(hcgr_k1_sum<8, false>, gs, bs, 0, st, tm.stage(1), sa);
+        if (sa.nseg == 1) klaunch(hcgr_k1_sum<8, true, 1>, gs, bs, 0, st, tm.stage(1), sa);
+        else if (sg == 4) klaunch(hcgr_k1_sum<8, false, 4>, gs, bs, 0, st, tm.stage(1), sa);
+        else klaunch(hcgr_k1_sum<8, false, 1>, gs, bs, 0, st, tm.stage(1), sa);
         break;
       default:
-        if (sa.nseg == 1) klaunch(hcgr_k1_sum<4, true>, gs, bs, 0, st, tm.stage(1), sa);
-        else klaunch(hcgr_k1_sum<4, false>, gs, bs, 0, st, tm.stage(1), sa);
+        if (sa.nseg == 1) klaunch(hcgr_k1_sum<4, true, 1>, gs, bs, 0, st, tm.stage(1), sa);
+        else if (sg == 4) klaunch(hcgr_k1_sum<4, false, 4>, gs, bs, 0, st, tm.stage(1), sa);
+        else klaunch(hcgr_k1_sum<4, false, 1>, gs, bs, 0, st, tm.stage(1), sa);
         break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
