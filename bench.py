@@ -66,6 +66,10 @@ def kernel_bytes(name, M, merged=False, plan=""):
     act_in = K * 2 + HS * 2 + HC * 2          # R, y, inj
     if name == "hcgr_k1_dec":
         return wdown + M * (act_in + K * 2)     # + R2 out
+    if name == "hcgr_k1_fuse":                  # + R2, rrms, inj_next out (the reduction is in-kernel)
+        return wdown + M * (act_in + K * 2 + HC * 4 + HC * 2)
+    if name == "hcgr_dec_persist":              # the whole op in one kernel
+        return op_bytes(M, merged)
     if name == "hcgr_k1_reduce":
         return M * (HC * 4 + HC * 2)            # rrms, inj_next out
     if name in ("hcgr_k1_full", "hcgr_k1_tile"):
@@ -74,15 +78,17 @@ def kernel_bytes(name, M, merged=False, plan=""):
         return wdown + M * (act_in + out)
     if name == "hcgr_k1_sum":
         return M * HC * 2                       # inj_next out
-    if name in ("hcgr_k2_dec", "hcgr_k2_stage", "hcgr_k2_sweep"):
+    if name in ("hcgr_k2_dec", "hcgr_k2_decg", "hcgr_k2_stage", "hcgr_k2_sweep"):
         return K * R_LOW * 2 + HS * 2 + M * (K * 2 + HC * 4 + HS * 2)  # Wu, Wnorm; R2, rrms in; x out
     raise KeyError(name)
 
 
 def kernel_flops(name, M):
-    if name in ("hcgr_k1_dec", "hcgr_k1_full", "hcgr_k1_tile"):
+    if name in ("hcgr_k1_dec", "hcgr_k1_fuse", "hcgr_k1_full", "hcgr_k1_tile"):
         return M * 2 * (R_LOW + HC) * K
-    if name in ("hcgr_k2_dec", "hcgr_k2_stage", "hcgr_k2_sweep"):
+    if name == "hcgr_dec_persist":
+        return op_flops(M)
+    if name in ("hcgr_k2_dec", "hcgr_k2_decg", "hcgr_k2_stage", "hcgr_k2_sweep"):
         return M * 2 * R_LOW * K
     return 0
 
@@ -90,6 +96,10 @@ def kernel_flops(name, M):
 def stage_names(plan: str):
     """Kernels between the four timing marks of hcgr_forward_timed (None where
     a plan has no kernel between two marks)."""
+    if "plan=fused" in plan:
+        return ("hcgr_k1_fuse", None, "hcgr_k2_decg")
+    if "plan=persistent" in plan:
+        return ("hcgr_dec_persist", None, None)
     if "plan=split" in plan:
         return ("hcgr_k1_dec", "hcgr_k1_reduce", "hcgr_k2_dec")
     up = "hcgr_k2_sweep" if "k2_sweep" in plan else "hcgr_k2_gen" if "k2_gen" in plan else "hcgr_k2_stage"
@@ -115,7 +125,7 @@ class Sets:
                 inp["wd"] = synth.fold_merged_weight(inp["wd"], inp["wi"], inp["wnorm"], 336, HS)
                 inp["wi"] = None
             out = op.alloc_outputs(M)
-            ws = torch.empty(max(H.hcgr_workspace_size(op.handle, M), 256), dtype=torch.uint8, device="cuda")
+            ws = H.new_workspace(H.hcgr_workspace_size(op.handle, M))
             self.sets.append((inp, out, ws))
 
     def call(self, H, op, i, stream, events=None):

@@ -82,6 +82,9 @@ hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out);
 /* Frees a handle (NULL is allowed). Outstanding work on streams is unaffected. */
 void hcgr_destroy(hcgr_handle h);
 
+/* Bytes at the start of every workspace that hold arrival counters. */
+#define HCGR_WORKSPACE_COUNTER_BYTES 4096
+
 /* Bytes of device workspace that serve hcgr_forward for every token count
  * from 1 to M (0 for M == 0), with the handle's tuned table if it has one
  * (hcgr_set_plan_table: install the table before sizing the workspace);
@@ -89,9 +92,13 @@ void hcgr_destroy(hcgr_handle h);
  * workspace sized for the largest M serves all smaller calls. The workspace
  * holds the partial sums of the down/inject contraction (per K chunk at
  * decode sizes, per stream or stream segment at mid sizes), their sums of
- * squares and the SiLU output h handed to the up kernel. Its contents on
- * entry are ignored (no zero-fill needed); calls that may run concurrently
- * (different streams) need separate workspaces. */
+ * squares, the SiLU output h handed to the up kernel and, in its first
+ * HCGR_WORKSPACE_COUNTER_BYTES, the arrival counters of the decode plan.
+ * Zero-fill the workspace once after allocating it (hipMemset; at least the
+ * counter bytes): every call leaves the counter bytes zero when it completes,
+ * and reads nothing else of the workspace before writing it. After a call
+ * that returned HCGR_ERR_HIP, zero the counter bytes again. Calls that may
+ * run concurrently (different streams) need separate workspaces. */
 hcgr_status hcgr_workspace_size(hcgr_handle h, int64_t M, size_t* bytes);
 
 /* The full op for M tokens, enqueued on `stream` (a hipStream_t; NULL = the
@@ -233,15 +240,25 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
 #define HCGR_PLAN_HEURISTIC (-1) /* the library's own choice                          */
 #define HCGR_PLAN_SPLIT 0        /* decode plan: K-chunked down kernel, reduction, up */
 #define HCGR_PLAN_TILE 3         /* tile plan: 64-token down tiles, (stream sum), up  */
+#define HCGR_PLAN_FUSED 4        /* fused decode plan: down kernel with the chunk
+                                    reduction done by its last arrivals, then up     */
+#define HCGR_PLAN_PERSISTENT 5   /* persistent decode plan: one kernel, the up role
+                                    waits (bounded) for the down role's h; a wait
+                                    that gives up sets the last counter word of the
+                                    workspace to 1 and that call's x is invalid      */
 #define HCGR_SPLIT_VARIANTS 11   /* down-kernel variants of the decode plan           */
 
 typedef struct hcgr_plan_choice {
     int64_t tokens;         /* table key (token count >= 1); a candidate carries the M it was made for */
-    int32_t kind;           /* HCGR_PLAN_HEURISTIC, HCGR_PLAN_SPLIT or HCGR_PLAN_TILE                 */
+    int32_t kind;           /* HCGR_PLAN_HEURISTIC, HCGR_PLAN_SPLIT, HCGR_PLAN_TILE, HCGR_PLAN_FUSED
+                               or HCGR_PLAN_PERSISTENT                                              */
     int32_t down_variant;   /* SPLIT: 0 .. HCGR_SPLIT_VARIANTS-1 (token tile, row blocks, k waves,
-                               chunk width; hcgr_plan_lookup describes each); serves M <= 256 only.
+                               chunk width; hcgr_plan_lookup describes each); serves M <= 256 only,
+                               HC = 4 only.
                                TILE: 0 = 64-token down tiles, 1 = 128-token down tiles (needs
-                               streams_per_wg = 1)                                                   */
+                               streams_per_wg = 1).
+                               FUSED, PERSISTENT: 0 = 16-token, 1 = 32-token tiles; serve
+                               M <= 256 only                                                        */
     int32_t streams_per_wg; /* TILE: 1, or 4 with HC = 4                                            */
     int32_t segments;       /* TILE with 1 stream per workgroup: column segments per stream,
                                a divisor of HS/128 (1 with 4 streams per workgroup)                  */

@@ -30,6 +30,9 @@ HCGR_WEIGHTS_MERGED_FOLDED = 1
 HCGR_PLAN_HEURISTIC = -1
 HCGR_PLAN_SPLIT = 0
 HCGR_PLAN_TILE = 3
+HCGR_PLAN_FUSED = 4
+HCGR_PLAN_PERSISTENT = 5
+HCGR_WORKSPACE_COUNTER_BYTES = 4096
 PLAN_FIELDS = ("tokens", "kind", "down_variant", "streams_per_wg", "segments", "up_variant", "ranges")
 
 
@@ -330,6 +333,13 @@ def hcgr_validate(cfg: Config, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms
                                         int(ld_inj_next), _p(x), _p(workspace), int(workspace_bytes))
 
 
+def new_workspace(nbytes: int, device: int = 0):
+    """A zero-filled device workspace of at least nbytes (the counter bytes at
+    its start must be zero before the first call that uses it)."""
+    import torch
+    return torch.zeros(max(int(nbytes), HCGR_WORKSPACE_COUNTER_BYTES), dtype=torch.uint8, device=f"cuda:{device}")
+
+
 # ------------------------------------------------------------ convenience --
 class HCGR:
     """Handle + torch-allocated outputs/workspace around ``hcgr_forward``."""
@@ -370,10 +380,11 @@ class HCGR:
             pass
 
     def workspace(self, M: int):
-        import torch
+        """A workspace for M tokens, zero-filled when allocated (the library
+        keeps its counter bytes zero afterwards)."""
         n = hcgr_workspace_size(self.handle, M)
         if self._ws is None or self._ws.numel() < n:
-            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=f"cuda:{self.device}")
+            self._ws = new_workspace(n, self.device)
         return self._ws
 
     def alloc_outputs(self, M: int, ld_inj_next: int | None = None):

@@ -175,7 +175,9 @@ bool to_choice(const hcgr_plan_choice& c, hcgr::Choice* out) {
   x.nseg = c.segments;
   x.kt = c.up_variant;  // 0 staged, 1 sweep, 2 generic, 3 generic over 128 tokens: the planner's KT_* values
   x.nranges = c.ranges;
-  if (c.kind != HCGR_PLAN_HEURISTIC && c.kind != HCGR_PLAN_SPLIT && c.kind != HCGR_PLAN_TILE) return false;
+  if (c.kind != HCGR_PLAN_HEURISTIC && c.kind != HCGR_PLAN_SPLIT && c.kind != HCGR_PLAN_TILE &&
+      c.kind != HCGR_PLAN_FUSED && c.kind != HCGR_PLAN_PERSISTENT)
+    return false;
   *out = x;
   return true;
 }
@@ -184,7 +186,7 @@ hcgr_plan_choice from_choice(const hcgr::Choice& c, int64_t tokens) {
   hcgr_plan_choice o;
   o.tokens = tokens;
   o.kind = c.kind;
-  o.down_variant = c.kind == HCGR_PLAN_SPLIT || c.kind == HCGR_PLAN_TILE ? c.kd : 0;
+  o.down_variant = c.kind == HCGR_PLAN_HEURISTIC ? 0 : c.kd;
   o.streams_per_wg = c.kind == HCGR_PLAN_TILE ? c.spw : 0;
   o.segments = c.kind == HCGR_PLAN_TILE ? c.nseg : 0;
   o.up_variant = c.kind == HCGR_PLAN_TILE ? c.kt : 0;
@@ -255,6 +257,19 @@ static void describe(const hcgr::Shape& s, const hcgr::Plan& p, int64_t M, char*
   if (len) {
     if (M == 0) {
       snprintf(buf, len, "M=0: no launch");
+    } else if (p.kind == hcgr::PLAN_FUSED) {
+      snprintf(buf, len,
+               "M=%lld plan=fused mpad=%lld | k1_fuse tm=%d row_blocks=1 chunks=%d (%d per stream) tiles=%d grid=%dx%d "
+               "last-arrival reduction | k2_decg tm=%d waves=%d channels=%d grid=%dx%d | workspace=%zu",
+               (long long)M, (long long)p.mpad, p.tm, p.nkc, p.kcps, p.ntiles, s.nblk() * p.nkc, p.ntiles, p.tm, p.upw,
+               p.cb, s.hs / p.cb, p.ntiles, p.ws_bytes);
+    } else if (p.kind == hcgr::PLAN_PERSIST) {
+      snprintf(buf, len,
+               "M=%lld plan=persistent mpad=%lld | dec_persist tm=%d one kernel: down role row_blocks=1 chunks=%d "
+               "(%d per stream) tiles=%d workgroups=%d, last-arrival reduction; up role waves=4 channels=%d "
+               "workgroups=%d, waits for the tile's h | workspace=%zu",
+               (long long)M, (long long)p.mpad, p.tm, p.nkc, p.kcps, p.ntiles, s.nblk() * p.nkc * p.ntiles, p.cb,
+               s.hs / p.cb * p.ntiles, p.ws_bytes);
     } else if (p.kind == hcgr::PLAN_SPLIT) {
       hcgr::KDShape a = hcgr::kd_shape(p.k1);
       hcgr::K2Shape b = hcgr::k2_shape(p.k2);

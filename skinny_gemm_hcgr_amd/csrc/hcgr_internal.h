@@ -49,7 +49,15 @@
 
 namespace hcgr {
 
-enum PlanKind { PLAN_SPLIT = 0, PLAN_STREAM = 1, PLAN_FULL = 2, PLAN_TILE = 3 };
+enum PlanKind { PLAN_SPLIT = 0, PLAN_STREAM = 1, PLAN_FULL = 2, PLAN_TILE = 3, PLAN_FUSED = 4, PLAN_PERSIST = 5 };
+
+// Arrival counters. The first kCtrBytes of every workspace hold 32-bit
+// counters that the fused decode plan's workgroups increment; every plan keeps
+// its data past them, a counter is reset to zero by the workgroup that sees
+// its last arrival, so a workspace zeroed once before its first use stays
+// zero there after every completed call.
+constexpr size_t kCtrBytes = 4096;
+constexpr int kCtrWords = (int)(kCtrBytes / 4);
 
 // SPLIT-plan down kernel variants: token tile, 16-row blocks per workgroup,
 // waves splitting each block's k range, columns per chunk.
@@ -149,6 +157,8 @@ struct Plan {
   int64_t mq = 0;                  // rows of the per-stream partials (STREAM)
   int nranges = 1;                 // channel-group ranges per token tile (hcgr_k2_sweep)
   int xgroup = 0;                  // TILE: the down workgroups of a token tile share an XCD
+  // FUSED: chunks per stream (kcps), chunk count (nkc), token tiles, up-kernel waves
+  int ntiles = 0, upw = 0;
   size_t off_p = 0, off_ss = 0, off_h = 0, off_q = 0, ws_bytes = 0;
 };
 
@@ -201,13 +211,99 @@ inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
   p.cb = k2_shape(p.k2).nw * 4;
   p.mpad = (M + p.tm - 1) / p.tm * p.tm;
   const size_t np = (size_t)s.np();
-  p.off_p = 0;
+  p.off_p = kCtrBytes;
   p.off_ss = align256(p.off_p + (size_t)p.nkc * np * (size_t)p.mpad * sizeof(float));
   p.off_h = align256(p.off_ss + (size_t)p.nkc * (size_t)p.mpad * sizeof(float));
   p.ws_bytes = align256(p.off_h + (size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
   *out = p;
   return true;
 }
+
+// FUSED plan (decode sizes, any stream count): two kernels.
+//   K1  hcgr_k1_fuse    a workgroup owns one 16-row block of the down/inject
+//                       rows and one K chunk inside one stream (HS split into
+//                       kcps chunks of whole 128-column units) for a token
+//                       tile; weights, R, y and Wnorm arrive in LDS by direct
+//                       global->LDS loads; COMBINE, the chunk's sums of squares
+//                       and its unscaled partial product go to the workspace,
+//                       and the last workgroup to arrive at the block's
+//                       counter sums the block's chunks per stream, forms
+//                       rrms and writes h, inj_next and rrms
+//   K2  hcgr_k2_decg    the decode up kernel for HC streams (below)
+// kFuseUmax: widest chunk in 128-column units (the LDS holds R, y and the
+// weight rows of one chunk for 32 tokens).
+constexpr int kFuseUmax = 7;
+constexpr int kFuseTarget = 256;  // workgroups per token tile the chunk count aims at
+// Decode up kernel for HC streams: a wave's 16 MFMA rows are 16/HC channels x
+// HC streams; NW waves per workgroup (HC waves up to 4 in the fused plan's up
+// kernel, 4 in the persistent plan).
+inline int decg_waves(int hc) { return hc < 4 ? hc : 4; }
+inline int decg_channels(int hc, int nw) { return nw * (16 / hc); }
+inline int decg_channels(int hc) { return decg_channels(hc, decg_waves(hc)); }
+// Its LDS: Wu rows and the h tile, then the tile's R2 rows of its channels,
+// rrms and Wnorm (each rounded up to whole 1 KB direct-load instructions) and
+// a flag word.
+inline size_t k2_decg_lds(int hc, int tm, int r, int nw) {
+  const size_t cw = (size_t)decg_channels(hc, nw);
+  auto kb = [](size_t b) { return (b + 1023) / 1024 * 1024; };
+  return (size_t)(nw * 16 + tm) * (size_t)r * 2u + kb((size_t)tm * hc * cw * 2) + kb((size_t)tm * hc * 4) +
+         kb((size_t)hc * cw * 2) + 16;
+}
+inline size_t k2_decg_lds(int hc, int tm, int r) { return k2_decg_lds(hc, tm, r, decg_waves(hc)); }
+inline size_t k1_fuse_lds(int tm) {
+  const size_t row = (size_t)kFuseUmax * 128 * 2;  // bytes of one chunk row
+  return (size_t)(2 * tm + 16) * row + 2048 + (size_t)tm * 12;  // R, y, weights, Wnorm slot, iw and sums
+}
+
+// Counter words of the decode plans: block counters [0, 512), then the
+// persistent plan's per-tile "h complete" counters [512, 768), its per-tile
+// exit counters [768, 1023) and the word kErrWord that a persistent wait
+// which gave up sets to 1.
+constexpr int kHdoneWord = 512, kExitWord = 768, kErrWord = kCtrWords - 1;
+
+// FUSED plan (persist = false) or PERSISTENT plan (persist = true) with tm
+// tokens per tile (16 or 32); false when the shape does not fit their limits
+// (counters, LDS, chunk count).
+inline bool make_fused(const Shape& s, int64_t M, int tm, Plan* out, bool persist = false) {
+  if (M <= 0 || (tm != 16 && tm != 32)) return false;
+  const int U = s.hs / 128, nblk = s.nblk();
+  // chunks per stream: about kFuseTarget workgroups per token tile, at most
+  // 4*kFuseUmax chunks in all (the last arriver stages the block's partials
+  // in the y area of its LDS), at least enough that none is wider than
+  // kFuseUmax units
+  int kcps = kFuseTarget / (nblk * s.hc);
+  if (kcps > 4 * kFuseUmax / s.hc) kcps = 4 * kFuseUmax / s.hc;
+  const int kmin = (U + kFuseUmax - 1) / kFuseUmax;
+  if (kcps < kmin) kcps = kmin;
+  if (kcps > U) kcps = U;
+  const int nkc = s.hc * kcps;
+  const int64_t ntiles = cdiv(M, (int64_t)tm);
+  if (nkc > 4 * kFuseUmax || ntiles * nblk > kHdoneWord) return false;
+  if (k1_fuse_lds(tm) > kLdsPerCu) return false;
+  if (persist) {
+    if (ntiles > kErrWord - kExitWord || k2_decg_lds(s.hc, tm, s.r, 4) > kLdsPerCu) return false;
+  } else if (k2_decg_lds(s.hc, tm, s.r) > kLdsPerCu) {
+    return false;
+  }
+  Plan p;
+  p.M = M;
+  p.kind = persist ? PLAN_PERSIST : PLAN_FUSED;
+  p.tm = tm;
+  p.kcps = kcps;
+  p.nkc = nkc;
+  p.ntiles = (int)ntiles;
+  p.upw = persist ? 4 : decg_waves(s.hc);
+  p.cb = decg_channels(s.hc, p.upw);
+  p.mpad = ntiles * tm;
+  p.off_p = kCtrBytes;
+  p.off_ss = align256(p.off_p + (size_t)ntiles * nblk * nkc * tm * 16 * sizeof(float));
+  p.off_h = align256(p.off_ss + (size_t)ntiles * nblk * nkc * tm * sizeof(float));
+  p.ws_bytes = align256(p.off_h + (size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
+  *out = p;
+  return true;
+}
+// Largest M the heuristic serves with the FUSED plan.
+constexpr int64_t kFusedMaxM = 32;
 
 // TILE plan with explicit parameters: spw streams per down workgroup (1, or 4
 // with HC = 4), nseg column segments per stream (spw = 1; divides HS/128),
@@ -247,8 +343,8 @@ inline bool make_tile(const Shape& s, int64_t M, int spw, int nseg, int kt, int 
   const int tm2 = kt_shape(kt).tm;
   p.mpad = cdiv(M, tm2) * tm2;
   p.mq = cdiv(M, (int64_t)tm) * tm;
-  p.off_h = 0;
-  p.off_q = align256((size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
+  p.off_h = kCtrBytes;
+  p.off_q = align256(p.off_h + (size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
   p.ws_bytes = p.off_q;
   if (spw == 1) {
     const size_t parts = (size_t)s.hc * (size_t)nseg;
@@ -266,7 +362,15 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   if (M <= 0) return p;
   const int hs = s.hs;
   const size_t np = (size_t)s.np();
-  // stream counts other than 4 (1, 2 or 8) take the tile plan at every M:
+  // decode sizes with one or two streams: the fused plan (two kernels).
+  // Measured on MI355X (HS, r = 2560, 320; cold buffers): HC = 1 11.8-14.4 us
+  // at M = 1..32 against 18.2-21.9 for the tile plan, HC = 2 12.9-15.8 against
+  // 21.3-23.4. With four streams the split plan's three kernels stay faster
+  // (12.8 and 14.6 us at M = 1 and 32 against 14.4 and 19.4), and with eight
+  // the tile plan (28.6 against 37.5 us at M = 32): both spread a stream's
+  // weight rows over more workgroups than one 16-row block per chunk.
+  if (M <= kFusedMaxM && (s.hc == 1 || s.hc == 2) && make_fused(s, M, M <= 16 ? 16 : 32, &p)) return p;
+  // stream counts other than 4 (1, 2 or 8) take the tile plan above that:
   // one stream per down workgroup, the stream sum, and hcgr_k2_gen
   const bool generic = s.hc != 4;
   if (M <= split_max(s.k(), s.np()) && !generic) {
@@ -360,25 +464,32 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   p.tm = tm1;
   p.mpad = cdiv(M, tm2) * tm2;  // h rows the up kernel may read
   p.mq = cdiv(M, tm1) * tm1;
-  p.off_h = 0;
-  p.off_q = align256((size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
+  p.off_h = kCtrBytes;
+  p.off_q = align256(p.off_h + (size_t)p.mpad * (size_t)s.r * sizeof(uint16_t));
   p.ws_bytes = p.off_q;
   if (p.kind == PLAN_STREAM) p.ws_bytes = align256(p.off_q + (size_t)s.hc * (size_t)p.mq * np * sizeof(float));
   return p;
 }
 
 // Workspace that serves every token count up to M: the largest plan need
-// over M' <= M. Plans are piecewise: the split plan for M' <= kSplitMaxM, and
-// tile plans whose partial-sum storage depends on the token tile count
-// (every M' with the same tile count needs at most what its largest member
-// needs), so the maximum is taken over at most kSplitMaxM + 256 + 1 plans.
+// over M' <= M. Plans are piecewise: the decode plans for M' <= kSplitMaxM,
+// then tile plans whose partial-sum storage depends on the 64-token tile count
+// only (every M' with the same tile count needs what its largest member
+// needs) until the 128-token down tiles take over, whose need grows with M'.
+// The maximum is therefore taken over M' = 1 .. kSplitMaxM, the multiples of
+// 64 up to the 128-token switch, and M itself.
 inline size_t workspace_bound(const Shape& s, int64_t M) {
   if (M <= 0) return 0;
   size_t best = make_plan(s, M).ws_bytes;
-  for (int64_t m = 1; m <= M && m <= kSplitMaxM; ++m) best = best > make_plan(s, m).ws_bytes ? best : make_plan(s, m).ws_bytes;
-  for (int64_t t = 1; t * kTileTm <= M && t <= 256; ++t) {
+  for (int64_t m = 1; m <= M && m <= kSplitMaxM; ++m) {
+    const size_t b = make_plan(s, m).ws_bytes;
+    best = best > b ? best : b;
+  }
+  const int64_t tsplit = cdiv(s.nblk(), kTileMaxBlk);
+  for (int64_t t = 1; t * kTileTm <= M; ++t) {
     const size_t b = make_plan(s, t * kTileTm).ws_bytes;
     best = best > b ? best : b;
+    if (cdiv(t * kTileTm, (int64_t)128) * s.hc * tsplit >= 256) break;  // 128-token tiles from here on
   }
   return best;
 }
@@ -392,8 +503,9 @@ inline size_t workspace_bound(const Shape& s, int64_t M) {
 constexpr int kChoiceHeuristic = -1;
 constexpr int64_t kSplitChoiceMaxM = 256;  // a decode-plan choice serves token counts up to this
 struct Choice {
-  int kind = kChoiceHeuristic;  // kChoiceHeuristic, PLAN_SPLIT or PLAN_TILE
-  int kd = 0;                   // PLAN_SPLIT: down-kernel variant; PLAN_TILE: 0 = 64-token, 1 = 128-token down tiles
+  int kind = kChoiceHeuristic;  // kChoiceHeuristic, PLAN_SPLIT, PLAN_TILE, PLAN_FUSED or PLAN_PERSIST
+  int kd = 0;                   // PLAN_SPLIT: down-kernel variant; PLAN_TILE: 0 = 64-token, 1 = 128-token down tiles;
+                                // PLAN_FUSED, PLAN_PERSIST: 0 = 16-token, 1 = 32-token tiles
   int spw = 1, nseg = 1, kt = KT_S128, nranges = 1;  // PLAN_TILE: as make_tile
 };
 struct TableEntry {
@@ -406,6 +518,9 @@ inline bool plan_from_choice(const Shape& s, int64_t M, const Choice& c, Plan* o
     return s.hc == 4 && M >= 1 && M <= kSplitChoiceMaxM && c.kd >= 0 && c.kd < KD_NVAR && make_split(s, M, c.kd, out);
   if (c.kind == PLAN_TILE)
     return (c.kd == 0 || c.kd == 1) && make_tile(s, M, c.spw, c.nseg, c.kt, c.nranges, out, c.kd ? 128 : 64);
+  if (c.kind == PLAN_FUSED || c.kind == PLAN_PERSIST)
+    return M >= 1 && M <= kSplitChoiceMaxM && (c.kd == 0 || c.kd == 1) &&
+           make_fused(s, M, c.kd ? 32 : 16, out, c.kind == PLAN_PERSIST);
   return false;
 }
 
@@ -425,6 +540,13 @@ inline int plan_choices(const Shape& s, int64_t M, Choice* out, int cap) {
     c.kd = kd;
     add(c);
   }
+  for (int kind : {(int)PLAN_FUSED, (int)PLAN_PERSIST})
+    for (int kd = 0; kd < 2; ++kd) {
+      Choice c;
+      c.kind = kind;
+      c.kd = kd;
+      add(c);
+    }
   const int ups[4] = {KT_S128, KT_SWEEP, KT_GEN, KT_GEN128};
   const int pairs = s.hs / 128;
   for (int big = 0; big < 2; ++big)
@@ -489,7 +611,7 @@ inline size_t workspace_bound_table(const Shape& s, int64_t M, const TableEntry*
     const size_t h = workspace_bound(s, hi);  // heuristic wherever entry i falls back
     best = best > h ? best : h;
     Plan p;
-    if (t[i].c.kind == PLAN_SPLIT) {
+    if (t[i].c.kind == PLAN_SPLIT || t[i].c.kind == PLAN_FUSED || t[i].c.kind == PLAN_PERSIST) {
       const int64_t m = hi < kSplitChoiceMaxM ? hi : kSplitChoiceMaxM;
       if (m >= lo && plan_from_choice(s, m, t[i].c, &p)) best = best > p.ws_bytes ? best : p.ws_bytes;
     } else if (t[i].c.kind == PLAN_TILE && plan_from_choice(s, hi, t[i].c, &p)) {
@@ -526,6 +648,12 @@ int launch_combine(const CombineArgs& a, void* stream);
 
 // Raises the dynamic-LDS limit of the up kernels on the current device.
 int configure_kernels();
+// The same for the fused decode plan's kernels (hcgr_decode.hip).
+int configure_decode_kernels();
+
+// Enqueues the fused or persistent decode plan (hcgr_decode.hip); events as
+// launch_forward (the persistent plan's one kernel is stage 0).
+int launch_fused(const Shape& s, const Plan& p, const ForwardArgs& a, void* stream, void* const* events);
 
 // Enqueues the plan's kernels on `stream`; returns the hipError_t of the
 // launches. With `events` (6 hipEvent_t) events[2i] and events[2i+1] mark the

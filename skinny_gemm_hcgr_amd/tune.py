@@ -92,7 +92,7 @@ def tune(cfg, tokens, reps=30, seed=0, log=print):
         cands = H.hcgr_plan_candidates(cfg, M)
         choices = [{"tokens": M, "kind": H.HCGR_PLAN_HEURISTIC}] + cands
         need = max(H.hcgr_workspace_size_table(cfg, [c], M) for c in choices)
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        ws = H.new_workspace(need)
         outs = op.alloc_outputs(M)
 
         def run(i):

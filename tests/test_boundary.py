@@ -161,16 +161,21 @@ def test_config_errors(lib, kw, st):
 
 @pytest.mark.parametrize("hc", [1, 2, 8])
 def test_other_stream_counts(lib, hc):
-    """HC = 1, 2 and 8 are accepted; their plan is the tile plan at every M
-    (one stream per down workgroup, the stream sum, the HC-generic up kernel)
-    and one workspace sized for the largest M serves every smaller one."""
+    """HC = 1, 2 and 8 are accepted; with one or two streams the plan is the
+    fused decode plan up to 32 tokens (last-arrival reduction, the HC-generic
+    decode up kernel), otherwise the tile plan (one stream per down
+    workgroup, the stream sum, the HC-generic up kernel); one workspace sized
+    for the largest M serves every smaller one."""
     cfg = H.Config(hc=hc)
-    for M in (1, 5, 64, 65, 1000, 8192):
+    for M in (1, 5, 32, 33, 64, 65, 1000, 8192):
         assert Layout(cfg, M).call() == H.HCGR_OK
         L = Layout(cfg, M)
         assert _mix(L) == H.HCGR_OK and _combine(L) == H.HCGR_OK
         d = H.hcgr_describe_plan(cfg, M)
-        assert "plan=tile" in d and "k1_sum" in d and "k2_gen" in d, d
+        if M <= 32 and hc in (1, 2):
+            assert "plan=fused" in d and "k2_decg" in d, d
+        else:
+            assert "plan=tile" in d and "k1_sum" in d and "k2_gen" in d, d
     for hs, r in ((2560, 320), (256, 96), (1024, 512)):
         c = H.Config(hc=hc, hs=hs, r=r)
         prev = 0

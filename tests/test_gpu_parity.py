@@ -369,7 +369,8 @@ def test_workspace_reuse_across_sizes(H, op, weights):
     """One workspace shared by calls of different M (different plans) in a row:
     a call's result does not depend on what an earlier call left behind."""
     ws = torch.empty(H.hcgr_workspace_size(op.handle, 2048) + 4096, dtype=torch.uint8, device="cuda")
-    ws.fill_(0xFF)  # NaN patterns everywhere
+    ws.fill_(0xFF)  # NaN patterns everywhere past the counters
+    ws[:H.HCGR_WORKSPACE_COUNTER_BYTES].zero_()
     res = {}
     for M in (2048, 7, 300, 7, 33, 64, 16, 33):
         inp = synth.make_inputs(M, SHAPE, seed=10, device="cuda", weights=weights)
@@ -383,13 +384,14 @@ def test_workspace_reuse_across_sizes(H, op, weights):
         res[M] = out
     inp = synth.make_inputs(7, SHAPE, seed=10, device="cuda", weights=weights)
     check_all(res[7], run_oracle(inp))
+    assert int(ws[:H.HCGR_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0  # every counter back at zero
 
 
 def test_decode_interleaved_stress(H, op, weights):
     """Many back-to-back decode-size calls of four sizes interleaved on one
     workspace (cross-workgroup partials written by one kernel and summed by
     the next): bitwise-identical results every time, matching the oracle."""
-    ws = torch.empty(max(H.hcgr_workspace_size(op.handle, 64), 256), dtype=torch.uint8, device="cuda")
+    ws = H.new_workspace(H.hcgr_workspace_size(op.handle, 64))
     sizes = (5, 32, 64, 1)
     inps = {M: synth.make_inputs(M, SHAPE, seed=20 + M, device="cuda", weights=weights) for M in sizes}
     outs = {M: op.alloc_outputs(M) for M in sizes}
@@ -419,7 +421,7 @@ def test_forward_timed_matches_forward(H, op, weights, M):
     inp = synth.make_inputs(M, SHAPE, seed=3, device="cuda", weights=weights)
     ref = gpu_forward(op, inp)
     out = op.alloc_outputs(M)
-    ws = torch.empty(H.hcgr_workspace_size(op.handle, M), dtype=torch.uint8, device="cuda")
+    ws = H.new_workspace(H.hcgr_workspace_size(op.handle, M))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for e in ev:
         e.record()

@@ -135,3 +135,39 @@ def test_shipped_tables_load_and_validate(lib):
             H.hcgr_plan_lookup(cfg, t, M)
             assert H.hcgr_workspace_size_table(cfg, t, M) >= ws_of(H.hcgr_plan_lookup(cfg, t, M)[1])
     assert H.shipped_plan_table(H.Config(hs=1024)) is None
+
+
+@pytest.mark.parametrize("hc", [1, 2, 4, 8])
+@pytest.mark.parametrize("hs,r", [(2560, 320), (1024, 64), (4096, 512), (640, 96)])
+def test_workspace_bound_covers_every_smaller_plan(lib, hc, hs, r):
+    """hcgr_workspace_size_for(M) never decreases and is at least the need of
+    the plan of every M' <= M, so a workspace sized for the largest M serves
+    every smaller call (at HC = 1 the 64-token tile plan runs past 16384
+    tokens, with more column segments at some counts than at larger ones)."""
+    cfg = H.Config(hc=hc, hs=hs, r=r)
+    Ms = sorted(set(list(range(1, 300)) + list(range(300, 40000, 61)) + [16383, 16384, 16448, 24576, 24577, 32640,
+                                                                           32641, 40000, 65536]))
+    prev, need_max = 0, 0
+    for M in Ms:
+        n = H.hcgr_workspace_size_for(cfg, M)
+        need_max = max(need_max, ws_of(H.hcgr_describe_plan(cfg, M)))
+        assert n >= prev, (M, n, prev)
+        assert n >= need_max, (M, n, need_max)
+        prev = n
+
+
+def test_workspace_keeps_the_counter_bytes(lib):
+    """Every plan's data starts past the counter bytes, and the fused plan is
+    the heuristic at decode sizes with one or two streams."""
+    for hc in (1, 2, 4, 8):
+        cfg = H.Config(hc=hc)
+        for M in (1, 16, 17, 32, 33, 100, 5000):
+            d = H.hcgr_describe_plan(cfg, M)
+            assert ("plan=fused" in d) == (hc in (1, 2) and M <= 32), d
+            assert ws_of(d) > H.HCGR_WORKSPACE_COUNTER_BYTES
+            for kind in (H.HCGR_PLAN_FUSED, H.HCGR_PLAN_PERSISTENT):
+                if M <= 256:
+                    c = {"tokens": M, "kind": kind, "down_variant": int(M > 16)}
+                    chosen, desc = H.hcgr_plan_lookup(cfg, [c], M)
+                    assert chosen["kind"] == kind, (hc, M, desc)
+                    assert H.hcgr_workspace_size_table(cfg, [c], M) >= ws_of(desc)
