@@ -161,6 +161,31 @@ hcgr_status hcgr_forward_timed(hcgr_handle h,
                                void* workspace, size_t workspace_bytes,
                                void* stream, void* const* events);
 
+/* hcgr_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). The workspace is the library's own static scratch
+ * array of hcgr_noalloc_scratch_bytes() bytes (32 MiB), one copy per GPU,
+ * held until the process ends; hcgr_create looks its address up and zeroes its
+ * counter bytes once per device. Arguments, checks and results as
+ * hcgr_forward; a call whose plan needs more workspace than the scratch holds
+ * (HC = 4, HS = 2560, r = 320: above 4096 tokens) returns
+ * HCGR_ERR_WORKSPACE_TOO_SMALL and launches nothing. Every call on one GPU
+ * shares the scratch, so calls that may overlap on one GPU (different
+ * streams, or threads) race: serialise them. Allocates nothing and does not
+ * synchronise. */
+hcgr_status hcgr_forward_noalloc(hcgr_handle h,
+                                 const uint16_t* R, const uint16_t* y,
+                                 const uint16_t* inj, int64_t ld_inj,
+                                 const uint16_t* wnorm, const uint16_t* wd,
+                                 const uint16_t* wi, const uint16_t* wu,
+                                 int64_t M,
+                                 uint16_t* R2, float* rrms,
+                                 uint16_t* inj_next, int64_t ld_inj_next,
+                                 uint16_t* x, void* stream);
+
+/* Bytes of the scratch hcgr_forward_noalloc uses on each GPU. */
+size_t hcgr_noalloc_scratch_bytes(void);
+
 /* The host-side checks of hcgr_forward for a configuration, without a handle,
  * a device or a launch: returns what hcgr_forward would return before
  * launching (device and stream checks excluded). Pure host code. */

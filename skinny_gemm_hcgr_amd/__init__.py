@@ -113,6 +113,9 @@ def load_library(path: str = LIB_PATH):
     lib.hcgr_forward.argtypes = [P, P, P, P, I64, P, P, P, P, I64, P, P, P, I64, P, P, SZ, P]
     lib.hcgr_forward_timed.argtypes = [P, P, P, P, I64, P, P, P, P, I64, P, P, P, I64, P, P, SZ, P,
                                        ctypes.POINTER(P)]
+    lib.hcgr_forward_noalloc.argtypes = [P, P, P, P, I64, P, P, P, P, I64, P, P, P, I64, P, P]
+    lib.hcgr_noalloc_scratch_bytes.argtypes = []
+    lib.hcgr_noalloc_scratch_bytes.restype = SZ
     lib.hcgr_validate.argtypes = [CFG, P, P, P, I64, P, P, P, P, I64, P, P, P, I64, P, P, SZ]
     lib.hcgr_combine.argtypes = [P, P, P, P, I64, I64, P, P]
     lib.hcgr_mix.argtypes = [P, P, P, P, P, P, I64, P, P, I64, P, P, SZ, P]
@@ -129,7 +132,7 @@ def load_library(path: str = LIB_PATH):
     lib.hcgr_last_error.argtypes = []
     lib.hcgr_last_error.restype = ctypes.c_char_p
     for name in ("hcgr_create", "hcgr_workspace_size", "hcgr_workspace_size_for", "hcgr_forward",
-                 "hcgr_forward_timed", "hcgr_combine", "hcgr_mix", "hcgr_validate_combine",
+                 "hcgr_forward_timed", "hcgr_forward_noalloc", "hcgr_combine", "hcgr_mix", "hcgr_validate_combine",
                  "hcgr_validate_mix", "hcgr_validate", "hcgr_describe_plan", "hcgr_plan_candidates",
                  "hcgr_plan_lookup", "hcgr_workspace_size_table", "hcgr_set_plan_table"):
         getattr(lib, name).restype = ctypes.c_int
@@ -286,6 +289,23 @@ def hcgr_forward_timed(handle, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms
                                            _p(wu), int(M), _p(R2), _p(rrms), _p(inj_next), int(ld_inj_next), _p(x),
                                            _p(workspace), int(workspace_bytes), stream, ev)
     return _check(st, "hcgr_forward_timed")
+
+
+def hcgr_forward_noalloc(handle, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x,
+                         stream=None, *, check: bool = True) -> int:
+    """``hcgr_forward`` on the library's own per-GPU scratch instead of a caller
+    workspace (stream as in ``hcgr_forward``)."""
+    stream = _stream(stream, R)
+    st = load_library().hcgr_forward_noalloc(handle, _p(R), _p(y), _p(inj), int(ld_inj), _p(wnorm), _p(wd), _p(wi),
+                                             _p(wu), int(M), _p(R2), _p(rrms), _p(inj_next), int(ld_inj_next),
+                                             _p(x), stream)
+    if check:
+        _check(st, "hcgr_forward_noalloc")
+    return st
+
+
+def hcgr_noalloc_scratch_bytes() -> int:
+    return int(load_library().hcgr_noalloc_scratch_bytes())
 
 
 def hcgr_combine(handle, R, y, inj, ld_inj, M, R2, stream=None, *, check: bool = True) -> int:

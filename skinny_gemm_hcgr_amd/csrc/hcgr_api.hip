@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -20,7 +21,19 @@ struct hcgr_op {
   std::vector<hcgr::TableEntry> table;  // tuned plans (empty: the heuristic)
 };
 
+// Scratch for hcgr_forward_noalloc: the workspace of callers that cannot
+// allocate. Each GPU the library runs on holds one copy until the process
+// ends; every call on that GPU shares it.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
+
+// Device address of each GPU's copy of `scratch`, looked up once per device
+// (the host-side name of the array is not a device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
 
 thread_local char g_err[512] = "";
 
@@ -372,6 +385,21 @@ hcgr_status hcgr_set_plan_table(hcgr_handle h, const hcgr_plan_choice* table, in
   return ok();
 }
 
+// Looks up the current device's copy of `scratch` and zeroes its counter
+// bytes, once per device; `device` must be current.
+static hcgr_status scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return fail(HCGR_ERR_UNSUPPORTED, "device %d: at most %d devices", device, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[device]) return HCGR_OK;
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return fail(HCGR_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  if ((e = hipMemset(p, 0, hcgr::kCtrBytes)) != hipSuccess)
+    return fail(HCGR_ERR_HIP, "zeroing the scratch counters: %s", hipGetErrorString(e));
+  g_scratch[device] = p;
+  return HCGR_OK;
+}
+
 hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out) {
   if (!out) return fail(HCGR_ERR_INVALID_ARGUMENT, "out is NULL");
   *out = nullptr;
@@ -395,9 +423,11 @@ hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out) {
   if (cur != device && (e = hipSetDevice(device)) != hipSuccess)
     return fail(HCGR_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(e));
   int ke = hcgr::configure_kernels();
+  const hcgr_status sst = ke == (int)hipSuccess ? scratch_setup(device) : HCGR_OK;
   if (cur != device) (void)hipSetDevice(cur);
   if (ke != (int)hipSuccess)
     return fail(HCGR_ERR_HIP, "kernel attribute set-up failed: %s", hipGetErrorString((hipError_t)ke));
+  if (sst != HCGR_OK) return sst;
   hcgr_op* op = new (std::nothrow) hcgr_op;
   if (!op) return fail(HCGR_ERR_INVALID_ARGUMENT, "out of host memory");
   op->shape = s;
@@ -490,6 +520,31 @@ hcgr_status hcgr_forward(hcgr_handle h, const uint16_t* R, const uint16_t* y, co
   return forward_impl(h, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x, workspace,
                       workspace_bytes, stream, nullptr);
 }
+
+hcgr_status hcgr_forward_noalloc(hcgr_handle h, const uint16_t* R, const uint16_t* y, const uint16_t* inj,
+                                 int64_t ld_inj, const uint16_t* wnorm, const uint16_t* wd, const uint16_t* wi,
+                                 const uint16_t* wu, int64_t M, uint16_t* R2, float* rrms, uint16_t* inj_next,
+                                 int64_t ld_inj_next, uint16_t* x, void* stream) {
+  if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ws = h->device >= 0 && h->device < kMaxDevices ? g_scratch[h->device] : nullptr;
+  }
+  if (!ws) return fail(HCGR_ERR_HIP, "no scratch on device %d", h->device);
+  if (M > 0) {
+    const hcgr::Plan plan = hcgr::plan_for(h->shape, M, h->table.data(), (int)h->table.size());
+    if (plan.ws_bytes > kScratchBytes)
+      return fail(HCGR_ERR_WORKSPACE_TOO_SMALL,
+                  "M=%lld needs %zu bytes of workspace; the library's scratch holds %zu (call hcgr_forward with a "
+                  "workspace)",
+                  (long long)M, plan.ws_bytes, kScratchBytes);
+  }
+  return forward_impl(h, R, y, inj, ld_inj, wnorm, wd, wi, wu, M, R2, rrms, inj_next, ld_inj_next, x, ws,
+                      kScratchBytes, stream, nullptr);
+}
+
+size_t hcgr_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 hcgr_status hcgr_forward_timed(hcgr_handle h, const uint16_t* R, const uint16_t* y, const uint16_t* inj,
                                int64_t ld_inj, const uint16_t* wnorm, const uint16_t* wd, const uint16_t* wi,
