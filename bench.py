@@ -182,6 +182,29 @@ def time_calls(H, op, sets, steps, warmup, stream):
     return start.elapsed_time(end) * 1e3 / steps, host_us
 
 
+def time_call_stats(H, op, sets, stream, n=60, sweeps=3):
+    """The statistic of the pages' benchmark table: each call of a sweep timed
+    on its own (HIP events between back-to-back calls, all queued behind a GPU
+    spin before the first runs), the median of n calls per sweep, then the
+    median of the sweeps and their spread (max - min) / median."""
+    import torch
+    meds = []
+    for _ in range(sweeps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        _spin(torch, 40 * n + 2000)
+        ev[0].record()
+        for i in range(n):
+            sets.call(H, op, i, stream)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n))
+        meds.append(d[n // 2] if n % 2 else 0.5 * (d[n // 2 - 1] + d[n // 2]))
+    med = sorted(meds)[len(meds) // 2]
+    return {"median_us": round(med, 3), "sweep_medians_us": [round(m, 3) for m in meds],
+            "spread": round((max(meds) - min(meds)) / med, 4), "calls_per_sweep": n, "sweeps": sweeps}
+
+
 def time_kernels(H, op, sets, steps, stream, host_us):
     """Average duration (µs) of each of the three kernels over `steps` calls,
     from the start/end HIP events hcgr_forward_timed takes around each kernel
@@ -296,17 +319,22 @@ def roofline_entry(name, M, us, merged, plan, workload):
             "source_digest": kernel_source_digest()}
 
 
-def run_workload(H, op_sep, op_merged, name, M, merged, scale0, steps, warmup, cold, stream):
+def run_workload(H, op_sep, op_merged, name, M, merged, scale0, steps, warmup, cold, stream, extras=True):
+    """Times one workload: K back-to-back calls (the headline), per-kernel
+    durations, and with `extras` the pages' per-call statistic and a graph
+    replay."""
     op = op_merged if merged else op_sep
     nb = set_count(M, merged, cold)
     sets = Sets(H, op, M, nb, merged=merged, scale_stream0=scale0)
     us, host_us = time_calls(H, op, sets, steps, warmup, stream)
     kern = time_kernels(H, op, sets, max(8, min(steps, 200)), stream, host_us)
-    graph_us = time_graph(H, op, sets, max(1, min(200, (steps + nb - 1) // nb)), stream)
+    stats = time_call_stats(H, op, sets, stream) if extras else None
+    graph_us = time_graph(H, op, sets, max(1, min(200, (steps + nb - 1) // nb)), stream) if extras else None
     B, F = op_bytes(M, merged), op_flops(M)
     res = {"workload": name, "M": M, "merged": merged, "buffer_sets": nb,
            "cache": "cold (rotating sets > Infinity Cache)" if nb > 1 else ("warm" if not cold else "single set"),
-           "us_per_call": round(us, 3), "us_per_call_graph": round(graph_us, 3),
+           "us_per_call": round(us, 3), "us_per_call_graph": round(graph_us, 3) if graph_us else None,
+           "per_call_stats": stats,
            "host_enqueue_us_per_call": round(host_us, 2), "tokens_per_s": round(M / (us * 1e-6), 1),
            "op_alg_bytes": B, "op_flops": F,
            "op_hbm_frac": round(B / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
@@ -319,27 +347,66 @@ def run_workload(H, op_sep, op_merged, name, M, merged, scale0, steps, warmup, c
     return res
 
 
-def cpu_baseline(M, budget_s=12.0):
-    """The fp64 oracle (as it stands) on this host's cores, on the same
-    workload shape: repeated full M-token batches until ~budget_s of CPU time."""
-    import torch
+def cpu_model():
+    """CPU model name and the host's logical core count."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    name = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return name, os.cpu_count()
+
+
+# The oracle's CPU baseline: per workload, the tokens timed with all cores and
+# with one thread and the repetitions (median taken). Every step is per token,
+# so a row sample of a large workload runs at that workload's per-token cost;
+# the samples keep the whole leg to about ten seconds of CPU time.
+CPU_PLAN = {1: (1, 5, 1, 5), 32: (32, 5, 32, 3), 1024: (256, 3, 16, 3), 8192: (256, 3, 16, 3),
+            65536: (256, 3, 16, 3)}
+
+
+def cpu_baseline(M_head):
+    """The fp64 oracle (as it stands, OpenMP over tokens) on this host's cores:
+    µs/call and tokens/s per workload size, all cores and one thread, on the
+    same seeded inputs as the GPU run (row samples of the larger sizes)."""
     import oracle
     import synth
-    d = synth.make_inputs(M, synth.Shape(HC, HS, R_LOW), seed=0, device="cpu")
     cfg = oracle.OracleConfig()
-    oracle.forward(cfg, d["R"][:1], d["y"][:1], d["inj"][:1], d["wnorm"], d["wd"], d["wi"], d["wu"])
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        oracle.forward(cfg, d["R"], d["y"], d["inj"], d["wnorm"], d["wd"], d["wi"], d["wu"])
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    del torch
-    return {"value": round(n * M / dt, 2), "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{n} full batches of the M={M} workload ({n * M} tokens), fp64, OpenMP over tokens",
-            "us_per_call": round(dt / n * 1e6, 1)}
+    wts = synth.make_weights(synth.Shape(HC, HS, R_LOW), seed=0, device="cpu")
+    model, ncpu = cpu_model()
+    nthreads = oracle.max_threads()
+    per_m = []
+    head = None
+    for M, (n_all, reps_all, n_one, reps_one) in CPU_PLAN.items():
+        d = synth.make_inputs(max(n_all, n_one), synth.Shape(HC, HS, R_LOW), seed=0, device="cpu", weights=wts,
+                              scale_stream0=8.0 if M == 8192 else 1.0)
+        rec = {"M": M}
+        for label, n, reps, threads in (("all_cores", n_all, reps_all, 0), ("one_thread", n_one, reps_one, 1)):
+            times = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                oracle.forward(cfg, d["R"][:n], d["y"][:n], d["inj"][:n], d["wnorm"], d["wd"], d["wi"], d["wu"],
+                               threads=threads)
+                times.append(time.perf_counter() - t0)
+            t = sorted(times)[len(times) // 2]
+            rec[label] = {"tokens_timed": n, "reps": reps, "tokens_per_s": round(n / t, 2),
+                          "us_per_token": round(t / n * 1e6, 2),
+                          "us_per_call_est": round(t / n * M * 1e6, 1), "threads": nthreads if threads == 0 else 1}
+        per_m.append(rec)
+        if M == M_head:
+            head = rec
+    if head is None:
+        head = per_m[1]
+    a = head["all_cores"]
+    return {"value": a["tokens_per_s"], "unit": "tokens/s", "cores": a["threads"], "kind": "oracle",
+            "sample": f"{a['reps']} runs (median) of {a['tokens_timed']} tokens of the M={head['M']} workload, fp64 "
+                      "oracle, OpenMP over tokens on all cores",
+            "cpu_model": model, "nproc": ncpu, "per_m": per_m,
+            "note": "large M timed on row samples (every step is per token); us_per_call_est = per-token time x M"}
 
 
 def entry_bytes(entry, M):
@@ -403,6 +470,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--warm", action="store_true", help="headline on one re-read buffer set")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="only the headline's cold rotating-set calls (no warm set, graph replay, per-call "
+                         "statistic, sweep or CPU leg): the command the kernel traces are taken with")
     ap.add_argument("--heuristic", action="store_true",
                     help="plan by the library's heuristic instead of the tuned tables shipped with the package")
     ap.add_argument("--json-out", default=None)
@@ -444,10 +514,14 @@ def main():
 
     M, merged, scale0 = WORKLOADS[args.workload]
     torch.cuda.synchronize()
-    head = run_workload(H, op, opm, args.workload, M, merged, scale0, args.steps, args.warmup, not args.warm, stream)
+    if args.cold_only:
+        args.no_sweep = args.no_cpu = True
+    head = run_workload(H, op, opm, args.workload, M, merged, scale0, args.steps, args.warmup, not args.warm, stream,
+                        extras=not args.cold_only)
     warm = None
-    if not args.warm:
-        warm = run_workload(H, op, opm, args.workload, M, merged, scale0, args.steps, args.warmup, False, stream)
+    if not args.warm and not args.cold_only:
+        warm = run_workload(H, op, opm, args.workload, M, merged, scale0, args.steps, args.warmup, False, stream,
+                            extras=False)
     torch.cuda.synchronize()
     print(f"[bench] {args.workload}: {head['us_per_call']} us/call ({head['cache']}), kernels {head['kernels_us']}",
           file=sys.stderr, flush=True)
@@ -493,6 +567,7 @@ def main():
                        "weights": "merged_folded_n336" if merged else "separate",
                        "buffers": head["cache"], "buffer_sets": head["buffer_sets"], "plans": plans},
             "us_per_call": head["us_per_call"], "us_per_call_graph": head["us_per_call_graph"],
+            "per_call_stats": head["per_call_stats"],
             "us_per_call_warm": warm["us_per_call"] if warm else None,
             "op_roofline_frac": head["op_roofline_frac"], "op_hbm_frac": head["op_hbm_frac"],
             "kernels_us": head["kernels_us"], "roofline": roof,
@@ -503,12 +578,13 @@ def main():
                                                      "65536": 2636.4},
                         "note": "page numbers: MI355X, merged/folded weights, graph replay; context only"}}
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(M if M <= 1024 else 64)
+        line["cpu_baseline"] = cpu_baseline(M)
     else:
         line["cpu_baseline"] = None
     if sweep:
-        line["sweep"] = [{k: r[k] for k in ("workload", "M", "us_per_call", "us_per_call_graph", "tokens_per_s",
-                                            "op_roofline_frac", "op_hbm_frac", "op_mfma_frac", "kernels_us")}
+        line["sweep"] = [{k: r[k] for k in ("workload", "M", "us_per_call", "us_per_call_graph", "per_call_stats",
+                                            "tokens_per_s", "op_roofline_frac", "op_hbm_frac", "op_mfma_frac",
+                                            "kernels_us")}
                          for r in sweep]
     if entries:
         line["entries"] = entries

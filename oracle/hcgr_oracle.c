@@ -111,13 +111,15 @@ static int run_tokens(const hcgr_oracle_cfg* cfg, int64_t M, int parts,
         return -2;
     }
     int status = 0;
+    /* nthreads > 0 sets this region's team size only (num_threads clause),
+       so a one-thread call leaves later calls on every core */
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
+    const int team = nthreads > 0 ? nthreads : omp_get_max_threads();
 #else
     (void)nthreads;
 #endif
 
-#pragma omp parallel
+#pragma omp parallel num_threads(team)
     {
         double* iw = (double*)malloc(sizeof(double) * HC);
         double* r2 = (double*)malloc(sizeof(double) * K);

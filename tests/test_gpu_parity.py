@@ -123,29 +123,52 @@ def test_decode_m32(op, weights):
     check_all(gpu_forward(op, inp), run_oracle(inp))
 
 
-@pytest.mark.parametrize("M", [1, 7, 32, 100, 1024, 3000, 8192])
+def tile_rows(M, tile=128, seed=3):
+    """One row drawn from every `tile`-token tile of M (the last tile ragged),
+    plus both ends of the first and last tiles."""
+    rng = np.random.default_rng(seed)
+    starts = np.arange(0, M, tile)
+    ends = np.minimum(starts + tile, M)
+    rows = {int(rng.integers(a, b)) for a, b in zip(starts, ends)} | {0, min(tile, M) - 1, int(starts[-1]), M - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("M", [1, 7, 32, 100, 1024, 3000, 8192, 16384, 65536])
 def test_merged_folded_n336(H, weights, M):
     """Merged 336-row down/inject weight with (1+Wnorm) folded in (the M=1024
     workload; also decode and large M, where the folded path has no other
-    coverage)."""
+    coverage). From 8192 tokens: one row of every 128-token tile."""
     _say(f"[parity] merged M={M}")
     o = H.HCGR(H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336), 0)
     inp = synth.make_inputs(M, SHAPE, seed=0, device="cuda", weights=weights)
     inp["wm"] = synth.fold_merged_weight(inp["wd"], inp["wi"], inp["wnorm"], 336, SHAPE.hs)
     out = gpu_forward(o, inp, wd=inp["wm"], wi=None)
-    rows = None if M <= 1024 else sample_rows(M)
+    rows = None if M <= 1024 else sample_rows(M) if M < 8192 else tile_rows(M)
     check_all(out, run_oracle(inp, rows, merged=True, n_pad=336, wd_key="wm"), rows)
     o.close()
 
 
+def test_prefill_m65536_every_tile(op, weights):
+    """The M=65536 workload in the configuration the benchmark times: one row
+    of every 128-token tile (the down kernel's tile-to-XCD grouping and the
+    up kernel's channel ranges both index by tile) against the oracle."""
+    M = 65536
+    _say(f"[parity] every tile M={M}")
+    inp = synth.make_inputs(M, SHAPE, seed=0, device="cuda", weights=weights)
+    out = gpu_forward(op, inp)
+    rows = tile_rows(M)
+    assert len(rows) >= 512
+    check_all(out, run_oracle(inp, rows), rows)
+
+
 def test_prefill_m8192_stream0_x8(op, weights):
-    """M=8192 with stream 0 of R scaled by 8 (per-stream RMS range)."""
+    """M=8192 with stream 0 of R scaled by 8 (per-stream RMS range), every row."""
+    _say("[parity] M=8192 stream 0 x8, every row")
     inp = synth.make_inputs(8192, SHAPE, seed=0, device="cuda", weights=weights, scale_stream0=8.0)
     out = gpu_forward(op, inp)
-    rows = sample_rows(8192, 128)
-    ref = run_oracle(inp, rows)
-    check_all(out, ref, rows)
-    r = to64(out["rrms"][torch.as_tensor(rows, device="cuda")])
+    ref = run_oracle(inp)
+    check_all(out, ref)
+    r = to64(out["rrms"])
     assert np.all(r[:, 0] < r[:, 1:].min(axis=1))
 
 
