@@ -288,11 +288,12 @@ static void describe(const hcgr::Shape& s, const hcgr::Plan& p, int64_t M, char*
       hcgr::K2Shape b = hcgr::k2_shape(p.k2);
       snprintf(buf, len,
                "M=%lld plan=split mpad=%lld | k1_dec tm=%d row_blocks=%d k_waves=%d k_chunk=%d chunks=%d n_tiles=%d "
-               "grid=%dx%lld | k1_reduce waves=%lld | k2_dec tm=%d waves=%d channels=%d grid=%dx%lld | "
+               "grid=%dx%lld | k1_reduce waves=%lld | %s tm=%d waves=%d channels=%d grid=%dx%lld | "
                "workspace=%zu",
                (long long)M, (long long)p.mpad, a.tm, a.rb, a.kw, p.kc, p.nkc, p.ntiles_n, p.ntiles_n * p.nkc,
-               (long long)(p.mpad / p.tm), (long long)(s.n_rows() * (p.mpad / 16)), b.tm, b.nw, p.cb,
-               s.hs / p.cb, (long long)hcgr::cdiv(M, (int64_t)b.tm), p.ws_bytes);
+               (long long)(p.mpad / p.tm), (long long)(s.n_rows() * (p.mpad / 16)), s.hc == 4 ? "k2_dec" : "k2_decg",
+               b.tm, s.hc == 4 ? b.nw : hcgr::decg_waves(s.hc), p.cb, s.hs / p.cb,
+               (long long)hcgr::cdiv(M, (int64_t)b.tm), p.ws_bytes);
     } else if (p.kind == hcgr::PLAN_TILE) {
       hcgr::KTShape t = hcgr::kt_shape(p.kt);
       snprintf(buf, len,

@@ -606,6 +606,12 @@ static hipError_t set_decode_lds() {
   return e;
 }
 
+template <int HC>
+static hipError_t set_decg64_lds() {
+  return hipFuncSetAttribute((const void*)hcgr_k2_decg<HC, 64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)kLdsPerCu);
+}
+
 int configure_decode_kernels() {
   hipError_t e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k1_fuse<16>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -617,7 +623,29 @@ int configure_decode_kernels() {
       (e = set_decode_lds<4, 16>()) != hipSuccess || (e = set_decode_lds<4, 32>()) != hipSuccess ||
       (e = set_decode_lds<8, 16>()) != hipSuccess || (e = set_decode_lds<8, 32>()) != hipSuccess)
     return (int)e;
+  // 64-token tiles of the up kernel (the split plan's 64-token down tiles)
+  if ((e = set_decg64_lds<1>()) != hipSuccess || (e = set_decg64_lds<2>()) != hipSuccess ||
+      (e = set_decg64_lds<4>()) != hipSuccess || (e = set_decg64_lds<8>()) != hipSuccess)
+    return (int)e;
   return (int)hipSuccess;
+}
+
+template <int TM>
+static void launch_decg(int hc, const DecUpArgs& u, dim3 g, size_t lds, hipStream_t st, const hipEvent_t* ev);
+
+int launch_decg_up(const Shape& s, int tm, const uint16_t* H, const ForwardArgs& f, void* stream, void* const* events) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(events);
+  DecUpArgs u;
+  u.h = H; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = (int)s.k(); u.wu = f.wu; u.R2 = f.res; u.rrms = f.rrms;
+  u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0; u.x = f.x;
+  u.hdone = u.exitc = u.err = nullptr; u.need = 0;
+  const dim3 g((unsigned)(s.hs / decg_channels(s.hc)), (unsigned)cdiv(f.M, (int64_t)tm));
+  const size_t lds = k2_decg_lds(s.hc, tm, s.r);
+  if (tm == 16) launch_decg<16>(s.hc, u, g, lds, st, ev);
+  else if (tm == 32) launch_decg<32>(s.hc, u, g, lds, st, ev);
+  else launch_decg<64>(s.hc, u, g, lds, st, ev);
+  return (int)hipGetLastError();
 }
 
 template <int TM>

@@ -36,10 +36,14 @@
 //                         h and Wu staged through LDS by direct global->LDS
 //                         loads, R2 and rrms in registers, and the sigmoid +
 //                         MIX epilogue in registers
-//   Stream counts other than 4 (HC = 1, 2, 8) take the TILE plan at every M
-//   with one stream per down workgroup, hcgr_k1_sum over the HC stream
+//   Stream counts other than 4 (HC = 1, 2, 8) take the SPLIT plan at decode
+//   sizes with the reduction over HC streams and the decode up kernel
+//   hcgr_k2_decg (16/HC channels x HC streams per MFMA block), then the TILE
+//   plan with one stream per down workgroup, hcgr_k1_sum over the HC stream
 //   partials, and K2 hcgr_k2_gen: 64 tokens x 32 channels x HC streams, one
 //   16-row MFMA block per stream so that MIX stays lane-local.
+//   FUSED and PERSISTENT (decode sizes, any HC; tuned-table choices): see
+//   make_fused.
 #pragma once
 
 #include <stddef.h>
@@ -90,6 +94,22 @@ inline size_t k2_dec_lds(int tm, int r) {
          (size_t)(tm > 64 ? tm : 64) * 16 + 1024;
 }
 constexpr size_t kLdsPerCu = 160 * 1024;
+// Decode up kernel for HC streams: a wave's 16 MFMA rows are 16/HC channels x
+// HC streams; NW waves per workgroup (HC waves up to 4 in the fused plan's up
+// kernel, 4 in the persistent plan).
+inline int decg_waves(int hc) { return hc < 4 ? hc : 4; }
+inline int decg_channels(int hc, int nw) { return nw * (16 / hc); }
+inline int decg_channels(int hc) { return decg_channels(hc, decg_waves(hc)); }
+// Its LDS: Wu rows and the h tile, then the tile's R2 rows of its channels,
+// rrms and Wnorm (each rounded up to whole 1 KB direct-load instructions) and
+// a flag word.
+inline size_t k2_decg_lds(int hc, int tm, int r, int nw) {
+  const size_t cw = (size_t)decg_channels(hc, nw);
+  auto kb = [](size_t b) { return (b + 1023) / 1024 * 1024; };
+  return (size_t)(nw * 16 + tm) * (size_t)r * 2u + kb((size_t)tm * hc * cw * 2) + kb((size_t)tm * hc * 4) +
+         kb((size_t)hc * cw * 2) + 16;
+}
+inline size_t k2_decg_lds(int hc, int tm, int r) { return k2_decg_lds(hc, tm, r, decg_waves(hc)); }
 // The reduction kernel gives each of a wave's 4 lane groups up to kRedMaxCpl
 // chunks per stream (instantiated: 1, 2, 3, 5, 8).
 constexpr int kRedMaxCpl = 8;
@@ -197,7 +217,9 @@ inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
   // workgroup per CU for its LDS, is 1 us slower than four 32-token ones,
   // while the 128-token down tile is 1.2 us faster than four 32-token ones)
   const int k2 = d.tm == 16 ? K2_T16 : d.tm == 64 ? K2_T64S : K2_T32;
-  if (s.hs % d.kc != 0 || s.hs / d.kc > 4 * kRedMaxCpl || k2_dec_lds(k2_shape(k2).tm, s.r) > kLdsPerCu) return false;
+  const int tm2 = k2_shape(k2).tm;
+  const size_t lds2 = s.hc == 4 ? k2_dec_lds(tm2, s.r) : k2_decg_lds(s.hc, tm2, s.r);
+  if (s.hs % d.kc != 0 || s.hs / d.kc > 4 * kRedMaxCpl || lds2 > kLdsPerCu) return false;
   Plan p;
   p.M = M;
   p.kind = PLAN_SPLIT;
@@ -208,7 +230,7 @@ inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
   p.kcps = s.hs / d.kc;
   p.nkc = s.hc * p.kcps;
   p.ntiles_n = (s.nblk() + d.rb - 1) / d.rb;
-  p.cb = k2_shape(p.k2).nw * 4;
+  p.cb = s.hc == 4 ? k2_shape(p.k2).nw * 4 : decg_channels(s.hc);  // up-kernel channels per workgroup
   p.mpad = (M + p.tm - 1) / p.tm * p.tm;
   const size_t np = (size_t)s.np();
   p.off_p = kCtrBytes;
@@ -234,22 +256,6 @@ inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
 // weight rows of one chunk for 32 tokens).
 constexpr int kFuseUmax = 7;
 constexpr int kFuseTarget = 256;  // workgroups per token tile the chunk count aims at
-// Decode up kernel for HC streams: a wave's 16 MFMA rows are 16/HC channels x
-// HC streams; NW waves per workgroup (HC waves up to 4 in the fused plan's up
-// kernel, 4 in the persistent plan).
-inline int decg_waves(int hc) { return hc < 4 ? hc : 4; }
-inline int decg_channels(int hc, int nw) { return nw * (16 / hc); }
-inline int decg_channels(int hc) { return decg_channels(hc, decg_waves(hc)); }
-// Its LDS: Wu rows and the h tile, then the tile's R2 rows of its channels,
-// rrms and Wnorm (each rounded up to whole 1 KB direct-load instructions) and
-// a flag word.
-inline size_t k2_decg_lds(int hc, int tm, int r, int nw) {
-  const size_t cw = (size_t)decg_channels(hc, nw);
-  auto kb = [](size_t b) { return (b + 1023) / 1024 * 1024; };
-  return (size_t)(nw * 16 + tm) * (size_t)r * 2u + kb((size_t)tm * hc * cw * 2) + kb((size_t)tm * hc * 4) +
-         kb((size_t)hc * cw * 2) + 16;
-}
-inline size_t k2_decg_lds(int hc, int tm, int r) { return k2_decg_lds(hc, tm, r, decg_waves(hc)); }
 inline size_t k1_fuse_lds(int tm) {
   const size_t row = (size_t)kFuseUmax * 128 * 2;  // bytes of one chunk row
   return (size_t)(2 * tm + 16) * row + 2048 + (size_t)tm * 12;  // R, y, weights, Wnorm slot, iw and sums
@@ -362,17 +368,27 @@ inline Plan make_plan(const Shape& s, int64_t M) {
   if (M <= 0) return p;
   const int hs = s.hs;
   const size_t np = (size_t)s.np();
-  // decode sizes with one or two streams: the fused plan (two kernels).
-  // Measured on MI355X (HS, r = 2560, 320; cold buffers): HC = 1 11.8-14.4 us
-  // at M = 1..32 against 18.2-21.9 for the tile plan, HC = 2 12.9-15.8 against
-  // 21.3-23.4. With four streams the split plan's three kernels stay faster
-  // (12.8 and 14.6 us at M = 1 and 32 against 14.4 and 19.4), and with eight
-  // the tile plan (28.6 against 37.5 us at M = 32): both spread a stream's
-  // weight rows over more workgroups than one 16-row block per chunk.
-  if (M <= kFusedMaxM && (s.hc == 1 || s.hc == 2) && make_fused(s, M, M <= 16 ? 16 : 32, &p)) return p;
-  // stream counts other than 4 (1, 2 or 8) take the tile plan above that:
-  // one stream per down workgroup, the stream sum, and hcgr_k2_gen
+  // stream counts other than 4 (1, 2 or 8) take the split plan with the
+  // stream-generic reduction and decode up kernel up to the split limit, then
+  // the tile plan: one stream per down workgroup, the stream sum, hcgr_k2_gen
   const bool generic = s.hc != 4;
+  if (M <= split_max(s.k(), s.np()) && generic) {
+    // down-kernel variant by K, measured on MI355X at HS, r = 2560, 320 (cold
+    // buffers): up to 40 128-column chunks (HC = 1, 2) 16-token tiles of
+    // 7-row blocks up to 64 tokens (HC = 1: 10.8-12.0 us at M = 1..64, against
+    // 11.8-14.6 for the fused plan and 23.6 for the tile plan at 64; HC = 2:
+    // 11.8-14.4 us), then 32-token tiles (13.9 and 17.2 us at 128); from 160
+    // chunks (HC = 8) 512-column chunks: one row block with four k waves at
+    // M <= 8 (17.8 us), 3-row blocks with two k waves above (18.9 us at 16,
+    // 22.7 at 32 on 32-token tiles, 29.2 at 64, against 26.1, 26.8, 28.8 and
+    // 32.5 for the tile plan)
+    const int64_t c128 = s.k() / 128;
+    int kd;
+    if (c128 <= 40) kd = M <= 64 ? KD_T16_R7_K1_C128 : KD_T32_R7_K1_C128;
+    else if (c128 >= 160) kd = M <= 8 ? KD_T16_R1_K4_C512 : M <= 16 ? KD_T16_R3_K2_C512 : KD_T32_R3_K2_C512;
+    else kd = M <= 16 ? KD_T16_R7_K1_C128 : KD_T32_R7_K1_C128;
+    if (make_split(s, M, kd, &p) || make_split(s, M, M <= 16 ? KD_T16_R3_K2_C512 : KD_T32_R3_K2_C512, &p)) return p;
+  }
   if (M <= split_max(s.k(), s.np()) && !generic) {
     // above 16 tokens: 32-token down tiles (they pad M to 32, not 64); at
     // every M, 3-row blocks where those leave fewer padded 16-row blocks than
@@ -515,7 +531,7 @@ struct TableEntry {
 
 inline bool plan_from_choice(const Shape& s, int64_t M, const Choice& c, Plan* out) {
   if (c.kind == PLAN_SPLIT)
-    return s.hc == 4 && M >= 1 && M <= kSplitChoiceMaxM && c.kd >= 0 && c.kd < KD_NVAR && make_split(s, M, c.kd, out);
+    return M >= 1 && M <= kSplitChoiceMaxM && c.kd >= 0 && c.kd < KD_NVAR && make_split(s, M, c.kd, out);
   if (c.kind == PLAN_TILE)
     return (c.kd == 0 || c.kd == 1) && make_tile(s, M, c.spw, c.nseg, c.kt, c.nranges, out, c.kd ? 128 : 64);
   if (c.kind == PLAN_FUSED || c.kind == PLAN_PERSIST)
@@ -654,6 +670,9 @@ int configure_decode_kernels();
 // Enqueues the fused or persistent decode plan (hcgr_decode.hip); events as
 // launch_forward (the persistent plan's one kernel is stage 0).
 int launch_fused(const Shape& s, const Plan& p, const ForwardArgs& a, void* stream, void* const* events);
+// Enqueues the stream-generic decode up kernel over token tiles of tm (16,
+// 32 or 64) reading h from H; events: null or a (start, end) pair.
+int launch_decg_up(const Shape& s, int tm, const uint16_t* H, const ForwardArgs& a, void* stream, void* const* events);
 
 // Enqueues the plan's kernels on `stream`; returns the hipError_t of the
 // launches. With `events` (6 hipEvent_t) events[2i] and events[2i+1] mark the

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(RB * KW * 64) void hcgr_k1_dec(DownArgs a) {
 // inject rows -> inj_next (bf16). One wave per (row n, 16 tokens): lane
 // l handles token l % 16 and every 4th chunk starting at l / 16; all of a
 // lane's loads are issued before the first add (one memory round trip), and
-// the four lane groups are then summed with cross-lane adds. HC = 4.
+// the four lane groups are then summed with cross-lane adds. HC streams.
 // ---------------------------------------------------------------------------
 struct ReduceArgs {
   const float* P;
@@ -238,7 +238,7 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
   return v;
 }
 
-template <int CPL>
+template <int HC, int CPL>
 __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -248,9 +248,9 @@ __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
   const int64_t m = (wid % mblocks) * 16 + (lane & 15);
   const int g = lane >> 4;
   const int kcps = a.kcps;  // <= 4 * CPL
-  float sv[4][CPL], pv[4][CPL];
+  float sv[HC][CPL], pv[HC][CPL];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < HC; ++s)
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = g + 4 * i;
@@ -260,9 +260,9 @@ __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
       sv[s][i] = c < kcps ? sl : 0.0f;
       pv[s][i] = c < kcps ? pl : 0.0f;
     }
-  float ss[4], ps[4];
+  float ss[HC], ps[HC];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < HC; ++s) {
     float t = 0.0f, u = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
@@ -273,16 +273,16 @@ __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
     ps[s] = u;
   }
   float v = 0.0f;
-  float rr[4];
+  float rr[HC];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < HC; ++s) {
     rr[s] = 1.0f / sqrtf(sum_lane_groups(ss[s]) * a.inv_hs + a.eps);
     v = fmaf(rr[s], sum_lane_groups(ps[s]), v);
   }
   if (g != 0) return;
   if (n == 0 && m < a.M) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) a.rrms[m * 4 + s] = rr[s];
+    for (int s = 0; s < HC; ++s) a.rrms[m * HC + s] = rr[s];
   }
   if (n < a.r) {
     const float z = v * a.inv_hc;
@@ -2102,13 +2102,22 @@ static void launch_kd_variant(int v, const DownArgs& d, dim3 grid, hipStream_t s
     default: launch_kd<64, 3, 1, 256>(d, grid, st, ev); break;
   }
 }
-static void launch_reduce(int cpl, const ReduceArgs& r, dim3 grid, hipStream_t st, const hipEvent_t* ev = nullptr) {
+template <int HC>
+static void launch_reduce_hc(int cpl, const ReduceArgs& r, dim3 grid, hipStream_t st, const hipEvent_t* ev) {
   switch (cpl) {
-    case 1: klaunch(hcgr_k1_reduce<1>, grid, dim3(256), 0, st, ev, r); break;
-    case 2: klaunch(hcgr_k1_reduce<2>, grid, dim3(256), 0, st, ev, r); break;
-    case 3: klaunch(hcgr_k1_reduce<3>, grid, dim3(256), 0, st, ev, r); break;
-    case 5: klaunch(hcgr_k1_reduce<5>, grid, dim3(256), 0, st, ev, r); break;
-    default: klaunch(hcgr_k1_reduce<8>, grid, dim3(256), 0, st, ev, r); break;
+    case 1: klaunch(hcgr_k1_reduce<HC, 1>, grid, dim3(256), 0, st, ev, r); break;
+    case 2: klaunch(hcgr_k1_reduce<HC, 2>, grid, dim3(256), 0, st, ev, r); break;
+    case 3: klaunch(hcgr_k1_reduce<HC, 3>, grid, dim3(256), 0, st, ev, r); break;
+    case 5: klaunch(hcgr_k1_reduce<HC, 5>, grid, dim3(256), 0, st, ev, r); break;
+    default: klaunch(hcgr_k1_reduce<HC, 8>, grid, dim3(256), 0, st, ev, r); break;
+  }
+}
+static void launch_reduce(int hc, int cpl, const ReduceArgs& r, dim3 grid, hipStream_t st, const hipEvent_t* ev = nullptr) {
+  switch (hc) {
+    case 1: launch_reduce_hc<1>(cpl, r, grid, st, ev); break;
+    case 2: launch_reduce_hc<2>(cpl, r, grid, st, ev); break;
+    case 8: launch_reduce_hc<8>(cpl, r, grid, st, ev); break;
+    default: launch_reduce_hc<4>(cpl, r, grid, st, ev); break;
   }
 }
 template <int TM, int NW, int BPW, int KS>
@@ -2165,8 +2174,10 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   r.eps = s.eps; r.inv_hc = 1.0f / (float)s.hc; r.inv_hs = 1.0f / (float)s.hs;
   r.rrms = f.rrms; r.h = H; r.inj_next = f.inj_next; r.ld_inj_next = f.ld_inj_next;
   const int64_t waves = (int64_t)s.n_rows() * (p.mpad / 16);
-  launch_reduce(red_cpl(p.kcps), r, dim3((unsigned)((waves + 3) / 4)), st, tm.stage(1));
+  launch_reduce(s.hc, red_cpl(p.kcps), r, dim3((unsigned)((waves + 3) / 4)), st, tm.stage(1));
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  if (s.hc != 4)  // the stream-generic decode up kernel
+    return launch_decg_up(s, k2_shape(p.k2).tm, H, f, st, reinterpret_cast<void* const*>(tm.stage(2)));
 
   UpArgs u;
   u.h = H; u.Mpad = p.mpad; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = K;

@@ -161,19 +161,19 @@ def test_config_errors(lib, kw, st):
 
 @pytest.mark.parametrize("hc", [1, 2, 8])
 def test_other_stream_counts(lib, hc):
-    """HC = 1, 2 and 8 are accepted; with one or two streams the plan is the
-    fused decode plan up to 32 tokens (last-arrival reduction, the HC-generic
-    decode up kernel), otherwise the tile plan (one stream per down
-    workgroup, the stream sum, the HC-generic up kernel); one workspace sized
-    for the largest M serves every smaller one."""
+    """HC = 1, 2 and 8 are accepted; their plan is the split plan at decode
+    sizes (the reduction over HC streams, the HC-generic decode up kernel),
+    then the tile plan (one stream per down workgroup, the stream sum, the
+    HC-generic up kernel); one workspace sized for the largest M serves every
+    smaller one."""
     cfg = H.Config(hc=hc)
     for M in (1, 5, 32, 33, 64, 65, 1000, 8192):
         assert Layout(cfg, M).call() == H.HCGR_OK
         L = Layout(cfg, M)
         assert _mix(L) == H.HCGR_OK and _combine(L) == H.HCGR_OK
         d = H.hcgr_describe_plan(cfg, M)
-        if M <= 32 and hc in (1, 2):
-            assert "plan=fused" in d and "k2_decg" in d, d
+        if M <= (94 if hc == 8 else 256):  # the split limit: M x K x padded rows < 6.5e8
+            assert "plan=split" in d and "k2_decg" in d, d
         else:
             assert "plan=tile" in d and "k1_sum" in d and "k2_gen" in d, d
     for hs, r in ((2560, 320), (256, 96), (1024, 512)):

@@ -216,12 +216,34 @@ def test_decode_plans_interleaved_stress(H, kind):
         ops[M].close()
 
 
-def test_fused_is_the_decode_heuristic_for_one_and_two_streams(H):
-    """The heuristic plan at decode sizes with HC = 1 and 2 is the fused plan,
-    and it matches the oracle there (HC = 1, M = 32; HC = 2, M = 3)."""
-    for hc, M in ((1, 32), (2, 3)):
+@pytest.mark.parametrize("hc", [1, 2, 8])
+@pytest.mark.parametrize("kd", list(range(11)))
+def test_split_plan_other_stream_counts(H, hc, kd):
+    """The split plan at HC = 1, 2, 8 (the reduction over HC streams, the
+    stream-generic decode up kernel over 16-, 32- and 64-token tiles): every
+    down-kernel variant, every row, at a ragged token count and one past a
+    token tile."""
+    cfg = H.Config(hc=hc)
+    for M in (3, 33):
+        op = H.HCGR(cfg, 0, plan_table=[{"tokens": M, "kind": 0, "down_variant": kd}])
+        d = op.describe(M)
+        if "plan=split" not in d:  # this variant cannot split the stream width
+            op.close()
+            continue
+        _say(f"[split] hc={hc} {d[:100]}")
+        inp = synth.make_inputs(M, synth.Shape(hc, 2560, 320), seed=kd + M, device="cuda")
+        out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"])
+        torch.cuda.synchronize()
+        check_all(out, oracle_forward(oracle.OracleConfig(hc=hc), inp))
+        op.close()
+
+
+def test_split_is_the_decode_heuristic_for_other_stream_counts(H):
+    """The heuristic plan at decode sizes with HC = 1, 2, 8 is the split plan
+    with the stream-generic kernels, matching the oracle."""
+    for hc, M in ((1, 32), (2, 3), (8, 17)):
         cfg = H.Config(hc=hc)
-        assert "plan=fused" in H.hcgr_describe_plan(cfg, M)
+        assert "plan=split" in H.hcgr_describe_plan(cfg, M)
         op = H.HCGR(cfg, 0)
         inp = synth.make_inputs(M, synth.Shape(hc, 2560, 320), seed=70, device="cuda")
         out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"])

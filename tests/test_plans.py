@@ -43,7 +43,7 @@ def test_every_candidate_is_a_valid_one_entry_table(lib, cfg, M):
     assert cands, (cfg, M)
     kinds = {c["kind"] for c in cands}
     assert H.HCGR_PLAN_TILE in kinds
-    assert (H.HCGR_PLAN_SPLIT in kinds) == (cfg.hc == 4 and M <= 256)
+    assert (H.HCGR_PLAN_SPLIT in kinds) == (M <= 256)
     for c in cands:
         assert c["tokens"] == M
         chosen, desc = H.hcgr_plan_lookup(cfg, [c], M)
@@ -98,7 +98,8 @@ def test_malformed_tables_are_rejected(lib, table):
 
 def test_other_stream_counts_reject_four_stream_choices(lib):
     c2 = H.Config(hc=2)
-    for bad in ([tile(64, spw=4)], [tile(64, up=0)], [split(16, 0)]):
+    assert H.hcgr_plan_lookup(c2, [split(16, 0)], 16)[0]["kind"] == H.HCGR_PLAN_SPLIT
+    for bad in ([tile(64, spw=4)], [tile(64, up=0)]):
         with pytest.raises(H.HcgrError):
             H.hcgr_plan_lookup(c2, bad, 64)
     assert H.hcgr_plan_lookup(c2, [tile(64, seg=5, up=2)], 64)[0]["segments"] == 5
@@ -157,13 +158,13 @@ def test_workspace_bound_covers_every_smaller_plan(lib, hc, hs, r):
 
 
 def test_workspace_keeps_the_counter_bytes(lib):
-    """Every plan's data starts past the counter bytes, and the fused plan is
-    the heuristic at decode sizes with one or two streams."""
+    """Every plan's data starts past the counter bytes; the fused and
+    persistent decode plans are tuned-table choices at every stream count."""
     for hc in (1, 2, 4, 8):
         cfg = H.Config(hc=hc)
         for M in (1, 16, 17, 32, 33, 100, 5000):
             d = H.hcgr_describe_plan(cfg, M)
-            assert ("plan=fused" in d) == (hc in (1, 2) and M <= 32), d
+            assert "plan=fused" not in d, d
             assert ws_of(d) > H.HCGR_WORKSPACE_COUNTER_BYTES
             for kind in (H.HCGR_PLAN_FUSED, H.HCGR_PLAN_PERSISTENT):
                 if M <= 256:
