@@ -78,7 +78,7 @@ def kernel_bytes(name, M, merged=False, plan=""):
         return wdown + M * (act_in + out)
     if name == "hcgr_k1_sum":
         return M * HC * 2                       # inj_next out
-    if name in ("hcgr_k2_dec", "hcgr_k2_decg", "hcgr_k2_stage", "hcgr_k2_sweep"):
+    if name in ("hcgr_k2_dec", "hcgr_k2_decg", "hcgr_k2_stage", "hcgr_k2_sweep", "hcgr_k2_sweep2"):
         return K * R_LOW * 2 + HS * 2 + M * (K * 2 + HC * 4 + HS * 2)  # Wu, Wnorm; R2, rrms in; x out
     raise KeyError(name)
 
@@ -88,7 +88,7 @@ def kernel_flops(name, M):
         return M * 2 * (R_LOW + HC) * K
     if name == "hcgr_dec_persist":
         return op_flops(M)
-    if name in ("hcgr_k2_dec", "hcgr_k2_decg", "hcgr_k2_stage", "hcgr_k2_sweep"):
+    if name in ("hcgr_k2_dec", "hcgr_k2_decg", "hcgr_k2_stage", "hcgr_k2_sweep", "hcgr_k2_sweep2"):
         return M * 2 * R_LOW * K
     return 0
 
@@ -102,7 +102,8 @@ def stage_names(plan: str):
         return ("hcgr_dec_persist", None, None)
     if "plan=split" in plan:
         return ("hcgr_k1_dec", "hcgr_k1_reduce", "hcgr_k2_dec")
-    up = "hcgr_k2_sweep" if "k2_sweep" in plan else "hcgr_k2_gen" if "k2_gen" in plan else "hcgr_k2_stage"
+    up = ("hcgr_k2_sweep2" if "k2_sweep2" in plan else "hcgr_k2_sweep" if "k2_sweep" in plan else
+          "hcgr_k2_gen" if "k2_gen" in plan else "hcgr_k2_stage")
     if "plan=tile" in plan:
         return ("hcgr_k1_tile", "hcgr_k1_sum" if "streams/wg=1" in plan else None, up)
     if "plan=stream" in plan:

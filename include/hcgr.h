@@ -289,8 +289,9 @@ typedef struct hcgr_plan_choice {
                                a divisor of HS/128 (1 with 4 streams per workgroup)                  */
     int32_t up_variant;     /* TILE: 0 staged (HC = 4), 1 sweep (HC = 4, 96 <= r <= 320),
                                2 stream-generic (HC != 4), 3 stream-generic over 128-token tiles
-                               (HC = 2 or 8)                                                         */
-    int32_t ranges;         /* TILE with the sweep: channel ranges per token tile, 1 .. HS/32;
+                               (HC = 2 or 8), 4 sweep over 256-token tiles (HC = 4,
+                               96 <= r <= 320)                                                       */
+    int32_t ranges;         /* TILE with a sweep: channel ranges per token tile, 1 .. HS/32;
                                1 otherwise                                                           */
 } hcgr_plan_choice;
 

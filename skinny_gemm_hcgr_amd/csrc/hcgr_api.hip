@@ -186,7 +186,7 @@ bool to_choice(const hcgr_plan_choice& c, hcgr::Choice* out) {
   x.kd = c.down_variant;
   x.spw = c.streams_per_wg;
   x.nseg = c.segments;
-  x.kt = c.up_variant;  // 0 staged, 1 sweep, 2 generic, 3 generic over 128 tokens: the planner's KT_* values
+  x.kt = c.up_variant;  // 0 staged, 1 sweep, 2 generic, 3 generic over 128 tokens, 4 sweep over 256: KT_* values
   x.nranges = c.ranges;
   if (c.kind != HCGR_PLAN_HEURISTIC && c.kind != HCGR_PLAN_SPLIT && c.kind != HCGR_PLAN_TILE &&
       c.kind != HCGR_PLAN_FUSED && c.kind != HCGR_PLAN_PERSISTENT)
@@ -257,12 +257,12 @@ hcgr_status hcgr_workspace_size_for(const hcgr_config* cfg, int64_t M, size_t* b
 }
 
 static const char* k2_name(int kt) {
-  return kt == hcgr::KT_SWEEP ? "k2_sweep" : hcgr::is_gen(kt) ? "k2_gen" : "k2_stage";
+  return kt == hcgr::KT_SWEEP2 ? "k2_sweep2" : kt == hcgr::KT_SWEEP ? "k2_sweep" : hcgr::is_gen(kt) ? "k2_gen" : "k2_stage";
 }
 static long long k2_grid(const hcgr::Shape& s, const hcgr::Plan& p, int64_t M) {
   const hcgr::KTShape t = hcgr::kt_shape(p.kt);
   if (hcgr::is_gen(p.kt)) return (long long)(hcgr::cdiv(M, t.tm) * (s.hs / t.cb));
-  if (p.kt == hcgr::KT_SWEEP) return (long long)(hcgr::cdiv(M, t.tm) * p.nranges);
+  if (hcgr::is_sweep(p.kt)) return (long long)(hcgr::cdiv(M, t.tm) * p.nranges);
   return (long long)(hcgr::cdiv(hcgr::cdiv(M, t.tm) * (s.hs / 64), 8) * 16);
 }
 

@@ -134,12 +134,17 @@ inline KFShape kf_shape(int v) {
 // channels x HC streams per workgroup).
 // KT_GEN128: hcgr_k2_gen over 128-token tiles (HC = 2 or 8: each Wu row read
 // once per 128 tokens instead of 64).
-enum KTVariant { KT_S128 = 0, KT_SWEEP = 1, KT_GEN = 2, KT_GEN128 = 3, KT_NVAR };
+// KT_SWEEP2: hcgr_k2_sweep2 (hcgr_sweep.hip), the sweep over 256-token tiles:
+// each wave owns 32 tokens and every gate row of a group, so a Wu stage
+// feeds twice the products per barrier and is fetched once per 256 tokens.
+constexpr int kSweep2Tm = 256;
+enum KTVariant { KT_S128 = 0, KT_SWEEP = 1, KT_GEN = 2, KT_GEN128 = 3, KT_SWEEP2 = 4, KT_NVAR };
 struct KTShape { int tm, cb; };
 inline KTShape kt_shape(int v) {
-  static const KTShape t[KT_NVAR] = {{128, 32}, {128, 32}, {64, 32}, {128, 32}};
+  static const KTShape t[KT_NVAR] = {{128, 32}, {128, 32}, {64, 32}, {128, 32}, {kSweep2Tm, 32}};
   return t[v];
 }
+inline bool is_sweep(int kt) { return kt == KT_SWEEP || kt == KT_SWEEP2; }
 inline bool is_gen(int kt) { return kt == KT_GEN || kt == KT_GEN128; }
 // hcgr_k2_sweep serves 96 <= r <= 320 (2 to 5 k stages of 64) from
 // kSweepMinM tokens, with enough channel ranges per token tile to give
@@ -325,8 +330,8 @@ inline bool make_tile(const Shape& s, int64_t M, int spw, int nseg, int kt, int 
   if (spw != 1 && !(spw == 4 && !generic)) return false;
   if (nseg < 1 || (s.hs / 128) % nseg != 0 || (spw == 4 && nseg != 1)) return false;
   if (generic != is_gen(kt) || (kt == KT_GEN128 && s.hc != 2 && s.hc != 8)) return false;
-  if (kt == KT_SWEEP) {
-    if (!sweep_fits(s.r) || nranges < 1 || nranges > s.hs / kt_shape(KT_SWEEP).cb) return false;
+  if (is_sweep(kt)) {
+    if (!sweep_fits(s.r) || nranges < 1 || nranges > s.hs / kt_shape(kt).cb) return false;
   } else if (kt != KT_S128 && !is_gen(kt)) {
     return false;
   } else if (nranges != 1) {
@@ -563,14 +568,14 @@ inline int plan_choices(const Shape& s, int64_t M, Choice* out, int cap) {
       c.kd = kd;
       add(c);
     }
-  const int ups[4] = {KT_S128, KT_SWEEP, KT_GEN, KT_GEN128};
+  const int ups[5] = {KT_S128, KT_SWEEP, KT_GEN, KT_GEN128, KT_SWEEP2};
   const int pairs = s.hs / 128;
   for (int big = 0; big < 2; ++big)
     for (int spw : {1, 4})
       for (int d = 1; d <= pairs; ++d) {
         if (pairs % d != 0 || (spw == 4 && d != 1)) continue;
         for (int kt : ups)
-          for (int nr = 1; nr <= (kt == KT_SWEEP ? 8 : 1); nr *= 2) {
+          for (int nr = 1; nr <= (is_sweep(kt) ? 8 : 1); nr *= 2) {
             Choice c;
             c.kind = PLAN_TILE;
             c.kd = big;
@@ -670,6 +675,11 @@ int configure_decode_kernels();
 // Enqueues the fused or persistent decode plan (hcgr_decode.hip); events as
 // launch_forward (the persistent plan's one kernel is stage 0).
 int launch_fused(const Shape& s, const Plan& p, const ForwardArgs& a, void* stream, void* const* events);
+// The 256-token sweep up kernel (hcgr_sweep.hip): LDS limits, and its launch
+// reading h from H; events: null or a (start, end) pair.
+int configure_sweep2_kernels();
+int launch_sweep2(const Shape& s, const Plan& p, const ForwardArgs& a, const uint16_t* H, void* stream,
+                  void* const* events);
 // Enqueues the stream-generic decode up kernel over token tiles of tm (16,
 // 32 or 64) reading h from H; events: null or a (start, end) pair.
 int launch_decg_up(const Shape& s, int tm, const uint16_t* H, const ForwardArgs& a, void* stream, void* const* events);

@@ -2134,6 +2134,7 @@ int configure_kernels() {
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<3>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(3))) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(4))) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<5>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(5))) != hipSuccess) return (int)e;
+  if ((e = (hipError_t)configure_sweep2_kernels()) != hipSuccess) return (int)e;
   return configure_decode_kernels();
 }
 
@@ -2303,6 +2304,8 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
         break;
       default: return (int)hipErrorInvalidValue;  // make_plan takes this kernel for HC = 1, 2, 8 only
     }
+  } else if (p.kt == KT_SWEEP2) {
+    return launch_sweep2(s, p, f, H, st, reinterpret_cast<void* const*>(tm.stage(2)));
   } else if (p.kt == KT_SWEEP) {
     SweepArgs wa;
     wa.h = H; wa.M = f.M; wa.r = s.r; wa.HS = s.hs; wa.K = K; wa.wu = f.wu; wa.R2 = f.res; wa.rrms = f.rrms;

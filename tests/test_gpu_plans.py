@@ -218,3 +218,46 @@ def test_split128_up_tiles(H, weights, M):
     torch.cuda.synchronize()
     check_rows(out, run_oracle(inp), None)
     op.close()
+
+
+@pytest.mark.parametrize("hs,r,M,ranges,extra", [
+    (2560, 320, 300, 1, ""), (2560, 320, 300, 3, ""),        # a partial second tile; ranges of 27/26 groups
+    (2560, 320, 5000, 7, ""), (2560, 320, 65536, 1, ""),     # sampled rows
+    (640, 96, 257, 2, ""), (1024, 192, 700, 32, ""),         # two and three k stages; one group per range
+    (1280, 160, 500, 2, "wnfull"), (2560, 320, 1000, 2, "merged"), (2560, 256, 600, 4, "mix"),
+])
+def test_sweep256_shapes(H, hs, r, M, ranges, extra):
+    """The up kernel over 256-token tiles (up variant 4): partial last tiles,
+    channel ranges down to one 32-channel group, k stages of 64 with a part
+    past r, full-width Wnorm, merged weights and the mix entry point."""
+    shape = synth.Shape(hc=4, hs=hs, r=r)
+    merged = extra == "merged"
+    n_pad = (r + 4 + 15) // 16 * 16
+    cfg = H.Config(hs=hs, r=r, wnorm_len=4 * hs if extra == "wnfull" else 0,
+                   weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED if merged else H.HCGR_WEIGHTS_SEPARATE,
+                   n_pad=n_pad if merged else 0)
+    op = H.HCGR(cfg, 0, plan_table=[_tile128(M, 1, 4, ranges)])
+    desc = op.describe(M)
+    _say(f"[plans] sweep256 {extra} hs={hs} r={r} M={M} ranges={ranges}: {desc}")
+    assert "k2_sweep2" in desc
+    inp = synth.make_inputs(M, shape, seed=40 + M, device="cuda", wnorm_full=extra == "wnfull")
+    wd = synth.fold_merged_weight(inp["wd"], inp["wi"], inp["wnorm"], n_pad, hs) if merged else inp["wd"]
+    wi = None if merged else inp["wi"]
+    ocfg = oracle.OracleConfig(hs=hs, r=r, wnorm_full=extra == "wnfull", merged=merged, n_pad=n_pad if merged else 0)
+    rows = None if M <= 1000 else sample_rows(M, n=64)
+    sel = (lambda t: t) if rows is None else (lambda t: t[torch.as_tensor(rows, device="cuda")])
+    if extra == "mix":
+        out = op.mix(inp["R"], inp["wnorm"], wd, wi, inp["wu"])
+        torch.cuda.synchronize()
+        ref = oracle.mix(ocfg, sel(inp["R"]).cpu(), inp["wnorm"].cpu(), wd.cpu(), wi.cpu(), inp["wu"].cpu())
+        from parity import check_rrms, check_tol
+        check_rrms(sel(out["rrms"]), ref["rrms"])
+        check_tol(sel(out["inj_next"]), ref["inj_next"], "inj_next")
+        check_tol(sel(out["x"]), ref["x"], "x")
+    else:
+        out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], wd, wi, inp["wu"])
+        torch.cuda.synchronize()
+        ref = oracle.forward(ocfg, sel(inp["R"]).cpu(), sel(inp["y"]).cpu(), sel(inp["inj"]).cpu(),
+                             inp["wnorm"].cpu(), wd.cpu(), None if merged else wi.cpu(), inp["wu"].cpu())
+        check_rows(out, ref, rows)
+    op.close()
