@@ -135,8 +135,9 @@ inline KFShape kf_shape(int v) {
 // KT_GEN128: hcgr_k2_gen over 128-token tiles (HC = 2 or 8: each Wu row read
 // once per 128 tokens instead of 64).
 // KT_SWEEP2: hcgr_k2_sweep2 (hcgr_sweep.hip), the sweep over 256-token tiles:
-// each wave owns 32 tokens and every gate row of a group, so a Wu stage
-// feeds twice the products per barrier and is fetched once per 256 tokens.
+// each wave owns 32 tokens and every gate row; Wu streams in 16-row blocks
+// over the whole of k (fetched once per 256 tokens), and each block's
+// sigmoid + MIX runs beside the next block's products.
 constexpr int kSweep2Tm = 256;
 enum KTVariant { KT_S128 = 0, KT_SWEEP = 1, KT_GEN = 2, KT_GEN128 = 3, KT_SWEEP2 = 4, KT_NVAR };
 struct KTShape { int tm, cb; };
@@ -164,6 +165,18 @@ struct Shape {
   int nblk() const { return (n_rows() + 15) / 16; } // 16-row MFMA blocks
   int np() const { return nblk() * 16; }
 };
+
+// hcgr_k2_sweep2 channel ranges hold whole pairs of 32-channel groups (at
+// most one range per pair). LDS: a ring of kSweep2Ring Wu stages (4 blocks of
+// 16 rows x NC chunks of 64 k, 2 KB per chunk) and 0.25 (1 + Wnorm) of a
+// channel range as f32 (four per channel for a full-width Wnorm).
+constexpr int kSweep2Ring = 3;
+inline int sweep2_pairs(const Shape& s) { return s.hs / 64; }
+inline constexpr size_t sweep2_stage_bytes(int nc) { return (size_t)4 * nc * 2048; }
+inline size_t sweep2_lds(const Shape& s, int nranges) {
+  const int np = sweep2_pairs(s), gmax = 2 * ((np + nranges - 1) / nranges);
+  return kSweep2Ring * sweep2_stage_bytes(sweep_nks(s.r)) + (size_t)gmax * 32 * (s.wn_full ? 16 : 4);
+}
 
 struct Plan {
   int64_t M = 0, mpad = 0;
@@ -332,6 +345,7 @@ inline bool make_tile(const Shape& s, int64_t M, int spw, int nseg, int kt, int 
   if (generic != is_gen(kt) || (kt == KT_GEN128 && s.hc != 2 && s.hc != 8)) return false;
   if (is_sweep(kt)) {
     if (!sweep_fits(s.r) || nranges < 1 || nranges > s.hs / kt_shape(kt).cb) return false;
+    if (kt == KT_SWEEP2 && (nranges > sweep2_pairs(s) || sweep2_lds(s, nranges) > kLdsPerCu)) return false;
   } else if (kt != KT_S128 && !is_gen(kt)) {
     return false;
   } else if (nranges != 1) {
@@ -420,11 +434,22 @@ inline Plan make_plan(const Shape& s, int64_t M) {
     // MI355X at HS = 2560, r = 320: 4-6% faster up kernel at M = 1024..32768;
     // with eight streams it was 7-18% slower, one workgroup per CU)
     if (generic && s.hc == 2 && M >= 1024) kt = KT_GEN128;
+    // from kSweepMinM tokens the 256-token sweep, with enough channel ranges
+    // to give every CU a workgroup (measured on MI355X at HS = 2560, r = 320,
+    // against the 128-token sweep: 47 vs 91 us at M = 4096, 87 vs 107 at
+    // 8192, 174 vs 339 at 16384, 626 vs 800 at 65536); the 128-token sweep
+    // where its LDS does not fit (a full-width Wnorm over few ranges)
     if (M >= kSweepMinM && sweep_fits(s.r) && !generic) {
-      kt = KT_SWEEP;
-      const int64_t t2 = cdiv(M, kt_shape(KT_SWEEP).tm);
-      const int ng = hs / kt_shape(KT_SWEEP).cb;
-      nranges = (int)(t2 >= target ? 1 : cdiv(target, t2) < ng ? cdiv(target, t2) : ng);
+      const int64_t t2 = cdiv(M, (int64_t)kSweep2Tm);
+      const int np = sweep2_pairs(s);
+      nranges = (int)(t2 >= target ? 1 : cdiv(target, t2) < np ? cdiv(target, t2) : np);
+      kt = KT_SWEEP2;
+      if (sweep2_lds(s, nranges) > kLdsPerCu) {
+        kt = KT_SWEEP;
+        const int64_t t1 = cdiv(M, kt_shape(KT_SWEEP).tm);
+        const int ng = hs / kt_shape(KT_SWEEP).cb;
+        nranges = (int)(t1 >= target ? 1 : cdiv(target, t1) < ng ? cdiv(target, t1) : ng);
+      }
     }
     // once 128-token down tiles alone give every CU a workgroup (one stream
     // each), take them: they stream each weight stage once per 128 tokens
@@ -575,7 +600,7 @@ inline int plan_choices(const Shape& s, int64_t M, Choice* out, int cap) {
       for (int d = 1; d <= pairs; ++d) {
         if (pairs % d != 0 || (spw == 4 && d != 1)) continue;
         for (int kt : ups)
-          for (int nr = 1; nr <= (is_sweep(kt) ? 8 : 1); nr *= 2) {
+          for (int nr = 1; nr <= (kt == KT_SWEEP2 ? 32 : kt == KT_SWEEP ? 8 : 1); nr *= 2) {
             Choice c;
             c.kind = PLAN_TILE;
             c.kd = big;

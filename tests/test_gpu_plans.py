@@ -223,13 +223,13 @@ def test_split128_up_tiles(H, weights, M):
 @pytest.mark.parametrize("hs,r,M,ranges,extra", [
     (2560, 320, 300, 1, ""), (2560, 320, 300, 3, ""),        # a partial second tile; ranges of 27/26 groups
     (2560, 320, 5000, 7, ""), (2560, 320, 65536, 1, ""),     # sampled rows
-    (640, 96, 257, 2, ""), (1024, 192, 700, 32, ""),         # two and three k stages; one group per range
+    (640, 96, 257, 2, ""), (1024, 192, 700, 16, ""),         # two and three k stages; one pair of groups per range
     (1280, 160, 500, 2, "wnfull"), (2560, 320, 1000, 2, "merged"), (2560, 256, 600, 4, "mix"),
 ])
 def test_sweep256_shapes(H, hs, r, M, ranges, extra):
     """The up kernel over 256-token tiles (up variant 4): partial last tiles,
-    channel ranges down to one 32-channel group, k stages of 64 with a part
-    past r, full-width Wnorm, merged weights and the mix entry point."""
+    channel ranges down to one pair of 32-channel groups, k stages of 64 with
+    a part past r, full-width Wnorm, merged weights and the mix entry point."""
     shape = synth.Shape(hc=4, hs=hs, r=r)
     merged = extra == "merged"
     n_pad = (r + 4 + 15) // 16 * 16
