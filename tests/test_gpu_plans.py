@@ -225,6 +225,9 @@ def test_split128_up_tiles(H, weights, M):
     (2560, 320, 5000, 7, ""), (2560, 320, 65536, 1, ""),     # sampled rows
     (640, 96, 257, 2, ""), (1024, 192, 700, 16, ""),         # two and three k stages; one pair of groups per range
     (1280, 160, 500, 2, "wnfull"), (2560, 320, 1000, 2, "merged"), (2560, 256, 600, 4, "mix"),
+    (2560, 320, 100, 4, ""),                                 # one partial tile
+    (1024, 288, 600, 4, ""),                                 # last k chunk partly past r
+    (2560, 320, 2000, 8, "wnfull"),                          # full-width Wnorm with five k chunks
 ])
 def test_sweep256_shapes(H, hs, r, M, ranges, extra):
     """The up kernel over 256-token tiles (up variant 4): partial last tiles,
