@@ -82,8 +82,9 @@ hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out);
 /* Frees a handle (NULL is allowed). Outstanding work on streams is unaffected. */
 void hcgr_destroy(hcgr_handle h);
 
-/* Bytes at the start of every workspace that hold arrival counters. */
-#define HCGR_WORKSPACE_COUNTER_BYTES 4096
+/* Bytes at the start of every workspace that hold arrival counters (1024
+ * 32-bit counters, each at the start of a 128-byte line of its own). */
+#define HCGR_WORKSPACE_COUNTER_BYTES 131072
 
 /* Bytes of device workspace that serve hcgr_forward for every token count
  * from 1 to M (0 for M == 0), with the handle's tuned table if it has one

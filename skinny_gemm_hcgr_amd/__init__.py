@@ -32,7 +32,7 @@ HCGR_PLAN_SPLIT = 0
 HCGR_PLAN_TILE = 3
 HCGR_PLAN_FUSED = 4
 HCGR_PLAN_PERSISTENT = 5
-HCGR_WORKSPACE_COUNTER_BYTES = 4096
+HCGR_WORKSPACE_COUNTER_BYTES = 131072
 PLAN_FIELDS = ("tokens", "kind", "down_variant", "streams_per_wg", "segments", "up_variant", "ranges")
 
 

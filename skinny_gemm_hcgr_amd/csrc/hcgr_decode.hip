@@ -15,8 +15,10 @@
 //   PERSISTENT  one kernel, hcgr_dec_persist, with the down-role workgroups
 //               first and the up-role workgroups after them; an up workgroup
 //               loads its Wu rows into LDS at once, then waits (bounded) for
-//               its token tile's "h complete" counter, which every block's
-//               last arrival bumps after publishing its h rows.
+//               its token tile's ready flag: every block's last arrival
+//               bumps the tile's "h complete" counter after publishing its h
+//               rows, and the arrival that completes that count raises the
+//               flag.
 // Data that crosses workgroups inside a kernel (partials, sums of squares, and
 // in the persistent plan R2, rrms and h) moves by agent-coherent stores and
 // loads (below), so no L2 write-back or invalidation is needed.
@@ -70,14 +72,22 @@ template <bool AG>
 __device__ __forceinline__ void lds_load16_p(rsrc_t r, uint8_t* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, off, 0, 0, AG ? kAgentCoherent : 0);
 }
-// Bounded wait for the persistent plan's up role: polls *ctr (agent-coherent
-// loads, a short sleep between polls) until it reaches `need` or the poll
-// budget runs out; a wait that gives up raises *err and returns false.
+// Counter slot i of a slot array: each slot starts a 128-byte line of its
+// own, since agent-scope atomics on one line are serialised.
+__device__ __forceinline__ uint32_t* slot(uint32_t* base, int64_t i) { return base + i * kCtrStride; }
+
+// Bounded wait for the persistent plan's up role: polls the ready flag *flag
+// (an agent-coherent load, then a sleep of 8 x 64 cycles) until it is set or
+// the poll budget runs out; a wait that gives up raises *err and returns
+// false. The flag sits in a line of its own that only the arrival completing
+// the count writes: measured on MI355X, 160 workgroups polling the very
+// counter that 252 others increment delayed the increments by 2-5 us,
+// polling a separate flag by 0.3 us.
 constexpr int kSpinLimit = 1 << 20;
-__device__ __forceinline__ bool wait_count(uint32_t* ctr, uint32_t need, uint32_t* err) {
+__device__ __forceinline__ bool wait_flag(const uint32_t* flag, uint32_t* err) {
   for (int it = 0; it < kSpinLimit; ++it) {
-    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) return true;
-    __builtin_amdgcn_s_sleep(2);
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return true;
+    __builtin_amdgcn_s_sleep(8);
   }
   __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return false;
@@ -104,7 +114,8 @@ struct FuseArgs {
   float* P;       // [tiles][nblk][nkc][TM][16] unscaled chunk partials
   float* SS;      // [tiles][nblk][nkc][TM] chunk sums of squares
   uint32_t* ctr;  // [tiles][nblk] arrival counters (zero between calls)
-  uint32_t* hdone;  // [tiles] persistent plan: blocks whose h rows are published
+  uint32_t* hdone;  // [tiles] slots, persistent plan: blocks whose h rows are published
+  uint32_t* ready;  // [tiles] slots, persistent plan: raised when every block of the tile is published
 };
 
 // ---------------------------------------------------------------------------
@@ -301,7 +312,7 @@ __device__ __forceinline__ void fuse_down(const FuseArgs& a, int bx, int tile) {
   if (lane < TM) bst4_agent(rS, (uint32_t)((chunk * TM + lane) * 4), ssl[lane]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(a.ctr + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) old = __hip_atomic_fetch_add(slot(a.ctr, grp), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0, 64);
   if (old != (uint32_t)(a.nkc - 1)) return;
 
@@ -378,11 +389,14 @@ __device__ __forceinline__ void fuse_down(const FuseArgs& a, int bx, int tile) {
     }
   }
   if (PERSIST) {
-    // h (and, from block 0, rrms) complete before the tile's "h complete" count moves
+    // h (and, from block 0, rrms) complete before the tile's "h complete" count
+    // moves; the arrival that completes it raises the tile's ready flag
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (lane == 0) __hip_atomic_fetch_add(a.hdone + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0 &&
+        __hip_atomic_fetch_add(slot(a.hdone, tile), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(a.nblk - 1))
+      __hip_atomic_store(slot(a.ready, tile), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (lane == 0) __hip_atomic_store(a.ctr + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) __hip_atomic_store(slot(a.ctr, grp), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int TM>
@@ -413,11 +427,11 @@ struct DecUpArgs {
   const uint16_t* wn;
   int wn_full;
   uint16_t* x;
-  // persistent plan only
+  // persistent plan only (counter slot arrays)
   uint32_t* hdone;  // [tiles] published blocks of h per token tile
+  uint32_t* ready;  // [tiles] raised when the tile's h is complete
   uint32_t* exitc;  // [tiles] up workgroups past their wait
   uint32_t* err;    // raised by a wait that gave up
-  int need;         // blocks per token tile (the count that completes h)
 };
 
 // LDS of the up role: Wu rows, h tile, R2 rows, rrms, Wnorm, a flag word.
@@ -471,7 +485,7 @@ __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, in
     lds_load16(rWn, wnl, lane < nwn ? wo : kOutOfRange);
   }
   if (PERSIST) {
-    if (tid == 0) *flag = wait_count(a.hdone + tile, (uint32_t)a.need, a.err) ? 1 : 0;
+    if (tid == 0) *flag = wait_flag(slot(a.ready, tile), a.err) ? 1 : 0;
     __syncthreads();
   }
   const rsrc_t rH = make_rsrc(a.h + m0 * a.r, (uint32_t)rows * rowb);  // rows past M read as zero
@@ -494,9 +508,10 @@ __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, in
   lds_sync();  // every wave's global->LDS loads have landed
   if (PERSIST && tid == 0) {
     // the tile's last up workgroup past its wait returns the tile's counters to zero
-    if (__hip_atomic_fetch_add(a.exitc + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(ncg - 1)) {
-      __hip_atomic_store(a.hdone + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.exitc + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_fetch_add(slot(a.exitc, tile), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(ncg - 1)) {
+      __hip_atomic_store(slot(a.hdone, tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(slot(a.ready, tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(slot(a.exitc, tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -639,7 +654,7 @@ int launch_decg_up(const Shape& s, int tm, const uint16_t* H, const ForwardArgs&
   DecUpArgs u;
   u.h = H; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = (int)s.k(); u.wu = f.wu; u.R2 = f.res; u.rrms = f.rrms;
   u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0; u.x = f.x;
-  u.hdone = u.exitc = u.err = nullptr; u.need = 0;
+  u.hdone = u.ready = u.exitc = u.err = nullptr;
   const dim3 g((unsigned)(s.hs / decg_channels(s.hc)), (unsigned)cdiv(f.M, (int64_t)tm));
   const size_t lds = k2_decg_lds(s.hc, tm, s.r);
   if (tm == 16) launch_decg<16>(s.hc, u, g, lds, st, ev);
@@ -688,11 +703,13 @@ int launch_fused(const Shape& s, const Plan& p, const ForwardArgs& f, void* stre
   a.P = reinterpret_cast<float*>(ws + p.off_p);
   a.SS = reinterpret_cast<float*>(ws + p.off_ss);
   a.ctr = ctr;
-  a.hdone = ctr + kHdoneWord;
+  a.hdone = ctr + kHdoneSlot * kCtrStride;
+  a.ready = ctr + kReadySlot * kCtrStride;
   DecUpArgs u;
   u.h = H; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = K; u.wu = f.wu; u.R2 = f.res; u.rrms = f.rrms;
   u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0; u.x = f.x;
-  u.hdone = ctr + kHdoneWord; u.exitc = ctr + kExitWord; u.err = ctr + kErrWord; u.need = s.nblk();
+  u.hdone = ctr + kHdoneSlot * kCtrStride; u.ready = ctr + kReadySlot * kCtrStride;
+  u.exitc = ctr + kExitSlot * kCtrStride; u.err = ctr + kErrSlot * kCtrStride;
   hipError_t e;
   if (p.kind == PLAN_PERSIST) {
     const size_t lds = k1_fuse_lds(p.tm) > k2_decg_lds(s.hc, p.tm, s.r, 4) ? k1_fuse_lds(p.tm)

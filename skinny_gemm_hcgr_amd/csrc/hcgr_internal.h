@@ -55,13 +55,14 @@ namespace hcgr {
 
 enum PlanKind { PLAN_SPLIT = 0, PLAN_STREAM = 1, PLAN_FULL = 2, PLAN_TILE = 3, PLAN_FUSED = 4, PLAN_PERSIST = 5 };
 
-// Arrival counters. The first kCtrBytes of every workspace hold 32-bit
-// counters that the fused decode plan's workgroups increment; every plan keeps
+// Arrival counters. The first kCtrBytes of every workspace hold kCtrSlots
+// 32-bit counters (one per 128-byte line) that the fused and persistent
+// decode plans' workgroups increment; every plan keeps
 // its data past them, a counter is reset to zero by the workgroup that sees
 // its last arrival, so a workspace zeroed once before its first use stays
 // zero there after every completed call.
-constexpr size_t kCtrBytes = 4096;
-constexpr int kCtrWords = (int)(kCtrBytes / 4);
+constexpr int kCtrSlots = 1024, kCtrStride = 32;  // counters; words from one counter to the next
+constexpr size_t kCtrBytes = (size_t)kCtrSlots * kCtrStride * 4;  // 128 KiB
 
 // SPLIT-plan down kernel variants: token tile, 16-row blocks per workgroup,
 // waves splitting each block's k range, columns per chunk.
@@ -279,11 +280,16 @@ inline size_t k1_fuse_lds(int tm) {
   return (size_t)(2 * tm + 16) * row + 2048 + (size_t)tm * 12;  // R, y, weights, Wnorm slot, iw and sums
 }
 
-// Counter words of the decode plans: block counters [0, 512), then the
-// persistent plan's per-tile "h complete" counters [512, 768), its per-tile
-// exit counters [768, 1023) and the word kErrWord that a persistent wait
-// which gave up sets to 1.
-constexpr int kHdoneWord = 512, kExitWord = 768, kErrWord = kCtrWords - 1;
+// Counter slots of the decode plans (slot i at word i * kCtrStride: every
+// counter starts a 128-byte line of its own, since agent-scope atomics on
+// one line are serialised; measured on MI355X, 1680 arrivals on 21 counters
+// of one line took 13.7 us, on 21 lines of their own 0.5 us): block
+// counters [0, 512), then the persistent plan's per-tile "h complete"
+// counters [512, 640), its per-tile ready flags [640, 768) that the arrival
+// completing a tile's count raises and the up role polls, its per-tile exit
+// counters [768, 1023) and the slot kErrSlot that a persistent wait which
+// gave up sets to 1.
+constexpr int kHdoneSlot = 512, kReadySlot = 640, kExitSlot = 768, kErrSlot = kCtrSlots - 1;
 
 // FUSED plan (persist = false) or PERSISTENT plan (persist = true) with tm
 // tokens per tile (16 or 32); false when the shape does not fit their limits
@@ -302,10 +308,10 @@ inline bool make_fused(const Shape& s, int64_t M, int tm, Plan* out, bool persis
   if (kcps > U) kcps = U;
   const int nkc = s.hc * kcps;
   const int64_t ntiles = cdiv(M, (int64_t)tm);
-  if (nkc > 4 * kFuseUmax || ntiles * nblk > kHdoneWord) return false;
+  if (nkc > 4 * kFuseUmax || ntiles * nblk > kHdoneSlot) return false;
   if (k1_fuse_lds(tm) > kLdsPerCu) return false;
   if (persist) {
-    if (ntiles > kErrWord - kExitWord || k2_decg_lds(s.hc, tm, s.r, 4) > kLdsPerCu) return false;
+    if (ntiles > kExitSlot - kReadySlot || k2_decg_lds(s.hc, tm, s.r, 4) > kLdsPerCu) return false;
   } else if (k2_decg_lds(s.hc, tm, s.r) > kLdsPerCu) {
     return false;
   }
