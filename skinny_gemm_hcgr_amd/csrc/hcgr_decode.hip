@@ -506,14 +506,6 @@ __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, in
     for (int i = 0; i * 64 < TM * HC / 4; ++i) lds_load16_p<PERSIST>(rRr, rrl + i * 1024, (uint32_t)(i * 64 + lane) * 16u);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_sync();  // every wave's global->LDS loads have landed
-  if (PERSIST && tid == 0) {
-    // the tile's last up workgroup past its wait returns the tile's counters to zero
-    if (__hip_atomic_fetch_add(slot(a.exitc, tile), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(ncg - 1)) {
-      __hip_atomic_store(slot(a.hdone, tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(slot(a.ready, tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(slot(a.exitc, tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
 
   // epilogue operands of the lane's four rows: channel chl (in the
   // workgroup), stream st
@@ -576,6 +568,15 @@ __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, in
       float part = (g[0] + g[1]) + (g[2] + g[3]);  // streams 4(kg&1) .. +3 of channel kg/2
       part += __shfl_xor(part, 16, 64);
       if (m < a.M && (kg & 1) == 0) xr[kg >> 1] = to_bf(part * inv);
+    }
+  }
+  if (PERSIST && tid == 0) {
+    // the tile's last up workgroup returns the tile's counters to zero (its
+    // round trip overlaps the x stores: nothing after it waits for it)
+    if (__hip_atomic_fetch_add(slot(a.exitc, tile), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(ncg - 1)) {
+      __hip_atomic_store(slot(a.hdone, tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(slot(a.ready, tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(slot(a.exitc, tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -120,20 +120,22 @@ def test_bad_table_leaves_the_handle_unchanged(H, weights):
     op.close()
 
 
-@pytest.mark.parametrize("merged", [False, True])
-def test_shipped_table_at_every_tuned_key(H, weights, merged):
-    """Every non-heuristic entry of the shipped tables, at its own key, against
-    the oracle (sampled rows above 1024 tokens)."""
-    cfg = H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336) if merged else H.Config()
+@pytest.mark.parametrize("hc,merged", [(4, False), (4, True), (1, False), (2, False), (8, False)])
+def test_shipped_table_at_every_tuned_key(H, weights, hc, merged):
+    """Every non-heuristic entry of the shipped tables (HS = 2560, r = 320 at
+    every stream count), at its own key, against the oracle (sampled rows
+    above 1024 tokens)."""
+    cfg = H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336) if merged else H.Config(hc=hc)
+    shape = synth.Shape(hc, 2560, 320)
     op = H.HCGR(cfg, 0, plan_table="shipped")
     assert op.table
     for e in op.table:
         if e["kind"] == H.HCGR_PLAN_HEURISTIC:
             continue
         M = e["tokens"]
-        _say(f"[plans] shipped merged={merged} M={M}: {op.describe(M)}")
-        inp = synth.make_inputs(M, SHAPE, seed=80 + M, device="cuda", weights=weights)
-        wd = synth.fold_merged_weight(inp["wd"], inp["wi"], inp["wnorm"], 336, SHAPE.hs) if merged else inp["wd"]
+        _say(f"[plans] shipped hc={hc} merged={merged} M={M}: {op.describe(M)}")
+        inp = synth.make_inputs(M, shape, seed=80 + M, device="cuda", weights=weights if hc == 4 else None)
+        wd = synth.fold_merged_weight(inp["wd"], inp["wi"], inp["wnorm"], 336, shape.hs) if merged else inp["wd"]
         out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], wd, None if merged else inp["wi"], inp["wu"])
         torch.cuda.synchronize()
         rows = None if M <= 1024 else sample_rows(M)
@@ -141,7 +143,7 @@ def test_shipped_table_at_every_tuned_key(H, weights, merged):
         if rows is not None:
             idx = torch.as_tensor(rows, device="cuda")
             R, y, inj = R[idx], y[idx], inj[idx]
-        ocfg = oracle.OracleConfig(merged=merged, n_pad=336 if merged else 0)
+        ocfg = oracle.OracleConfig(hc=hc, merged=merged, n_pad=336 if merged else 0)
         ref = oracle.forward(ocfg, R.cpu(), y.cpu(), inj.cpu(), inp["wnorm"].cpu(), wd.cpu(),
                              None if merged else inp["wi"].cpu(), inp["wu"].cpu())
         check_rows(out, ref, rows)

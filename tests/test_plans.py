@@ -125,8 +125,9 @@ def test_workspace_bound_with_table(lib):
 
 def test_shipped_tables_load_and_validate(lib):
     """The tables shipped with the package (written by the tuner on an MI355X)
-    match their configuration and pass the library's table checks."""
-    cfgs = [CFG, H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336)]
+    match their configuration and pass the library's table checks: HC = 4
+    with separate and merged/folded weights, HC = 1, 2, 8 with separate ones."""
+    cfgs = [CFG, H.Config(weight_layout=H.HCGR_WEIGHTS_MERGED_FOLDED, n_pad=336)] + [H.Config(hc=hc) for hc in (1, 2, 8)]
     for cfg in cfgs:
         path = H.shipped_plan_table(cfg)
         assert path is not None, cfg
