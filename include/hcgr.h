@@ -270,8 +270,10 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
                                     reduction done by its last arrivals, then up     */
 #define HCGR_PLAN_PERSISTENT 5   /* persistent decode plan: one kernel, the up role
                                     waits (bounded) for the down role's h; a wait
-                                    that gives up sets the last counter word of the
-                                    workspace to 1 and that call's x is invalid      */
+                                    that gives up sets the last counter (the 32-bit
+                                    word at byte HCGR_WORKSPACE_COUNTER_BYTES - 128
+                                    of the workspace) to 1 and that call's x is
+                                    invalid                                          */
 #define HCGR_SPLIT_VARIANTS 11   /* down-kernel variants of the decode plan           */
 
 typedef struct hcgr_plan_choice {
