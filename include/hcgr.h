@@ -82,6 +82,20 @@ hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out);
 /* Frees a handle (NULL is allowed). Outstanding work on streams is unaffected. */
 void hcgr_destroy(hcgr_handle h);
 
+/* Poll budget of the one wait inside a launch: an up-role workgroup of the
+ * persistent decode plan (HCGR_PLAN_PERSISTENT) polls its token tile's ready
+ * flag, about 0.2 us apart, at most `polls` times before it gives up. A wait
+ * that gives up sets the workspace's error counter (the 32-bit word at byte
+ * HCGR_WORKSPACE_COUNTER_BYTES - 128) to 1 and goes on without h: that call's
+ * x is invalid, and the caller zeroes the counter bytes again before the next
+ * call on that workspace. 0 gives up at once (a check of that error path).
+ * Affects later calls through h; other plans do not wait. Default
+ * HCGR_DEFAULT_WAIT_POLLS (about 0.2 s). Pure host code. Errors:
+ * HCGR_ERR_INVALID_ARGUMENT (NULL h, polls < 0 or > HCGR_MAX_WAIT_POLLS). */
+#define HCGR_DEFAULT_WAIT_POLLS 1048576
+#define HCGR_MAX_WAIT_POLLS 16777216
+hcgr_status hcgr_set_wait_polls(hcgr_handle h, int32_t polls);
+
 /* Bytes at the start of every workspace that hold arrival counters (1024
  * 32-bit counters, each at the start of a 128-byte line of its own). */
 #define HCGR_WORKSPACE_COUNTER_BYTES 131072

@@ -33,6 +33,8 @@ HCGR_PLAN_TILE = 3
 HCGR_PLAN_FUSED = 4
 HCGR_PLAN_PERSISTENT = 5
 HCGR_WORKSPACE_COUNTER_BYTES = 131072
+HCGR_DEFAULT_WAIT_POLLS = 1 << 20
+HCGR_MAX_WAIT_POLLS = 1 << 24
 PLAN_FIELDS = ("tokens", "kind", "down_variant", "streams_per_wg", "segments", "up_variant", "ranges")
 
 
@@ -127,6 +129,7 @@ def load_library(path: str = LIB_PATH):
     lib.hcgr_plan_lookup.argtypes = [CFG, PC, ctypes.c_int32, I64, PC, ctypes.c_char_p, SZ]
     lib.hcgr_workspace_size_table.argtypes = [CFG, PC, ctypes.c_int32, I64, ctypes.POINTER(SZ)]
     lib.hcgr_set_plan_table.argtypes = [P, PC, ctypes.c_int32]
+    lib.hcgr_set_wait_polls.argtypes = [P, ctypes.c_int32]
     lib.hcgr_status_string.argtypes = [ctypes.c_int]
     lib.hcgr_status_string.restype = ctypes.c_char_p
     lib.hcgr_last_error.argtypes = []
@@ -134,7 +137,7 @@ def load_library(path: str = LIB_PATH):
     for name in ("hcgr_create", "hcgr_workspace_size", "hcgr_workspace_size_for", "hcgr_forward",
                  "hcgr_forward_timed", "hcgr_forward_noalloc", "hcgr_combine", "hcgr_mix", "hcgr_validate_combine",
                  "hcgr_validate_mix", "hcgr_validate", "hcgr_describe_plan", "hcgr_plan_candidates",
-                 "hcgr_plan_lookup", "hcgr_workspace_size_table", "hcgr_set_plan_table"):
+                 "hcgr_plan_lookup", "hcgr_workspace_size_table", "hcgr_set_plan_table", "hcgr_set_wait_polls"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -224,6 +227,10 @@ def hcgr_workspace_size_table(cfg: Config, table, M: int) -> int:
 def hcgr_set_plan_table(handle: int, table) -> None:
     arr, n = _choices_in(table)
     _check(load_library().hcgr_set_plan_table(handle, arr, n), "hcgr_set_plan_table")
+
+
+def hcgr_set_wait_polls(handle: int, polls: int) -> None:
+    _check(load_library().hcgr_set_wait_polls(handle, int(polls)), "hcgr_set_wait_polls")
 
 
 PLANS_DIR = os.path.join(_PKG, "plans")
@@ -384,6 +391,9 @@ class HCGR:
         hcgr_set_plan_table(self.handle, table)
         self.table = list(table)
         self._ws = None  # the workspace bound may change
+
+    def set_wait_polls(self, polls: int):
+        hcgr_set_wait_polls(self.handle, polls)
 
     def describe(self, M: int) -> str:
         return hcgr_plan_lookup(self.cfg, getattr(self, "table", []), M)[1]

@@ -19,7 +19,10 @@ struct hcgr_op {
   int device;
   int cu_count;
   std::vector<hcgr::TableEntry> table;  // tuned plans (empty: the heuristic)
+  int wait_polls = hcgr::kDefaultWaitPolls;  // hcgr_set_wait_polls
 };
+static_assert(HCGR_DEFAULT_WAIT_POLLS == hcgr::kDefaultWaitPolls && HCGR_MAX_WAIT_POLLS == hcgr::kMaxWaitPolls,
+              "the header's poll budgets are the library's");
 
 // Scratch for hcgr_forward_noalloc: the workspace of callers that cannot
 // allocate. Each GPU the library runs on holds one copy until the process
@@ -441,6 +444,14 @@ hcgr_status hcgr_create(const hcgr_config* cfg, int device, hcgr_handle* out) {
 
 void hcgr_destroy(hcgr_handle h) { delete h; }
 
+hcgr_status hcgr_set_wait_polls(hcgr_handle h, int32_t polls) {
+  if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
+  if (polls < 0 || polls > hcgr::kMaxWaitPolls)
+    return fail(HCGR_ERR_INVALID_ARGUMENT, "polls=%d is outside 0..%d", (int)polls, hcgr::kMaxWaitPolls);
+  h->wait_polls = polls;
+  return ok();
+}
+
 hcgr_status hcgr_workspace_size(hcgr_handle h, int64_t M, size_t* bytes) {
   if (!h) return fail(HCGR_ERR_INVALID_ARGUMENT, "handle is NULL");
   if (!bytes) return fail(HCGR_ERR_INVALID_ARGUMENT, "bytes is NULL");
@@ -507,6 +518,7 @@ static hcgr_status forward_impl(hcgr_handle h, const uint16_t* R, const uint16_t
   a.ld_inj = ld_inj; a.ld_inj_next = ld_inj_next; a.M = M;
   a.R2 = R2; a.inj_next = inj_next; a.x = x; a.rrms = rrms; a.ws = workspace;
   a.res = mix ? R : R2;
+  a.wait_polls = h->wait_polls;
   int le = hcgr::launch_forward(h->shape, plan, a, stream, events);
   restore_device(h, cur);
   if (le != (int)hipSuccess)

@@ -78,14 +78,13 @@ __device__ __forceinline__ uint32_t* slot(uint32_t* base, int64_t i) { return ba
 
 // Bounded wait for the persistent plan's up role: polls the ready flag *flag
 // (an agent-coherent load, then a sleep of 8 x 64 cycles) until it is set or
-// the poll budget runs out; a wait that gives up raises *err and returns
-// false. The flag sits in a line of its own that only the arrival completing
+// `polls` polls have found it clear; a wait that gives up raises *err and
+// returns false. The flag sits in a line of its own that only the arrival completing
 // the count writes: measured on MI355X, 160 workgroups polling the very
 // counter that 252 others increment delayed the increments by 2-5 us,
 // polling a separate flag by 0.3 us.
-constexpr int kSpinLimit = 1 << 20;
-__device__ __forceinline__ bool wait_flag(const uint32_t* flag, uint32_t* err) {
-  for (int it = 0; it < kSpinLimit; ++it) {
+__device__ __forceinline__ bool wait_flag(const uint32_t* flag, uint32_t* err, int polls) {
+  for (int it = 0; it < polls; ++it) {
     if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return true;
     __builtin_amdgcn_s_sleep(8);
   }
@@ -432,6 +431,7 @@ struct DecUpArgs {
   uint32_t* ready;  // [tiles] raised when the tile's h is complete
   uint32_t* exitc;  // [tiles] up workgroups past their wait
   uint32_t* err;    // raised by a wait that gave up
+  int polls;        // poll budget of that wait
 };
 
 // LDS of the up role: Wu rows, h tile, R2 rows, rrms, Wnorm, a flag word.
@@ -485,7 +485,7 @@ __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, in
     lds_load16(rWn, wnl, lane < nwn ? wo : kOutOfRange);
   }
   if (PERSIST) {
-    if (tid == 0) *flag = wait_flag(slot(a.ready, tile), a.err) ? 1 : 0;
+    if (tid == 0) *flag = wait_flag(slot(a.ready, tile), a.err, a.polls) ? 1 : 0;
     __syncthreads();
   }
   const rsrc_t rH = make_rsrc(a.h + m0 * a.r, (uint32_t)rows * rowb);  // rows past M read as zero
@@ -655,7 +655,7 @@ int launch_decg_up(const Shape& s, int tm, const uint16_t* H, const ForwardArgs&
   DecUpArgs u;
   u.h = H; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = (int)s.k(); u.wu = f.wu; u.R2 = f.res; u.rrms = f.rrms;
   u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0; u.x = f.x;
-  u.hdone = u.ready = u.exitc = u.err = nullptr;
+  u.hdone = u.ready = u.exitc = u.err = nullptr; u.polls = 0;
   const dim3 g((unsigned)(s.hs / decg_channels(s.hc)), (unsigned)cdiv(f.M, (int64_t)tm));
   const size_t lds = k2_decg_lds(s.hc, tm, s.r);
   if (tm == 16) launch_decg<16>(s.hc, u, g, lds, st, ev);
@@ -710,7 +710,7 @@ int launch_fused(const Shape& s, const Plan& p, const ForwardArgs& f, void* stre
   u.h = H; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = K; u.wu = f.wu; u.R2 = f.res; u.rrms = f.rrms;
   u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0; u.x = f.x;
   u.hdone = ctr + kHdoneSlot * kCtrStride; u.ready = ctr + kReadySlot * kCtrStride;
-  u.exitc = ctr + kExitSlot * kCtrStride; u.err = ctr + kErrSlot * kCtrStride;
+  u.exitc = ctr + kExitSlot * kCtrStride; u.err = ctr + kErrSlot * kCtrStride; u.polls = f.wait_polls;
   hipError_t e;
   if (p.kind == PLAN_PERSIST) {
     const size_t lds = k1_fuse_lds(p.tm) > k2_decg_lds(s.hc, p.tm, s.r, 4) ? k1_fuse_lds(p.tm)

@@ -678,6 +678,10 @@ inline size_t workspace_bound_table(const Shape& s, int64_t M, const TableEntry*
 // The mix entry point (every step but COMBINE) passes y, inj and R2 as NULL
 // and res == R: the down kernels then read y as zeros (R2 = R exactly),
 // store no R2, and the up kernel rebuilds xn from the input residual.
+// Poll budget of a bounded wait inside one launch (the persistent decode
+// plan's up role): the default and the largest a caller may set.
+constexpr int kDefaultWaitPolls = 1 << 20, kMaxWaitPolls = 1 << 24;
+
 struct ForwardArgs {
   const uint16_t *R, *y, *inj, *wnorm, *wd, *wi, *wu;
   int64_t ld_inj, ld_inj_next, M;
@@ -685,6 +689,7 @@ struct ForwardArgs {
   const uint16_t* res;  // residual the up kernel reads: R2 (whole op) or R (mix)
   float* rrms;
   void* ws;
+  int wait_polls = kDefaultWaitPolls;  // polls before a bounded wait gives up (0: at once)
 };
 
 struct CombineArgs {

@@ -271,3 +271,13 @@ def test_mix_errors(lib):
         assert _mix(L, **{out: L.addr[other]}) == H.HCGR_ERR_ALIASING, (out, other)
     # the inputs mix does not take may share memory with its outputs freely
     assert _mix(L, x=L.addr["y"], rrms=L.addr["R2"]) == H.HCGR_OK
+
+
+def test_wait_polls_needs_a_handle(lib):
+    """hcgr_set_wait_polls is pure host code: a NULL handle is rejected with
+    the documented status and message."""
+    with pytest.raises(H.HcgrError) as e:
+        H.hcgr_set_wait_polls(None, 5)
+    assert e.value.status == H.HCGR_ERR_INVALID_ARGUMENT
+    assert "NULL" in H.last_error()
+    assert H.HCGR_DEFAULT_WAIT_POLLS == 1 << 20 and H.HCGR_MAX_WAIT_POLLS == 1 << 24

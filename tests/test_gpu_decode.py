@@ -216,6 +216,35 @@ def test_decode_plans_interleaved_stress(H, kind):
         ops[M].close()
 
 
+def test_persistent_wait_that_gives_up(H):
+    """The persistent plan's bounded wait, forced from the host to give up at
+    once (a poll budget of 0): the launch completes, the workspace's error
+    counter reads 1, and once the caller has zeroed the counter bytes and
+    restored the budget, the next call on the same workspace matches the
+    oracle and leaves every counter at zero. Budgets outside 0..2^24 are
+    rejected."""
+    M = 5
+    op = make_op(H, PERSISTENT, M)
+    for bad in (-1, H.HCGR_MAX_WAIT_POLLS + 1):
+        with pytest.raises(H.HcgrError):
+            op.set_wait_polls(bad)
+    inp = synth.make_inputs(M, synth.Shape(), seed=77, device="cuda")
+    ws = op.workspace(M)
+    op.set_wait_polls(0)
+    _say("[decode] persistent M=5 with a poll budget of 0")
+    op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"], workspace=ws)
+    torch.cuda.synchronize()
+    n = H.HCGR_WORKSPACE_COUNTER_BYTES
+    assert int(ws[n - 128:n - 124].view(torch.int32)[0]) == 1
+    ws[:n].zero_()
+    op.set_wait_polls(H.HCGR_DEFAULT_WAIT_POLLS)
+    out = op.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"], workspace=ws)
+    torch.cuda.synchronize()
+    check_all(out, oracle_forward(oracle.OracleConfig(), inp))
+    counters_clear(H, ws)
+    op.close()
+
+
 @pytest.mark.parametrize("hc", [1, 2, 8])
 @pytest.mark.parametrize("kd", list(range(11)))
 def test_split_plan_other_stream_counts(H, hc, kd):
