@@ -279,6 +279,28 @@ def measure_copy_gbs(torch, nbytes=1 << 30, reps=10):
     return 2 * nbytes / sorted(times)[len(times) // 2] / 1e9
 
 
+def measure_gemm_tflops(torch, n=8192, reps=10):
+    """bf16 dense GEMM rate of the platform's library GEMM (torch.matmul on an
+    n x n x n product): the achievable matrix-core rate on this machine, beside
+    the published 2.5 PFLOP/s. Median of reps event-timed calls."""
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    torch.cuda.empty_cache()
+    return 2.0 * n ** 3 / sorted(times)[len(times) // 2] / 1e12
+
+
 def kernel_source_digest():
     """Digest of the kernel sources; a counter summary taken on other sources no longer applies."""
     import glob
@@ -559,6 +581,7 @@ def main():
     dom = max(head["kernels_us"], key=lambda k: head["kernels_us"][k])
     roof = roofline_entry(dom, M, head["kernels_us"][dom], merged, head["plan"], args.workload)
     copy_gbs = measure_copy_gbs(torch)
+    gemm_tflops = measure_gemm_tflops(torch)
     roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbs, 4)
     line = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["us_per_call"] / 1e3, 6),
@@ -572,9 +595,10 @@ def main():
             "us_per_call_warm": warm["us_per_call"] if warm else None,
             "op_roofline_frac": head["op_roofline_frac"], "op_hbm_frac": head["op_hbm_frac"],
             "kernels_us": head["kernels_us"], "roofline": roof,
-            "measured_peaks": {"hbm_copy_gbs": round(copy_gbs, 1),
-                               "note": "read + write bytes per second of a 1 GiB device copy on this box; "
-                                       "op_hbm_frac and roofline.frac use the published 8 TB/s"},
+            "measured_peaks": {"hbm_copy_gbs": round(copy_gbs, 1), "bf16_gemm_tflops": round(gemm_tflops, 1),
+                               "note": "read + write bytes per second of a 1 GiB device copy, and the bf16 rate "
+                                       "of an 8192^3 library GEMM (torch.matmul), on this box; op_hbm_frac, "
+                                       "op_mfma_frac and roofline.frac use the published 8 TB/s and 2.5 PFLOP/s"},
             "context": {"pages_two_stage_graph_us": {"1": 21.0, "32": 28.8, "1024": 76.3, "8192": 339.2,
                                                      "65536": 2636.4},
                         "note": "page numbers: MI355X, merged/folded weights, graph replay; context only"}}
