@@ -112,7 +112,9 @@ hcgr_status hcgr_set_wait_polls(hcgr_handle h, int32_t polls);
  * Zero-fill the workspace once after allocating it (hipMemset; at least the
  * counter bytes): every call leaves the counter bytes zero when it completes,
  * and reads nothing else of the workspace before writing it. After a call
- * that returned HCGR_ERR_HIP, zero the counter bytes again. Calls that may
+ * that returned HCGR_ERR_HIP, or whose persistent-plan wait gave up (the
+ * error counter reads 1; hcgr_set_wait_polls), zero the counter bytes again.
+ * Calls that may
  * run concurrently (different streams) need separate workspaces. */
 hcgr_status hcgr_workspace_size(hcgr_handle h, int64_t M, size_t* bytes);
 
