@@ -36,12 +36,10 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every range
 __device__ __forceinline__ void lds_load16(rsrc_t r, uint8_t* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, off, 0, 0, 0);
 }
-// Agent-scope coherent accesses (the SC1 cache-policy bit): stores write
-// through the XCD's L2, loads do not return a line another XCD may have
-// changed. The partial products that cross workgroups use them, so their
-// publication needs no L2 write-back or invalidation, only the completion
-// of the stores before the counter update.
-constexpr int kAgentCoherent = 16;
+// Agent-coherent accesses (kAgentCoherent, the SC1 policy): the partial
+// products that cross workgroups use them, so their publication needs no L2
+// write-back or invalidation, only the completion of the stores before the
+// counter update.
 __device__ __forceinline__ void lds_load16_agent(rsrc_t r, uint8_t* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, off, 0, 0, kAgentCoherent);
 }

@@ -74,6 +74,20 @@ __device__ __forceinline__ uint2 bld8(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void bst8(rsrc_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, (int)off, 0, 0);
 }
+// Agent-scope coherent accesses (the SC1 cache-policy bit): stores write
+// through the XCD's L2 (the line does not stay dirty there), loads do not
+// return a line another XCD may have changed.
+constexpr int kAgentCoherent = 16;
+// Write-through stores, for a kernel's outputs at decode sizes, where the
+// write-back of dirty lines at the kernel's end would otherwise sit on the
+// critical path.
+__device__ __forceinline__ void bst16_wt(rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, kAgentCoherent);
+}
+__device__ __forceinline__ void st_f32(float* p, float v, int wt) {
+  if (wt) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // a store with SC1
+  else *p = v;
+}
 // Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
 // operations, then s_barrier. Unlike __syncthreads it does not wait for
 // outstanding global->LDS loads, which may stay in flight across it (their
