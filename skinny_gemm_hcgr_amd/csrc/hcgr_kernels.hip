@@ -2229,10 +2229,12 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     a.nseg = p.nseg; a.SSp = reinterpret_cast<float*>(ws + p.off_ss);
     a.tiles = (int)cdiv(f.M, (int64_t)p.tm);
     a.xgroup = p.xgroup;
-    // streaming policy for R and R2 when the up kernel cannot find R2 in the
-    // caches anyway: the sweep (large M), or R2 beyond the Infinity Cache;
-    // not for the mix entry point, whose up kernel reads R itself again
-    a.nt = f.R2 && (p.kt == KT_SWEEP || (double)f.M * K * 2.0 > kStreamBytes) ? 1 : 0;
+    // streaming policy for R and R2 under either sweep up kernel (large M:
+    // measured on MI355X with the 256-token sweep at M = 8192, R2 168 MB,
+    // 218-223 against 229-232 us per call, the down kernel 108.5 against 122
+    // us; no change at 4096) or R2 beyond the Infinity Cache; not for the mix
+    // entry point, whose up kernel reads R itself again
+    a.nt = f.R2 && (is_sweep(p.kt) || (double)f.M * K * 2.0 > kStreamBytes) ? 1 : 0;
     const int64_t tiles_g = p.xgroup ? cdiv((int64_t)a.tiles, 8) * 8 : a.tiles;
     const dim3 g1((unsigned)(tiles_g * p.nsplit * (s.hc / p.spw) * p.nseg));
     if (p.spw == 4) klaunch(hcgr_k1_tile<4, 64, 4>, g1, dim3(512), 0, st, tm.stage(0), a);
