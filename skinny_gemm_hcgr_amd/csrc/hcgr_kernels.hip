@@ -783,7 +783,8 @@ struct Tile1Args {
   float* SSp;  // [HC*nseg][Mq] per-segment sums of squares (nseg > 1)
   int tiles;   // token tiles
   int xgroup;  // 1: the workgroups of one token tile share an XCD (grid rounded up to 8 tiles)
-  int nt;      // 1: R read and R2 written with the non-temporal policy
+  int nt;      // 1: R2 written with the non-temporal policy
+  int ntr;     // 1: R read with the non-temporal policy
 };
 
 template <int N>
@@ -906,8 +907,8 @@ __global__ __launch_bounds__(512) void hcgr_k1_tile(Tile1Args a) {
     for (int j = 0; j < TPT; ++j) {
       const uint32_t oR = valid ? offR + (uint32_t)(j * 64) * rowb + (uint32_t)(s * HS) * 2u + col : kOut;
       const uint32_t oY = valid ? offY + (uint32_t)(j * 64 * HS) * 2u + col : kOut;
-      rv[k][j] = __builtin_bit_cast(u32x4_t, a.nt ? __builtin_amdgcn_raw_buffer_load_b128(rR, (int)oR, 0, kNonTemporal)
-                                                 : __builtin_amdgcn_raw_buffer_load_b128(rR, (int)oR, 0, 0));
+      rv[k][j] = __builtin_bit_cast(u32x4_t, a.ntr ? __builtin_amdgcn_raw_buffer_load_b128(rR, (int)oR, 0, kNonTemporal)
+                                                  : __builtin_amdgcn_raw_buffer_load_b128(rR, (int)oR, 0, 0));
       yv[k][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rY, (int)oY, 0, 0));
     }
     const uint32_t oW = valid ? (wnc ? (uint32_t)(s * HS) * 2u : 0u) + col + swz * 16u : kOut;
@@ -2229,12 +2230,19 @@ static int launch_tiled(const Shape& s, const Plan& p, const ForwardArgs& f, hip
     a.nseg = p.nseg; a.SSp = reinterpret_cast<float*>(ws + p.off_ss);
     a.tiles = (int)cdiv(f.M, (int64_t)p.tm);
     a.xgroup = p.xgroup;
-    // streaming policy for R and R2 under either sweep up kernel (large M:
+    // streaming policy for R2 (and R) under either sweep up kernel (large M:
     // measured on MI355X with the 256-token sweep at M = 8192, R2 168 MB,
     // 218-223 against 229-232 us per call, the down kernel 108.5 against 122
     // us; no change at 4096) or R2 beyond the Infinity Cache; not for the mix
     // entry point, whose up kernel reads R itself again
     a.nt = f.R2 && (is_sweep(p.kt) || (double)f.M * K * 2.0 > kStreamBytes) ? 1 : 0;
+    // R itself is read once and is dead after the op (R2 replaces it): the
+    // streaming policy at every M, so it does not displace the weights and y
+    // that the workgroups re-read through the caches (measured on MI355X,
+    // HC = 4: 51.2 against 54.5 us per call at M = 1024, 74-75 against 77-78
+    // at 2048; HC = 2: 82 against 86 at 4096; no change at 256 and 4096);
+    // not for the mix entry point either
+    a.ntr = f.R2 ? 1 : 0;
     const int64_t tiles_g = p.xgroup ? cdiv((int64_t)a.tiles, 8) * 8 : a.tiles;
     const dim3 g1((unsigned)(tiles_g * p.nsplit * (s.hc / p.spw) * p.nseg));
     if (p.spw == 4) klaunch(hcgr_k1_tile<4, 64, 4>, g1, dim3(512), 0, st, tm.stage(0), a);
