@@ -290,7 +290,7 @@ hcgr_status hcgr_describe_plan(const hcgr_config* cfg, int64_t M, char* buf, siz
                                     word at byte HCGR_WORKSPACE_COUNTER_BYTES - 128
                                     of the workspace) to 1 and that call's x is
                                     invalid                                          */
-#define HCGR_SPLIT_VARIANTS 11   /* down-kernel variants of the decode plan           */
+#define HCGR_SPLIT_VARIANTS 13   /* down-kernel variants of the decode plan           */
 
 typedef struct hcgr_plan_choice {
     int64_t tokens;         /* table key (token count >= 1); a candidate carries the M it was made for */

@@ -32,6 +32,7 @@ HCGR_PLAN_SPLIT = 0
 HCGR_PLAN_TILE = 3
 HCGR_PLAN_FUSED = 4
 HCGR_PLAN_PERSISTENT = 5
+HCGR_SPLIT_VARIANTS = 13  # down-kernel variants of the decode plans (include/hcgr.h)
 HCGR_WORKSPACE_COUNTER_BYTES = 131072
 HCGR_DEFAULT_WAIT_POLLS = 1 << 20
 HCGR_MAX_WAIT_POLLS = 1 << 24

@@ -70,6 +70,11 @@ template <bool AG>
 __device__ __forceinline__ void lds_load16_p(rsrc_t r, uint8_t* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, off, 0, 0, AG ? kAgentCoherent : 0);
 }
+// direct global->LDS loads of 4 bytes per lane (256 bytes per instruction)
+template <bool AG>
+__device__ __forceinline__ void lds_load4_p(rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, off, 0, 0, AG ? kAgentCoherent : 0);
+}
 // Counter slot i of a slot array: each slot starts a 128-byte line of its
 // own, since agent-scope atomics on one line are serialised.
 __device__ __forceinline__ uint32_t* slot(uint32_t* base, int64_t i) { return base + i * kCtrStride; }
@@ -435,7 +440,7 @@ struct DecUpArgs {
 // LDS of the up role: Wu rows, h tile, R2 rows, rrms, Wnorm, a flag word.
 template <int HC, int TM, int NW>
 struct DecgLds {
-  static constexpr int CW = NW * (16 / HC), CH8 = CW / 8;
+  static constexpr int CW = NW * (16 / HC);
   static constexpr int R2B = (TM * HC * CW * 2 + 1023) / 1024 * 1024, RRB = (TM * HC * 4 + 1023) / 1024 * 1024;
   static constexpr int WNB = (HC * CW * 2 + 1023) / 1024 * 1024;
   static size_t bytes(int r) { return k2_decg_lds(HC, TM, r, NW); }
@@ -445,8 +450,12 @@ template <int HC, int TM, int NW, bool PERSIST>
 __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, int ncg) {
   using L = DecgLds<HC, TM, NW>;
   constexpr int CPW = 16 / HC, CW = L::CW, WR = NW * 16;
-  constexpr int NTB = TM / 16, CH8 = L::CH8;  // 16-byte pieces per (token, stream) of the R2 rows
-  static_assert(CW % 8 == 0 && CH8 <= 64 && HC * CH8 <= 64, "whole 16-byte pieces of R2 and Wnorm per stream");
+  constexpr int NTB = TM / 16;
+  // the epilogue's R2 rows and Wnorm arrive in pieces of PB bytes: 16 when the
+  // workgroup's CW channels of a stream are whole 16-byte pieces, else 4
+  constexpr int PB = CW % 8 == 0 ? 16 : 4;
+  constexpr int CHP = CW * 2 / PB;  // pieces per (token, stream) row of CW channels
+  static_assert(CW % 2 == 0 && HC * CHP <= 64, "whole pieces of R2 and Wnorm per stream, one load for Wnorm");
   extern __shared__ __attribute__((aligned(1024))) uint8_t dl[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -478,9 +487,10 @@ __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, in
     lds_load16(rWu, wl + i * 1024, (uint32_t)(st * a.HS + ch) * rowb + (uint32_t)c * 16u);
   }
   if (wave == 0) {
-    const int nwn = a.wn_full ? HC * CH8 : CH8;
-    const uint32_t wo = (uint32_t)((a.wn_full ? (lane / CH8) * a.HS : 0) + cbase + (lane % CH8) * 8) * 2u;
-    lds_load16(rWn, wnl, lane < nwn ? wo : kOutOfRange);
+    const int nwn = a.wn_full ? HC * CHP : CHP;
+    const uint32_t wo = (uint32_t)((a.wn_full ? (lane / CHP) * a.HS : 0) + cbase + (lane % CHP) * (PB / 2)) * 2u;
+    if constexpr (PB == 16) lds_load16(rWn, wnl, lane < nwn ? wo : kOutOfRange);
+    else lds_load4_p<false>(rWn, wnl, lane < nwn ? wo : kOutOfRange);
   }
   if (PERSIST) {
     if (tid == 0) *flag = wait_flag(slot(a.ready, tile), a.err, a.polls) ? 1 : 0;
@@ -494,11 +504,12 @@ __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, in
     const int c = (sl & ~3) | ((sl ^ row) & 3);
     lds_load16_p<PERSIST>(rH, hl + i * 1024, (uint32_t)row * rowb + (uint32_t)c * 16u);
   }
-  constexpr int NR2 = TM * HC * CH8;  // pieces of the tile's R2 rows
+  constexpr int NR2 = TM * HC * CHP;  // pieces of the tile's R2 rows
   for (int i = wave; i * 64 < NR2; i += NW) {
-    const int q = i * 64 + lane, t = q / (HC * CH8), st = (q / CH8) % HC, half = q % CH8;
-    const uint32_t off = (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)(st * a.HS + cbase + half * 8) * 2u;
-    lds_load16_p<PERSIST>(rR2, r2l + i * 1024, q < NR2 ? off : kOutOfRange);
+    const int q = i * 64 + lane, t = q / (HC * CHP), st = (q / CHP) % HC, pc = q % CHP;
+    const uint32_t off = (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)(st * a.HS + cbase + pc * (PB / 2)) * 2u;
+    if constexpr (PB == 16) lds_load16_p<PERSIST>(rR2, r2l + i * 1024, q < NR2 ? off : kOutOfRange);
+    else lds_load4_p<PERSIST>(rR2, r2l + i * 256, q < NR2 ? off : kOutOfRange);
   }
   if (wave == 0)
     for (int i = 0; i * 64 < TM * HC / 4; ++i) lds_load16_p<PERSIST>(rRr, rrl + i * 1024, (uint32_t)(i * 64 + lane) * 16u);
@@ -579,9 +590,9 @@ __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, in
   }
 }
 
-template <int HC, int TM>
-__global__ __launch_bounds__(64 * (HC < 4 ? HC : 4)) void hcgr_k2_decg(DecUpArgs a) {
-  decg_up<HC, TM, (HC < 4 ? HC : 4), false>(a, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x);
+template <int HC, int TM, int NW>
+__global__ __launch_bounds__(64 * NW) void hcgr_k2_decg(DecUpArgs a) {
+  decg_up<HC, TM, NW, false>(a, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -610,10 +621,23 @@ static void klaunch_d(F k, dim3 grid, dim3 block, size_t lds, hipStream_t st, co
   hipExtLaunchKernelGGL(k, grid, block, (uint32_t)lds, st, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0u, args...);
 }
 
+// the up kernel's wave counts: HC waves up to 4, and five as well at HC = 8
+// (decg_waves picks by HS)
+constexpr int decg_nw(int hc) { return hc < 4 ? hc : 4; }
+
+template <int HC, int TM>
+static hipError_t set_decg_lds() {
+  hipError_t e = hipFuncSetAttribute((const void*)hcgr_k2_decg<HC, TM, decg_nw(HC)>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu);
+  if (e == hipSuccess && HC == 8)
+    e = hipFuncSetAttribute((const void*)hcgr_k2_decg<HC, TM, 5>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsPerCu);
+  return e;
+}
+
 template <int HC, int TM>
 static hipError_t set_decode_lds() {
-  hipError_t e = hipFuncSetAttribute((const void*)hcgr_k2_decg<HC, TM>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)kLdsPerCu);
+  hipError_t e = set_decg_lds<HC, TM>();
   if (e == hipSuccess)
     e = hipFuncSetAttribute((const void*)hcgr_dec_persist<HC, TM>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)kLdsPerCu);
@@ -622,8 +646,7 @@ static hipError_t set_decode_lds() {
 
 template <int HC>
 static hipError_t set_decg64_lds() {
-  return hipFuncSetAttribute((const void*)hcgr_k2_decg<HC, 64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)kLdsPerCu);
+  return set_decg_lds<HC, 64>();
 }
 
 int configure_decode_kernels() {
@@ -645,7 +668,7 @@ int configure_decode_kernels() {
 }
 
 template <int TM>
-static void launch_decg(int hc, const DecUpArgs& u, dim3 g, size_t lds, hipStream_t st, const hipEvent_t* ev);
+static void launch_decg(int hc, int nw, const DecUpArgs& u, dim3 g, size_t lds, hipStream_t st, const hipEvent_t* ev);
 
 int launch_decg_up(const Shape& s, int tm, const uint16_t* H, const ForwardArgs& f, void* stream, void* const* events) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -654,21 +677,25 @@ int launch_decg_up(const Shape& s, int tm, const uint16_t* H, const ForwardArgs&
   u.h = H; u.M = f.M; u.r = s.r; u.HS = s.hs; u.K = (int)s.k(); u.wu = f.wu; u.R2 = f.res; u.rrms = f.rrms;
   u.wn = f.wnorm; u.wn_full = s.wn_full ? 1 : 0; u.x = f.x;
   u.hdone = u.ready = u.exitc = u.err = nullptr; u.polls = 0;
-  const dim3 g((unsigned)(s.hs / decg_channels(s.hc)), (unsigned)cdiv(f.M, (int64_t)tm));
-  const size_t lds = k2_decg_lds(s.hc, tm, s.r);
-  if (tm == 16) launch_decg<16>(s.hc, u, g, lds, st, ev);
-  else if (tm == 32) launch_decg<32>(s.hc, u, g, lds, st, ev);
-  else launch_decg<64>(s.hc, u, g, lds, st, ev);
+  const int nw = decg_waves(s.hc, s.hs);
+  const dim3 g((unsigned)(s.hs / decg_channels(s.hc, nw)), (unsigned)cdiv(f.M, (int64_t)tm));
+  const size_t lds = k2_decg_lds(s.hc, tm, s.r, nw);
+  if (tm == 16) launch_decg<16>(s.hc, nw, u, g, lds, st, ev);
+  else if (tm == 32) launch_decg<32>(s.hc, nw, u, g, lds, st, ev);
+  else launch_decg<64>(s.hc, nw, u, g, lds, st, ev);
   return (int)hipGetLastError();
 }
 
 template <int TM>
-static void launch_decg(int hc, const DecUpArgs& u, dim3 g, size_t lds, hipStream_t st, const hipEvent_t* ev) {
+static void launch_decg(int hc, int nw, const DecUpArgs& u, dim3 g, size_t lds, hipStream_t st, const hipEvent_t* ev) {
   switch (hc) {
-    case 1: klaunch_d(hcgr_k2_decg<1, TM>, g, dim3(64), lds, st, ev, u); break;
-    case 2: klaunch_d(hcgr_k2_decg<2, TM>, g, dim3(128), lds, st, ev, u); break;
-    case 4: klaunch_d(hcgr_k2_decg<4, TM>, g, dim3(256), lds, st, ev, u); break;
-    default: klaunch_d(hcgr_k2_decg<8, TM>, g, dim3(256), lds, st, ev, u); break;
+    case 1: klaunch_d(hcgr_k2_decg<1, TM, 1>, g, dim3(64), lds, st, ev, u); break;
+    case 2: klaunch_d(hcgr_k2_decg<2, TM, 2>, g, dim3(128), lds, st, ev, u); break;
+    case 4: klaunch_d(hcgr_k2_decg<4, TM, 4>, g, dim3(256), lds, st, ev, u); break;
+    default:
+      if (nw == 5) klaunch_d(hcgr_k2_decg<8, TM, 5>, g, dim3(320), lds, st, ev, u);
+      else klaunch_d(hcgr_k2_decg<8, TM, 4>, g, dim3(256), lds, st, ev, u);
+      break;
   }
 }
 
@@ -731,9 +758,9 @@ int launch_fused(const Shape& s, const Plan& p, const ForwardArgs& f, void* stre
     if ((e = hipEventRecord(ev[2], st)) != hipSuccess || (e = hipEventRecord(ev[3], st)) != hipSuccess) return (int)e;
   }
   const dim3 g2((unsigned)(s.hs / p.cb), (unsigned)p.ntiles);
-  const size_t lds = k2_decg_lds(s.hc, p.tm, s.r);
-  if (p.tm == 16) launch_decg<16>(s.hc, u, g2, lds, st, ev ? ev + 4 : nullptr);
-  else launch_decg<32>(s.hc, u, g2, lds, st, ev ? ev + 4 : nullptr);
+  const size_t lds = k2_decg_lds(s.hc, p.tm, s.r, p.upw);
+  if (p.tm == 16) launch_decg<16>(s.hc, p.upw, u, g2, lds, st, ev ? ev + 4 : nullptr);
+  else launch_decg<32>(s.hc, p.upw, u, g2, lds, st, ev ? ev + 4 : nullptr);
   return (int)hipGetLastError();
 }
 

@@ -69,13 +69,14 @@ constexpr size_t kCtrBytes = (size_t)kCtrSlots * kCtrStride * 4;  // 128 KiB
 enum KDVariant {
   KD_T16_R7_K1_C128 = 0, KD_T16_R1_K4_C512, KD_T16_R3_K1_C256, KD_T16_R3_K2_C512,
   KD_T32_R7_K1_C128, KD_T32_R1_K4_C512, KD_T32_R3_K1_C256, KD_T32_R3_K2_C512,
-  KD_T64_R7_K1_C128, KD_T64_R3_K1_C256, KD_T128_R7_K1_C128, KD_NVAR
+  KD_T64_R7_K1_C128, KD_T64_R3_K1_C256, KD_T128_R7_K1_C128, KD_T16_R4_K2_C512, KD_T32_R4_K2_C512, KD_NVAR
 };
 struct KDShape { int tm, rb, kw, kc; };
 inline KDShape kd_shape(int v) {
   static const KDShape t[KD_NVAR] = {{16, 7, 1, 128}, {16, 1, 4, 512}, {16, 3, 1, 256}, {16, 3, 2, 512},
                                      {32, 7, 1, 128}, {32, 1, 4, 512}, {32, 3, 1, 256}, {32, 3, 2, 512},
-                                     {64, 7, 1, 128}, {64, 3, 1, 256}, {128, 7, 1, 128}};
+                                     {64, 7, 1, 128}, {64, 3, 1, 256}, {128, 7, 1, 128}, {16, 4, 2, 512},
+                                     {32, 4, 2, 512}};
   return t[v];
 }
 // SPLIT-plan up kernel variants: token tile; kDecUpWaves waves of 4
@@ -96,11 +97,13 @@ inline size_t k2_dec_lds(int tm, int r) {
 }
 constexpr size_t kLdsPerCu = 160 * 1024;
 // Decode up kernel for HC streams: a wave's 16 MFMA rows are 16/HC channels x
-// HC streams; NW waves per workgroup (HC waves up to 4 in the fused plan's up
-// kernel, 4 in the persistent plan).
-inline int decg_waves(int hc) { return hc < 4 ? hc : 4; }
+// HC streams; NW waves per workgroup (HC waves up to 4 in the split and fused
+// plans' up kernel, 4 in the persistent plan). At HC = 8, when HS is a
+// multiple of 2560, five waves (10 channels): HS/10 workgroups fill whole
+// rounds of the 256 CUs, where eight channels (HS/8 = 320 at HS = 2560) left
+// 64 CUs with two workgroups' Wu rows.
+inline int decg_waves(int hc, int hs) { return hc < 4 ? hc : (hc == 8 && hs % 2560 == 0) ? 5 : 4; }
 inline int decg_channels(int hc, int nw) { return nw * (16 / hc); }
-inline int decg_channels(int hc) { return decg_channels(hc, decg_waves(hc)); }
 // Its LDS: Wu rows and the h tile, then the tile's R2 rows of its channels,
 // rrms and Wnorm (each rounded up to whole 1 KB direct-load instructions) and
 // a flag word.
@@ -110,7 +113,6 @@ inline size_t k2_decg_lds(int hc, int tm, int r, int nw) {
   return (size_t)(nw * 16 + tm) * (size_t)r * 2u + kb((size_t)tm * hc * cw * 2) + kb((size_t)tm * hc * 4) +
          kb((size_t)hc * cw * 2) + 16;
 }
-inline size_t k2_decg_lds(int hc, int tm, int r) { return k2_decg_lds(hc, tm, r, decg_waves(hc)); }
 // The reduction kernel gives each of a wave's 4 lane groups up to kRedMaxCpl
 // chunks per stream (instantiated: 1, 2, 3, 5, 8).
 constexpr int kRedMaxCpl = 8;
@@ -237,7 +239,7 @@ inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
   // while the 128-token down tile is 1.2 us faster than four 32-token ones)
   const int k2 = d.tm == 16 ? K2_T16 : d.tm == 64 ? K2_T64S : K2_T32;
   const int tm2 = k2_shape(k2).tm;
-  const size_t lds2 = s.hc == 4 ? k2_dec_lds(tm2, s.r) : k2_decg_lds(s.hc, tm2, s.r);
+  const size_t lds2 = s.hc == 4 ? k2_dec_lds(tm2, s.r) : k2_decg_lds(s.hc, tm2, s.r, decg_waves(s.hc, s.hs));
   if (s.hs % d.kc != 0 || s.hs / d.kc > 4 * kRedMaxCpl || lds2 > kLdsPerCu) return false;
   Plan p;
   p.M = M;
@@ -249,7 +251,7 @@ inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
   p.kcps = s.hs / d.kc;
   p.nkc = s.hc * p.kcps;
   p.ntiles_n = (s.nblk() + d.rb - 1) / d.rb;
-  p.cb = s.hc == 4 ? k2_shape(p.k2).nw * 4 : decg_channels(s.hc);  // up-kernel channels per workgroup
+  p.cb = s.hc == 4 ? k2_shape(p.k2).nw * 4 : decg_channels(s.hc, decg_waves(s.hc, s.hs));  // up-kernel channels per workgroup
   p.mpad = (M + p.tm - 1) / p.tm * p.tm;
   const size_t np = (size_t)s.np();
   p.off_p = kCtrBytes;
@@ -312,7 +314,7 @@ inline bool make_fused(const Shape& s, int64_t M, int tm, Plan* out, bool persis
   if (k1_fuse_lds(tm) > kLdsPerCu) return false;
   if (persist) {
     if (ntiles > kExitSlot - kReadySlot || k2_decg_lds(s.hc, tm, s.r, 4) > kLdsPerCu) return false;
-  } else if (k2_decg_lds(s.hc, tm, s.r) > kLdsPerCu) {
+  } else if (k2_decg_lds(s.hc, tm, s.r, decg_waves(s.hc, s.hs)) > kLdsPerCu) {
     return false;
   }
   Plan p;
@@ -322,7 +324,7 @@ inline bool make_fused(const Shape& s, int64_t M, int tm, Plan* out, bool persis
   p.kcps = kcps;
   p.nkc = nkc;
   p.ntiles = (int)ntiles;
-  p.upw = persist ? 4 : decg_waves(s.hc);
+  p.upw = persist ? 4 : decg_waves(s.hc, s.hs);
   p.cb = decg_channels(s.hc, p.upw);
   p.mpad = ntiles * tm;
   p.off_p = kCtrBytes;
@@ -403,14 +405,16 @@ inline Plan make_plan(const Shape& s, int64_t M) {
     // 7-row blocks up to 64 tokens (HC = 1: 10.8-12.0 us at M = 1..64, against
     // 11.8-14.6 for the fused plan and 23.6 for the tile plan at 64; HC = 2:
     // 11.8-14.4 us), then 32-token tiles (13.9 and 17.2 us at 128); from 160
-    // chunks (HC = 8) 512-column chunks: one row block with four k waves at
-    // M <= 8 (17.8 us), 3-row blocks with two k waves above (18.9 us at 16,
-    // 22.7 at 32 on 32-token tiles, 29.2 at 64, against 26.1, 26.8, 28.8 and
-    // 32.5 for the tile plan)
+    // chunks (HC = 8) 512-column chunks in 4-row blocks with two k waves,
+    // 16-token tiles up to 16 tokens: 6 row tiles x 40 chunks = 240
+    // workgroups on the 256 CUs, where 3-row blocks (7 x 40 = 280) left 24
+    // CUs with two (16.6 against 17.9-18.2 us at M = 8, 16.8 against 18.2 at
+    // 16, 19.6 against 21.5 at 32 and 24.9 against 27.4 at 64; one row block
+    // with four k waves, 840 workgroups: 18.2 at M = 8)
     const int64_t c128 = s.k() / 128;
     int kd;
     if (c128 <= 40) kd = M <= 64 ? KD_T16_R7_K1_C128 : KD_T32_R7_K1_C128;
-    else if (c128 >= 160) kd = M <= 8 ? KD_T16_R1_K4_C512 : M <= 16 ? KD_T16_R3_K2_C512 : KD_T32_R3_K2_C512;
+    else if (c128 >= 160) kd = M <= 16 ? KD_T16_R4_K2_C512 : KD_T32_R4_K2_C512;
     else kd = M <= 16 ? KD_T16_R7_K1_C128 : KD_T32_R7_K1_C128;
     if (make_split(s, M, kd, &p) || make_split(s, M, M <= 16 ? KD_T16_R3_K2_C512 : KD_T32_R3_K2_C512, &p)) return p;
   }

@@ -2110,6 +2110,8 @@ static void launch_kd_variant(int v, const DownArgs& d, dim3 grid, hipStream_t s
     case KD_T32_R3_K2_C512: launch_kd<32, 3, 2, 512>(d, grid, st, ev); break;
     case KD_T64_R7_K1_C128: launch_kd<64, 7, 1, 128>(d, grid, st, ev); break;
     case KD_T128_R7_K1_C128: launch_kd<128, 7, 1, 128>(d, grid, st, ev); break;
+    case KD_T16_R4_K2_C512: launch_kd<16, 4, 2, 512>(d, grid, st, ev); break;
+    case KD_T32_R4_K2_C512: launch_kd<32, 4, 2, 512>(d, grid, st, ev); break;
     default: launch_kd<64, 3, 1, 256>(d, grid, st, ev); break;
   }
 }

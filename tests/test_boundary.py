@@ -33,6 +33,17 @@ def test_header_declares_the_api():
         assert n in names
 
 
+def test_binding_constants_match_the_header():
+    """Every integer #define of include/hcgr.h that the binding also defines
+    has the same value there (plan kinds, variant counts, status codes...)."""
+    import re
+    defs = dict(re.findall(r"^#define (HCGR_\w+)\s+\(?(-?\d+)\)?", open(HEADER).read(), re.M))
+    shared = [k for k in defs if hasattr(H, k)]
+    assert "HCGR_SPLIT_VARIANTS" in shared and "HCGR_PLAN_PERSISTENT" in shared
+    for k in shared:
+        assert getattr(H, k) == int(defs[k]), k
+
+
 def test_every_declared_symbol_is_exported(lib):
     for n in declared_functions():
         assert hasattr(lib, n), n

@@ -81,6 +81,27 @@ def test_stream_counts_merged_folded(H, hc, M):
     o.close()
 
 
+@pytest.mark.parametrize("kind", [None, 4])
+@pytest.mark.parametrize("full", [False, True])
+@pytest.mark.parametrize("M", [1, 17, 32])
+def test_hc8_ten_channel_up_kernel(H, kind, full, M):
+    """HC = 8 at HS = 2560: the decode up kernel runs five waves of two
+    channels (10 channels per workgroup, 256 workgroups), whose R2 rows and
+    Wnorm arrive in 4-byte pieces; split plan (heuristic) and fused plan, Wnorm
+    per channel or per element, 16- and 32-token tiles; every row against the
+    oracle."""
+    hs, r = 2560, 320
+    _say(f"[streams] hc=8 ten-channel up kernel M={M} full={full} kind={kind}")
+    cfg = H.Config(hc=8, hs=hs, r=r, wnorm_len=8 * hs if full else 0)
+    o = H.HCGR(cfg, 0, plan_table=[] if kind is None else [{"tokens": M, "kind": kind, "down_variant": int(M > 16)}])
+    assert "waves=5 channels=10 grid=256" in o.describe(M), o.describe(M)
+    inp = synth.make_inputs(M, synth.Shape(hc=8, hs=hs, r=r), seed=120 + M, device="cuda", wnorm_full=full)
+    out = o.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"])
+    torch.cuda.synchronize()
+    check_all(out, oracle_forward(oracle.OracleConfig(hc=8, hs=hs, r=r, wnorm_full=full), inp))
+    o.close()
+
+
 @pytest.mark.parametrize("hc", [2, 8])
 def test_stream_counts_full_width_wnorm(H, hc):
     hs, r, M = 512, 160, 40

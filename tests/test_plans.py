@@ -80,7 +80,7 @@ def test_choice_that_cannot_run_falls_back(lib):
     [tile(0)],                                             # key < 1
     [dict(tile(64), kind=7)],                              # unknown kind
     [split(512, 0)],                                       # decode plan above 256 tokens
-    [split(32, 11)],                                       # no such down variant
+    [split(32, H.HCGR_SPLIT_VARIANTS)],                     # no such down variant
     [tile(64, seg=3)],                                     # 3 does not divide HS/128 = 20
     [tile(64, spw=4, seg=2)],                              # segments with four streams per workgroup
     [tile(64, spw=2)],
