@@ -295,7 +295,7 @@ static void describe(const hcgr::Shape& s, const hcgr::Plan& p, int64_t M, char*
                "workspace=%zu",
                (long long)M, (long long)p.mpad, a.tm, a.rb, a.kw, p.kc, p.nkc, p.ntiles_n, p.ntiles_n * p.nkc,
                (long long)(p.mpad / p.tm), (long long)(s.n_rows() * (p.mpad / 16)), s.hc == 4 ? "k2_dec" : "k2_decg",
-               b.tm, s.hc == 4 ? b.nw : hcgr::decg_waves(s.hc, s.hs), p.cb, s.hs / p.cb,
+               b.tm, s.hc == 4 ? (p.cb + 3) / 4 : hcgr::decg_waves(s.hc, s.hs), p.cb, s.hs / p.cb,
                (long long)hcgr::cdiv(M, (int64_t)b.tm), p.ws_bytes);
     } else if (p.kind == hcgr::PLAN_TILE) {
       hcgr::KTShape t = hcgr::kt_shape(p.kt);

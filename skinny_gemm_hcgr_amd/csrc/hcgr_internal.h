@@ -79,20 +79,31 @@ inline KDShape kd_shape(int v) {
                                      {32, 4, 2, 512}};
   return t[v];
 }
-// SPLIT-plan up kernel variants: token tile; kDecUpWaves waves of 4
-// channels x 4 streams each per workgroup.
-constexpr int kDecUpWaves = 4;
+// SPLIT-plan up kernel variants (HC = 4): token tile; the workgroup's
+// channels come from the stream width (dec_up_channels), a wave per 4.
 enum K2Variant { K2_T16 = 0, K2_T32 = 1, K2_T64S = 2, K2_NVAR };
-struct K2Shape { int tm, nw, rbw; };
+struct K2Shape { int tm; };
 inline K2Shape k2_shape(int v) {
-  static const K2Shape t[K2_NVAR] = {{16, kDecUpWaves, 1}, {32, kDecUpWaves, 1}, {64, kDecUpWaves, 1}};
+  static const K2Shape t[K2_NVAR] = {{16}, {32}, {64}};
   return t[v];
 }
-// Dynamic LDS of the SPLIT-plan up kernel for a token tile of tm and rank r:
-// the workgroup's Wu rows and the h tile, the tile's R2 rows of its
-// channels, rrms and Wnorm; it must fit the 160 KB of one CU.
-inline size_t k2_dec_lds(int tm, int r) {
-  return (size_t)(kDecUpWaves * 16 + tm) * (size_t)r * 2u + (size_t)tm * 4 * (kDecUpWaves * 4) * 2u +
+// Channels per workgroup of the HC = 4 decode up kernel for M tokens in
+// tiles of tm: 10 where HS is a multiple of 2560 (HS / 10 workgroups per
+// token tile fill whole rounds of the 256 CUs) while the grid stays within
+// the two workgroups per CU that run at once, else 16. Measured on MI355X at
+// HS = 2560: 10 channels take 0.12 us off the up kernel at M = 32 and 0.45
+// at M = 48 and 64 (one or two tiles), are level at M = 1 to 16, and 2 us
+// slower at M = 96, where 768 workgroups of 10 channels need a second round
+// and 480 of 16 do not.
+inline int dec_up_channels(int hs, int64_t M, int tm) {
+  return hs % 2560 == 0 && (int64_t)(hs / 10) * ((M + tm - 1) / tm) <= 2 * 256 ? 10 : 16;
+}
+// Dynamic LDS of the SPLIT-plan up kernel for a token tile of tm, rank r and
+// cw channels: the workgroup's Wu rows (4 per channel, whole waves of 16) and
+// the h tile, the tile's R2 rows of its channels (whole KB), rrms and Wnorm;
+// it must fit the 160 KB of one CU.
+inline size_t k2_dec_lds(int tm, int r, int cw) {
+  return (size_t)((cw + 3) / 4 * 16 + tm) * (size_t)r * 2u + ((size_t)tm * 4 * cw * 2u + 1023) / 1024 * 1024 +
          (size_t)(tm > 64 ? tm : 64) * 16 + 1024;
 }
 constexpr size_t kLdsPerCu = 160 * 1024;
@@ -239,7 +250,8 @@ inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
   // while the 128-token down tile is 1.2 us faster than four 32-token ones)
   const int k2 = d.tm == 16 ? K2_T16 : d.tm == 64 ? K2_T64S : K2_T32;
   const int tm2 = k2_shape(k2).tm;
-  const size_t lds2 = s.hc == 4 ? k2_dec_lds(tm2, s.r) : k2_decg_lds(s.hc, tm2, s.r, decg_waves(s.hc, s.hs));
+  const int cw2 = s.hc == 4 ? dec_up_channels(s.hs, M, tm2) : decg_channels(s.hc, decg_waves(s.hc, s.hs));
+  const size_t lds2 = s.hc == 4 ? k2_dec_lds(tm2, s.r, cw2) : k2_decg_lds(s.hc, tm2, s.r, decg_waves(s.hc, s.hs));
   if (s.hs % d.kc != 0 || s.hs / d.kc > 4 * kRedMaxCpl || lds2 > kLdsPerCu) return false;
   Plan p;
   p.M = M;
@@ -251,7 +263,7 @@ inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
   p.kcps = s.hs / d.kc;
   p.nkc = s.hc * p.kcps;
   p.ntiles_n = (s.nblk() + d.rb - 1) / d.rb;
-  p.cb = s.hc == 4 ? k2_shape(p.k2).nw * 4 : decg_channels(s.hc, decg_waves(s.hc, s.hs));  // up-kernel channels per workgroup
+  p.cb = cw2;  // up-kernel channels per workgroup
   p.mpad = (M + p.tm - 1) / p.tm * p.tm;
   const size_t np = (size_t)s.np();
   p.off_p = kCtrBytes;

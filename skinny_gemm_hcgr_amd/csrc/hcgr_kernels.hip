@@ -305,8 +305,12 @@ __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
 // ---------------------------------------------------------------------------
 // hcgr_k2_dec (SPLIT plan, decode sizes): (G2) gate = h . Wu^T, G =
 // sigmoid(gate), (MIX) x[c] = 1/4 sum_s G xn, for a token tile of TM tokens
-// and 16 channels x 4 streams, 4 waves. The workgroup's 64 Wu rows (r values
-// each) and its h tile arrive in LDS by direct global->LDS loads (wide 1 KB
+// and CW channels x 4 streams, ceil(CW/4) waves: CW = 16, or 10 where HS is
+// a multiple of 2560 (HS/10 workgroups fill whole rounds of the 256 CUs; the
+// last wave's rows of channels past CW read as zero and store nothing, and
+// the R2 rows and Wnorm of 10 channels arrive in 4-byte pieces). The
+// workgroup's Wu rows (r values each) and its h tile arrive in LDS by direct
+// global->LDS loads (wide 1 KB
 // instructions instead of per-lane fragment loads); inside a row the 16-byte
 // chunk c sits in slot (c & ~3) | ((c ^ row) & 3), which spreads the 16-row
 // fragment reads over the banks. The epilogue's R2 rows, rrms and Wnorm
@@ -329,30 +333,31 @@ struct UpArgs {
   uint16_t* x;
 };
 
-template <int TM, int NW>
-__global__ __launch_bounds__(NW * 64) void hcgr_k2_dec(UpArgs a) {
+template <int TM, int CW>
+__global__ __launch_bounds__((CW + 3) / 4 * 64) void hcgr_k2_dec(UpArgs a) {
+  constexpr int NW = (CW + 3) / 4;
   constexpr int NTB = TM / 16;
-  constexpr int WR = NW * 16;  // Wu rows of the workgroup (NW * 4 channels x 4 streams)
+  constexpr int WR = NW * 16;  // Wu rows of the workgroup (NW * 4 channels x 4 streams, the last CW..4NW-1 zero)
   extern __shared__ __attribute__((aligned(1024))) uint8_t dl[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t m0 = (int64_t)blockIdx.y * TM;
   const int rows = (int)min((int64_t)TM, a.M - m0);
-  // channel groups of NW*4 channels; workgroup x goes to XCD x % 8 (the
+  // channel groups of CW channels; workgroup x goes to XCD x % 8 (the
   // dispatcher's round robin), so XCD k takes a contiguous run of groups and
   // the groups that share a 128-byte line of R2 or x share that XCD's L2
-  const int ncg = (int)gridDim.x;  // HS / 16: a multiple of 8 for every accepted HS
+  const int ncg = (int)gridDim.x;  // HS / CW: a multiple of 8 for every accepted HS
   const int cg = (ncg & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * (ncg >> 3) + (blockIdx.x >> 3));
-  const int cbase = cg * (NW * 4);
+  const int cbase = cg * CW;
   const int cpr = a.r / 8;  // 16-byte chunks per row (a multiple of 4)
   const uint32_t rowb = (uint32_t)a.r * 2u;
-  constexpr int CW = NW * 4;              // channels of the workgroup
   constexpr int RRB = (TM > 64 ? TM : 64) * 16;  // rrms slot: one 16-byte lane per token, 64 lanes at least
   uint8_t* wl = dl;              // [WR][r]: row 4*cl + s = stream s of channel cbase + cl
   uint8_t* hl = dl + WR * rowb;  // [TM][r]
-  uint8_t* r2l = hl + TM * rowb;  // [TM][4 streams][CW channels] bf16
-  uint8_t* rrl = r2l + TM * 4 * CW * 2;  // [TM][4] float
+  constexpr int R2B = (TM * 4 * CW * 2 + 1023) / 1024 * 1024;
+  uint8_t* r2l = hl + TM * rowb;  // [TM][4 streams][CW channels] bf16, in whole KB
+  uint8_t* rrl = r2l + R2B;       // [TM][4] float
   uint8_t* wnl = rrl + RRB;              // [4 streams or 1][CW] bf16 (1 KB slot)
   const rsrc_t rWu = make_rsrc(a.wu, (uint32_t)a.K * rowb);
   const rsrc_t rH = make_rsrc(a.h + m0 * a.r, (uint32_t)rows * rowb);  // rows past M read as zero
@@ -361,11 +366,14 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k2_dec(UpArgs a) {
   const rsrc_t rWn = make_rsrc(a.wn, (uint32_t)(a.wn_full ? a.K : a.HS) * 2u);
 
   // global -> LDS: instruction i fills LDS chunks [64 i, 64 i + 64) of a
-  // block; WR*cpr and TM*cpr are multiples of 64
-  for (int i = wave; i * 64 < WR * cpr; i += NW) {
+  // block; WR*cpr and TM*cpr are multiples of 64. Wu rows of channels past
+  // CW feed only MFMA rows whose results are not stored: the loads stop at
+  // the instruction that holds the last real row's chunks.
+  for (int i = wave; i * 64 < 4 * CW * cpr; i += NW) {
     const int q = i * 64 + lane, row = q / cpr, sl = q % cpr;
     const int c = (sl & ~3) | ((sl ^ row) & 3);  // the chunk this slot holds
-    const uint32_t off = (uint32_t)((row & 3) * a.HS + cbase + (row >> 2)) * rowb + (uint32_t)c * 16u;
+    const bool pad = CW % 4 != 0 && (row >> 2) >= CW;  // rows of channels past CW read zeros
+    const uint32_t off = pad ? 0x80000000u : (uint32_t)((row & 3) * a.HS + cbase + (row >> 2)) * rowb + (uint32_t)c * 16u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rWu, (lds_void_t*)(wl + i * 1024), 16, off, 0, 0, 0);
   }
   for (int i = wave; i * 64 < TM * cpr; i += NW) {
@@ -375,22 +383,36 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k2_dec(UpArgs a) {
                                              0, 0, 0);
   }
   // epilogue operands, also global -> LDS: the tile's R2 rows of the
-  // workgroup's channels (lane: token q / 8, stream (q / 2) % 4, half q % 2),
-  // its rrms rows and the channels' Wnorm
-  static_assert(TM % 8 == 0 && CW == 16, "R2 slots: 8 per token, 64 per instruction");
-  for (int i = wave; i < TM / 8; i += NW) {
-    const int q = i * 64 + lane, t = q >> 3, sq = (q >> 1) & 3;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rR2, (lds_void_t*)(r2l + i * 1024), 16,
-        (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)(sq * a.HS + cbase + (q & 1) * 8) * 2u, 0, 0, 0);
+  // workgroup's channels, its rrms rows and the channels' Wnorm
+  static_assert(TM % 8 == 0 && (CW == 16 || CW == 10), "R2 slots: 8 (16 channels) or 20 (10) per token");
+  if constexpr (CW == 16) {  // 16-byte pieces (lane: token q / 8, stream (q / 2) % 4, half q % 2)
+    for (int i = wave; i < TM / 8; i += NW) {
+      const int q = i * 64 + lane, t = q >> 3, sq = (q >> 1) & 3;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rR2, (lds_void_t*)(r2l + i * 1024), 16,
+          (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)(sq * a.HS + cbase + (q & 1) * 8) * 2u, 0, 0, 0);
+    }
+  } else {  // 4-byte pieces (lane: token q / 20, stream (q / 5) % 4, channel pair q % 5); TM * 20 = 64 * TM / 16 * 5
+    for (int i = wave; i * 64 < TM * 20; i += NW) {
+      const int q = i * 64 + lane, t = q / 20, sq = (q / 5) % 4, pc = q % 5;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rR2, (lds_void_t*)(r2l + i * 256), 4,
+          (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)(sq * a.HS + cbase + pc * 2) * 2u, 0, 0, 0);
+    }
   }
   if (wave == 0) {
     for (int i = 0; i * 64 < TM; ++i)  // lanes past the tile read zeros into the slot
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rRr, (lds_void_t*)(rrl + i * 1024), 16,
                                                (uint32_t)(i * 64 + lane) * 16u, 0, 0, 0);
-    const bool live = lane < (a.wn_full ? 8 : 2);
-    const uint32_t wo = (uint32_t)((a.wn_full ? (lane >> 1) * a.HS : 0) + cbase + (lane & 1) * 8) * 2u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWn, (lds_void_t*)wnl, 16, live ? wo : 0x80000000u, 0, 0, 0);
+    if constexpr (CW == 16) {
+      const bool live = lane < (a.wn_full ? 8 : 2);
+      const uint32_t wo = (uint32_t)((a.wn_full ? (lane >> 1) * a.HS : 0) + cbase + (lane & 1) * 8) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rWn, (lds_void_t*)wnl, 16, live ? wo : 0x80000000u, 0, 0, 0);
+    } else {
+      const bool live = lane < (a.wn_full ? 20 : 5);
+      const uint32_t wo = (uint32_t)((a.wn_full ? (lane / 5) * a.HS : 0) + cbase + (lane % 5) * 2) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rWn, (lds_void_t*)wnl, 4, live ? wo : 0x80000000u, 0, 0, 0);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_sync();  // every wave's global->LDS loads have landed
@@ -443,7 +465,7 @@ __global__ __launch_bounds__(NW * 64) void hcgr_k2_dec(UpArgs a) {
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb) {
     const int64_t m = m0 + tb * 16 + (lane & 15);
-    if (m < a.M) {
+    if (m < a.M && (CW % 4 == 0 || cl < CW)) {
       float sum = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) sum = fmaf(sigmoid_f(acc[tb][q]), pr2[tb][q] * prr[tb][q] * pone[q], sum);
@@ -2140,9 +2162,9 @@ static void launch_kf(const FullArgs& f, dim3 grid, hipStream_t st, const hipEve
 int configure_kernels() {
   const int lim = (int)kLdsPerCu;  // make_split keeps k2_dec_lds within it
   hipError_t e;
-  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<16, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
-  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<32, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
-  if ((e = hipFuncSetAttribute((const void*)hcgr_k2_dec<64, kDecUpWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
+  for (const void* k : {(const void*)hcgr_k2_dec<16, 16>, (const void*)hcgr_k2_dec<32, 16>, (const void*)hcgr_k2_dec<64, 16>,
+                        (const void*)hcgr_k2_dec<16, 10>, (const void*)hcgr_k2_dec<32, 10>, (const void*)hcgr_k2_dec<64, 10>})
+    if ((e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(2))) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<3>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(3))) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(4))) != hipSuccess) return (int)e;
@@ -2201,13 +2223,21 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   // the up kernel's token tiles: every one starts below M (with a smaller
   // tile than the down kernel's, p.mpad / tm2 tiles would not)
   const int tm2 = k2_shape(p.k2).tm;
-  const size_t lds = k2_dec_lds(tm2, s.r);
+  const size_t lds = k2_dec_lds(tm2, s.r, p.cb);
   const dim3 g2((unsigned)(s.hs / p.cb), (unsigned)cdiv(f.M, (int64_t)tm2));
-  const dim3 b2(kDecUpWaves * 64);
-  switch (p.k2) {
-    case K2_T16: klaunch(hcgr_k2_dec<16, kDecUpWaves>, g2, b2, lds, st, tm.stage(2), u); break;
-    case K2_T32: klaunch(hcgr_k2_dec<32, kDecUpWaves>, g2, b2, lds, st, tm.stage(2), u); break;
-    default: klaunch(hcgr_k2_dec<64, kDecUpWaves>, g2, b2, lds, st, tm.stage(2), u); break;
+  const dim3 b2((unsigned)((p.cb + 3) / 4 * 64));
+  if (p.cb == 10) {
+    switch (p.k2) {
+      case K2_T16: klaunch(hcgr_k2_dec<16, 10>, g2, b2, lds, st, tm.stage(2), u); break;
+      case K2_T32: klaunch(hcgr_k2_dec<32, 10>, g2, b2, lds, st, tm.stage(2), u); break;
+      default: klaunch(hcgr_k2_dec<64, 10>, g2, b2, lds, st, tm.stage(2), u); break;
+    }
+  } else {
+    switch (p.k2) {
+      case K2_T16: klaunch(hcgr_k2_dec<16, 16>, g2, b2, lds, st, tm.stage(2), u); break;
+      case K2_T32: klaunch(hcgr_k2_dec<32, 16>, g2, b2, lds, st, tm.stage(2), u); break;
+      default: klaunch(hcgr_k2_dec<64, 16>, g2, b2, lds, st, tm.stage(2), u); break;
+    }
   }
   return (int)hipGetLastError();
 }

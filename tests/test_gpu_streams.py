@@ -102,6 +102,31 @@ def test_hc8_ten_channel_up_kernel(H, kind, full, M):
     o.close()
 
 
+@pytest.mark.parametrize("full", [False, True])
+@pytest.mark.parametrize("hs,M,kd,cw", [(2560, 1, 0, 10), (2560, 17, 4, 10), (2560, 64, 8, 10), (2560, 45, 8, 10),
+                                        (2560, 30, 0, 10), (5120, 9, 1, 10), (2560, 90, 4, 16), (1280, 30, 4, 16),
+                                        (1280, 64, 8, 16)])
+def test_hc4_up_kernel_channel_groups(H, full, hs, M, kd, cw):
+    """HC = 4 decode up kernel: 10 channels per workgroup (three waves, the
+    last one's rows past the tenth channel zero, R2 rows and Wnorm in 4-byte
+    pieces) where HS is a multiple of 2560 and the grid fits two workgroups
+    per CU, else 16 (four waves: HS = 2560 in three 32-token tiles, HS =
+    1280); 16-, 32- and 64-token tiles, a ragged last tile, two tiles of 16,
+    Wnorm per channel or per element; every row against the oracle."""
+    r = 320
+    _say(f"[streams] hc=4 up kernel hs={hs} M={M} kd={kd} full={full}")
+    table = [{"tokens": M, "kind": H.HCGR_PLAN_SPLIT, "down_variant": kd, "streams_per_wg": 0, "segments": 0,
+              "up_variant": 0, "ranges": 0}]
+    o = H.HCGR(H.Config(hc=4, hs=hs, r=r, wnorm_len=4 * hs if full else 0), 0, plan_table=table)
+    desc = o.describe(M)
+    assert f"k2_dec tm={(16, 32, 64)[kd // 4]} waves={(cw + 3) // 4} channels={cw} grid={hs // cw}x" in desc, desc
+    inp = synth.make_inputs(M, synth.Shape(hc=4, hs=hs, r=r), seed=140 + M, device="cuda", wnorm_full=full)
+    out = o.forward(inp["R"], inp["y"], inp["inj"], inp["wnorm"], inp["wd"], inp["wi"], inp["wu"])
+    torch.cuda.synchronize()
+    check_all(out, oracle_forward(oracle.OracleConfig(hc=4, hs=hs, r=r, wnorm_full=full), inp))
+    o.close()
+
+
 @pytest.mark.parametrize("hc", [2, 8])
 def test_stream_counts_full_width_wnorm(H, hc):
     hs, r, M = 512, 160, 40
