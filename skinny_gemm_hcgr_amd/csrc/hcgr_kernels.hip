@@ -251,7 +251,7 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
 template <int HC, int CPL>
 __global__ __launch_bounds__(256) void hcgr_k1_reduce(ReduceArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int64_t mblocks = a.Mpad / 16;
   const int n = (int)(wid / mblocks);
   if (n >= a.n_rows) return;  // whole wave leaves together
@@ -2138,21 +2138,32 @@ static void launch_kd_variant(int v, const DownArgs& d, dim3 grid, hipStream_t s
   }
 }
 template <int HC>
-static void launch_reduce_hc(int cpl, const ReduceArgs& r, dim3 grid, hipStream_t st, const hipEvent_t* ev) {
+static void launch_reduce_hc(int cpl, const ReduceArgs& r, dim3 grid, dim3 block, hipStream_t st, const hipEvent_t* ev) {
   switch (cpl) {
-    case 1: klaunch(hcgr_k1_reduce<HC, 1>, grid, dim3(256), 0, st, ev, r); break;
-    case 2: klaunch(hcgr_k1_reduce<HC, 2>, grid, dim3(256), 0, st, ev, r); break;
-    case 3: klaunch(hcgr_k1_reduce<HC, 3>, grid, dim3(256), 0, st, ev, r); break;
-    case 5: klaunch(hcgr_k1_reduce<HC, 5>, grid, dim3(256), 0, st, ev, r); break;
-    default: klaunch(hcgr_k1_reduce<HC, 8>, grid, dim3(256), 0, st, ev, r); break;
+    case 1: klaunch(hcgr_k1_reduce<HC, 1>, grid, block, 0, st, ev, r); break;
+    case 2: klaunch(hcgr_k1_reduce<HC, 2>, grid, block, 0, st, ev, r); break;
+    case 3: klaunch(hcgr_k1_reduce<HC, 3>, grid, block, 0, st, ev, r); break;
+    case 5: klaunch(hcgr_k1_reduce<HC, 5>, grid, block, 0, st, ev, r); break;
+    default: klaunch(hcgr_k1_reduce<HC, 8>, grid, block, 0, st, ev, r); break;
   }
 }
-static void launch_reduce(int hc, int cpl, const ReduceArgs& r, dim3 grid, hipStream_t st, const hipEvent_t* ev = nullptr) {
+// waves: one per (row, 16 tokens); blocks of 1, 2 or 4 of them, the fewest
+// that keep the grid within 704 workgroups. Measured on MI355X (HS = 2560,
+// r = 320, whole calls back to back) against four-wave blocks throughout:
+// 0.3-0.45 us less per call at M = 32 for HC = 1, 2, 4 and 8 (about 650
+// one-wave blocks; HC = 4: 14.29 -> 13.96 us), 0.07-0.27 at M = 1..16,
+// 0.16-0.29 with two-wave blocks at 1000-1300 waves except HC = 4, M = 64
+// (0.2 more); the reduction kernel's own event time does not change, the
+// gain is in the hand-over to the next kernel. One-wave blocks at 2000
+// waves and more were 0.6-1.5 us slower.
+static void launch_reduce(int hc, int cpl, const ReduceArgs& r, int64_t waves, hipStream_t st, const hipEvent_t* ev = nullptr) {
+  const int wpb = waves <= 704 ? 1 : waves <= 2 * 704 ? 2 : 4;
+  const dim3 grid((unsigned)cdiv(waves, (int64_t)wpb)), block((unsigned)(64 * wpb));
   switch (hc) {
-    case 1: launch_reduce_hc<1>(cpl, r, grid, st, ev); break;
-    case 2: launch_reduce_hc<2>(cpl, r, grid, st, ev); break;
-    case 8: launch_reduce_hc<8>(cpl, r, grid, st, ev); break;
-    default: launch_reduce_hc<4>(cpl, r, grid, st, ev); break;
+    case 1: launch_reduce_hc<1>(cpl, r, grid, block, st, ev); break;
+    case 2: launch_reduce_hc<2>(cpl, r, grid, block, st, ev); break;
+    case 8: launch_reduce_hc<8>(cpl, r, grid, block, st, ev); break;
+    default: launch_reduce_hc<4>(cpl, r, grid, block, st, ev); break;
   }
 }
 template <int TM, int NW, int BPW, int KS>
@@ -2211,7 +2222,7 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   r.eps = s.eps; r.inv_hc = 1.0f / (float)s.hc; r.inv_hs = 1.0f / (float)s.hs;
   r.rrms = f.rrms; r.h = H; r.inj_next = f.inj_next; r.ld_inj_next = f.ld_inj_next;
   const int64_t waves = (int64_t)s.n_rows() * (p.mpad / 16);
-  launch_reduce(s.hc, red_cpl(p.kcps), r, dim3((unsigned)((waves + 3) / 4)), st, tm.stage(1));
+  launch_reduce(s.hc, red_cpl(p.kcps), r, waves, st, tm.stage(1));
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (s.hc != 4)  // the stream-generic decode up kernel
     return launch_decg_up(s, k2_shape(p.k2).tm, H, f, st, reinterpret_cast<void* const*>(tm.stage(2)));
