@@ -14,11 +14,14 @@ rounds; it becomes the key's entry unless the heuristic is within 4% of it
 (the run-to-run spread measured on MI355X is 2-4%) or it is the heuristic's
 own plan (then the entry is marked heuristic).
 Timing: median of rounds of ``--reps`` back-to-back calls, rotating over
-enough complete sets (inputs, outputs and weights) that together exceed the
-256 MB Infinity Cache, as the benchmark does: with one set at a few thousand
-tokens R2 stays cached between calls, which favours plans that rely on it
-(at M = 4096 the staged up kernel read 7% faster than the heuristic that
-way and 5% slower on cold sets). The table is written
+enough complete sets (inputs, outputs, weights and workspace) that together
+exceed the 256 MB Infinity Cache, as the benchmark does: with one set at a
+few thousand tokens R2 stays cached between calls, which favours plans that
+rely on it (at M = 4096 the staged up kernel read 7% faster than the
+heuristic that way and 5% slower on cold sets), and a workspace shared by
+the sets keeps the chunk partials cached, which favours plans with more of
+them (at M = 4096 a two-segment plan read 4% faster than the heuristic with
+one workspace and 1-3% slower with one per set). The table is written
 atomically, and not at all if any key is left without a passing candidate.
 The table format and the lookup rule (nearest key in log space, the
 heuristic below the smallest key) follow the tuned table of the aiter pull
@@ -100,11 +103,12 @@ def tune(cfg, tokens, reps=30, seed=0, log=print):
         cands = H.hcgr_plan_candidates(cfg, M)
         choices = [{"tokens": M, "kind": H.HCGR_PLAN_HEURISTIC}] + cands
         need = max(H.hcgr_workspace_size_table(cfg, [c], M) for c in choices)
-        ws = H.new_workspace(need)
+        wss = [H.new_workspace(need) for _ in range(nset)]  # one per set, as the benchmark's
         outs = sets[0][2]  # the set every plan's result is checked on
 
         def run(i):
             inp, w, o = sets[i % nset]
+            ws = wss[i % nset]
             H.hcgr_forward(op.handle, inp["R"], inp["y"], inp["inj"], inp["inj"].stride(0), w["wnorm"], w["wd"],
                            w["wi"], w["wu"], M, o["R2"], o["rrms"], o["inj_next"], o["ld_inj_next"],
                            o["x"], ws, ws.numel(), stream)
@@ -163,7 +167,7 @@ def tune(cfg, tokens, reps=30, seed=0, log=print):
         entries.append(entry)
         log(f"[tune] M={M}: heuristic {heur_us:.2f} us, chosen {best_us:.2f} us "
             f"({'heuristic' if entry['kind'] == H.HCGR_PLAN_HEURISTIC else H.hcgr_plan_lookup(cfg, [entry], M)[1]})")
-        del ws, outs, sets
+        del wss, outs, sets
         torch.cuda.empty_cache()
     op.close()
     return entries, failures
