@@ -87,17 +87,6 @@ inline K2Shape k2_shape(int v) {
   static const K2Shape t[K2_NVAR] = {{16}, {32}, {64}};
   return t[v];
 }
-// Channels per workgroup of the HC = 4 decode up kernel for M tokens in
-// tiles of tm: 10 where HS is a multiple of 2560 (HS / 10 workgroups per
-// token tile fill whole rounds of the 256 CUs) while the grid stays within
-// the two workgroups per CU that run at once, else 16. Measured on MI355X at
-// HS = 2560: 10 channels take 0.12 us off the up kernel at M = 32 and 0.45
-// at M = 48 and 64 (one or two tiles), are level at M = 1 to 16, and 2 us
-// slower at M = 96, where 768 workgroups of 10 channels need a second round
-// and 480 of 16 do not.
-inline int dec_up_channels(int hs, int64_t M, int tm) {
-  return hs % 2560 == 0 && (int64_t)(hs / 10) * ((M + tm - 1) / tm) <= 2 * 256 ? 10 : 16;
-}
 // Dynamic LDS of the SPLIT-plan up kernel for a token tile of tm, rank r and
 // cw channels: the workgroup's Wu rows (4 per channel, whole waves of 16) and
 // the h tile, the tile's R2 rows of its channels (whole KB), rrms and Wnorm;
@@ -107,6 +96,27 @@ inline size_t k2_dec_lds(int tm, int r, int cw) {
          (size_t)(tm > 64 ? tm : 64) * 16 + 1024;
 }
 constexpr size_t kLdsPerCu = 160 * 1024;
+// Channels per workgroup of the HC = 4 decode up kernel for M tokens in
+// tiles of tm (rank r): 10 where HS is a multiple of 2560 (HS / 10
+// workgroups per token tile fill whole rounds of the 256 CUs) unless they
+// need more rounds than 16 channels, a round being the workgroups that fit
+// the CUs' LDS at once; else 16. Measured on MI355X at HS = 2560, r = 320
+// (up kernel): 10 channels take 0.12 us off at M = 32 and 0.45 at M = 48
+// and 64; with 64-token tiles (two per CU for 10 channels, one for 16) 6.8
+// at M = 128 (two tiles), 10.5-10.8 against 11.6-11.9 us at M = 160-192
+// (three) and 11.9-12.3 against 16.7-17.1 at M = 224-256 (four); with
+// 32-token tiles (two per CU either way) level at four tiles and 1.6-2.7
+// us slower at three and from five, where 10 channels need a further round.
+inline int dec_up_channels(int hs, int64_t M, int tm, int r) {
+  if (hs % 2560 != 0) return 16;
+  const int64_t tiles = (M + tm - 1) / tm;
+  auto rounds = [&](int cw) {
+    const int64_t fit = (int64_t)(kLdsPerCu / k2_dec_lds(tm, r, cw));
+    const int64_t slots = 256 * (fit > 1 ? fit : 1);
+    return ((int64_t)(hs / cw) * tiles + slots - 1) / slots;
+  };
+  return rounds(10) <= rounds(16) ? 10 : 16;
+}
 // Decode up kernel for HC streams: a wave's 16 MFMA rows are 16/HC channels x
 // HC streams; NW waves per workgroup (HC waves up to 4 in the split and fused
 // plans' up kernel, 4 in the persistent plan). At HC = 8, when HS is a
@@ -250,7 +260,7 @@ inline bool make_split(const Shape& s, int64_t M, int kd, Plan* out) {
   // while the 128-token down tile is 1.2 us faster than four 32-token ones)
   const int k2 = d.tm == 16 ? K2_T16 : d.tm == 64 ? K2_T64S : K2_T32;
   const int tm2 = k2_shape(k2).tm;
-  const int cw2 = s.hc == 4 ? dec_up_channels(s.hs, M, tm2) : decg_channels(s.hc, decg_waves(s.hc, s.hs));
+  const int cw2 = s.hc == 4 ? dec_up_channels(s.hs, M, tm2, s.r) : decg_channels(s.hc, decg_waves(s.hc, s.hs));
   const size_t lds2 = s.hc == 4 ? k2_dec_lds(tm2, s.r, cw2) : k2_decg_lds(s.hc, tm2, s.r, decg_waves(s.hc, s.hs));
   if (s.hs % d.kc != 0 || s.hs / d.kc > 4 * kRedMaxCpl || lds2 > kLdsPerCu) return false;
   Plan p;

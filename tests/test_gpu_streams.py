@@ -104,15 +104,17 @@ def test_hc8_ten_channel_up_kernel(H, kind, full, M):
 
 @pytest.mark.parametrize("full", [False, True])
 @pytest.mark.parametrize("hs,M,kd,cw", [(2560, 1, 0, 10), (2560, 17, 4, 10), (2560, 64, 8, 10), (2560, 45, 8, 10),
-                                        (2560, 30, 0, 10), (5120, 9, 1, 10), (2560, 90, 4, 16), (1280, 30, 4, 16),
+                                        (2560, 30, 0, 10), (5120, 9, 1, 10), (2560, 90, 4, 16), (2560, 128, 4, 10),
+                                        (2560, 150, 4, 16), (2560, 150, 8, 10), (2560, 256, 8, 10), (1280, 30, 4, 16),
                                         (1280, 64, 8, 16)])
 def test_hc4_up_kernel_channel_groups(H, full, hs, M, kd, cw):
     """HC = 4 decode up kernel: 10 channels per workgroup (three waves, the
     last one's rows past the tenth channel zero, R2 rows and Wnorm in 4-byte
-    pieces) where HS is a multiple of 2560 and the grid fits two workgroups
-    per CU, else 16 (four waves: HS = 2560 in three 32-token tiles, HS =
-    1280); 16-, 32- and 64-token tiles, a ragged last tile, two tiles of 16,
-    Wnorm per channel or per element; every row against the oracle."""
+    pieces) where HS is a multiple of 2560 unless that takes more rounds of
+    workgroups than 16 channels, else 16 (four waves: HS = 2560 in three or
+    five 32-token tiles, HS = 1280); 16-, 32- and 64-token tiles, one to four
+    of them, a ragged last tile, Wnorm per channel or per element; every row
+    against the oracle."""
     r = 320
     _say(f"[streams] hc=4 up kernel hs={hs} M={M} kd={kd} full={full}")
     table = [{"tokens": M, "kind": H.HCGR_PLAN_SPLIT, "down_variant": kd, "streams_per_wg": 0, "segments": 0,
