@@ -39,6 +39,7 @@ struct DownArgs {
   float* P;   // [nkc][NP][Mpad] partial sums
   float* SS;  // [nkc][Mpad] partial sums of squares
   int wt;     // 1: P, SS and R2 are written through the L2 (decode sizes, below)
+  int wnt;    // 1: the variant that reads weight rows with the non-temporal policy (a single token tile, below)
 };
 
 // ---------------------------------------------------------------------------
@@ -61,8 +62,19 @@ struct DownArgs {
 // M = 1; HC = 1 and 8, 0.05-0.2 us slower; from 64 tokens slower for every
 // HC (the write-through traffic outweighs it). The launch sets it for HC = 2
 // and 4 up to 32 padded tokens.
+// WNT (chosen by the launch from wnt) reads the weight rows with the
+// non-temporal (streaming) policy: with a single token tile every weight line is read once per call,
+// and keeping it out of the caches shortens the call although this kernel's
+// own time grows by 0.06-0.2 us. Measured on MI355X (whole calls back to
+// back, the two forms interleaved, three sessions): per call 0.43-0.46 us
+// less at HC = 4, M = 1, 0.13-0.33 at M = 32, 0.2-0.47 and 0.78-0.80 at HC
+// = 8, M = 1 and 32, 0.14-0.18 at HC = 2, M = 1; HC = 4, M = 16 between
+// 0.29 less and 0.15 more. With two token tiles (HC = 4, M = 64; HC = 1, M
+// = 32 in 16-token tiles) it was 0.2-0.3 us slower, since the second tile
+// reads the lines from HBM again. The launch takes it when the plan has one
+// token tile; the other variant is the kernel's code as before.
 // ---------------------------------------------------------------------------
-template <int TM, int RB, int KW, int KC>
+template <int TM, int RB, int KW, int KC, bool WNT>
 __global__ __launch_bounds__(RB * KW * 64) void hcgr_k1_dec(DownArgs a) {
   constexpr int NW = RB * KW;
   constexpr int NT = NW * 64;
@@ -106,8 +118,13 @@ __global__ __launch_bounds__(RB * KW * 64) void hcgr_k1_dec(DownArgs a) {
                          : make_rsrc(a.w1, (uint32_t)a.HC * rowb);
   const uint32_t wrow = (uint32_t)((down ? nb * 16 : nb * 16 - a.r) + (lane & 15)) * rowb;
   uint4 wf[NKS];
+  if constexpr (WNT) {
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) wf[ks] = bld16(rW, wrow + (uint32_t)(kbeg + kw * KPW + ks * 32 + koff) * 2u);
+    for (int ks = 0; ks < NKS; ++ks) wf[ks] = bld16_nt(rW, wrow + (uint32_t)(kbeg + kw * KPW + ks * 32 + koff) * 2u);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) wf[ks] = bld16(rW, wrow + (uint32_t)(kbeg + kw * KPW + ks * 32 + koff) * 2u);
+  }
 
   // 2. activation chunks (R, y, Wnorm); a thread's chunks share one column
   const rsrc_t rR = make_rsrc(a.R + m0 * a.K, (uint32_t)rows * rowb);
@@ -2118,7 +2135,10 @@ static void klaunch(F k, dim3 grid, dim3 block, size_t lds, hipStream_t st, cons
 
 template <int TM, int RB, int KW, int KC>
 static void launch_kd(const DownArgs& d, dim3 grid, hipStream_t st, const hipEvent_t* ev) {
-  klaunch(hcgr_k1_dec<TM, RB, KW, KC>, grid, dim3(RB * KW * 64), 0, st, ev, d);
+  if (d.wnt)
+    klaunch(hcgr_k1_dec<TM, RB, KW, KC, true>, grid, dim3(RB * KW * 64), 0, st, ev, d);
+  else
+    klaunch(hcgr_k1_dec<TM, RB, KW, KC, false>, grid, dim3(RB * KW * 64), 0, st, ev, d);
 }
 static void launch_kd_variant(int v, const DownArgs& d, dim3 grid, hipStream_t st, const hipEvent_t* ev = nullptr) {
   switch (v) {
@@ -2213,6 +2233,7 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   d.inv_hc = 1.0f / (float)s.hc;
   d.R2 = f.R2; d.P = P; d.SS = SS;
   d.wt = p.mpad <= 32 && (s.hc == 2 || s.hc == 4) ? 1 : 0;
+  d.wnt = p.mpad == p.tm ? 1 : 0;  // one token tile: each weight line is read once
   dim3 g1((unsigned)(p.ntiles_n * p.nkc), (unsigned)(p.mpad / p.tm));
   launch_kd_variant(p.k1, d, g1, st, tm.stage(0));
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
