@@ -446,7 +446,7 @@ struct DecgLds {
   static size_t bytes(int r) { return k2_decg_lds(HC, TM, r, NW); }
 };
 
-template <int HC, int TM, int NW, bool PERSIST>
+template <int HC, int TM, int NW, bool PERSIST, bool WNT = false>
 __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, int ncg) {
   using L = DecgLds<HC, TM, NW>;
   constexpr int CPW = 16 / HC, CW = L::CW, WR = NW * 16;
@@ -484,7 +484,11 @@ __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, in
     const int c = (sl & ~3) | ((sl ^ row) & 3);
     const int i16 = row & 15;
     const int ch = cbase + (row >> 4) * CPW + i16 / HC, st = i16 % HC;
-    lds_load16(rWu, wl + i * 1024, (uint32_t)(st * a.HS + ch) * rowb + (uint32_t)c * 16u);
+    const uint32_t off = (uint32_t)(st * a.HS + ch) * rowb + (uint32_t)c * 16u;
+    if constexpr (WNT)  // streamed: a grid of one or two token tiles (split launch)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rWu, (lds_void_t*)(wl + i * 1024), 16, off, 0, 0, kNonTemporal);
+    else
+      lds_load16(rWu, wl + i * 1024, off);
   }
   if (wave == 0) {
     const int nwn = a.wn_full ? HC * CHP : CHP;
@@ -590,9 +594,9 @@ __device__ __forceinline__ void decg_up(const DecUpArgs& a, int bx, int tile, in
   }
 }
 
-template <int HC, int TM, int NW>
+template <int HC, int TM, int NW, bool WNT = false>
 __global__ __launch_bounds__(64 * NW) void hcgr_k2_decg(DecUpArgs a) {
-  decg_up<HC, TM, NW, false>(a, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x);
+  decg_up<HC, TM, NW, false, WNT>(a, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -629,6 +633,9 @@ template <int HC, int TM>
 static hipError_t set_decg_lds() {
   hipError_t e = hipFuncSetAttribute((const void*)hcgr_k2_decg<HC, TM, decg_nw(HC)>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu);
+  if (e == hipSuccess && HC < 4)
+    e = hipFuncSetAttribute((const void*)hcgr_k2_decg<HC, TM, decg_nw(HC), true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCu);
   if (e == hipSuccess && HC == 8)
     e = hipFuncSetAttribute((const void*)hcgr_k2_decg<HC, TM, 5>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)kLdsPerCu);
@@ -668,7 +675,8 @@ int configure_decode_kernels() {
 }
 
 template <int TM>
-static void launch_decg(int hc, int nw, const DecUpArgs& u, dim3 g, size_t lds, hipStream_t st, const hipEvent_t* ev);
+static void launch_decg(int hc, int nw, const DecUpArgs& u, dim3 g, size_t lds, hipStream_t st, const hipEvent_t* ev,
+                        bool wnt = false);
 
 int launch_decg_up(const Shape& s, int tm, const uint16_t* H, const ForwardArgs& f, void* stream, void* const* events) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -680,17 +688,30 @@ int launch_decg_up(const Shape& s, int tm, const uint16_t* H, const ForwardArgs&
   const int nw = decg_waves(s.hc, s.hs);
   const dim3 g((unsigned)(s.hs / decg_channels(s.hc, nw)), (unsigned)cdiv(f.M, (int64_t)tm));
   const size_t lds = k2_decg_lds(s.hc, tm, s.r, nw);
-  if (tm == 16) launch_decg<16>(s.hc, nw, u, g, lds, st, ev);
-  else if (tm == 32) launch_decg<32>(s.hc, nw, u, g, lds, st, ev);
-  else launch_decg<64>(s.hc, nw, u, g, lds, st, ev);
+  // Wu streamed (the non-temporal policy) at HC = 1 and 2 with one or two
+  // token tiles: measured per call on MI355X, 0.64 us less at HC = 1, M = 32
+  // and 0.23 at HC = 2, M = 32 (two 16-token tiles), level at M = 1; at HC =
+  // 8 streaming was 0.4-0.6 us slower even with one tile
+  const bool wnt = s.hc < 4 && g.y <= 2;
+  if (tm == 16) launch_decg<16>(s.hc, nw, u, g, lds, st, ev, wnt);
+  else if (tm == 32) launch_decg<32>(s.hc, nw, u, g, lds, st, ev, wnt);
+  else launch_decg<64>(s.hc, nw, u, g, lds, st, ev, wnt);
   return (int)hipGetLastError();
 }
 
+// wnt: Wu streamed (HC = 1 and 2 only; the split launch decides)
 template <int TM>
-static void launch_decg(int hc, int nw, const DecUpArgs& u, dim3 g, size_t lds, hipStream_t st, const hipEvent_t* ev) {
+static void launch_decg(int hc, int nw, const DecUpArgs& u, dim3 g, size_t lds, hipStream_t st, const hipEvent_t* ev,
+                        bool wnt) {
   switch (hc) {
-    case 1: klaunch_d(hcgr_k2_decg<1, TM, 1>, g, dim3(64), lds, st, ev, u); break;
-    case 2: klaunch_d(hcgr_k2_decg<2, TM, 2>, g, dim3(128), lds, st, ev, u); break;
+    case 1:
+      if (wnt) klaunch_d(hcgr_k2_decg<1, TM, 1, true>, g, dim3(64), lds, st, ev, u);
+      else klaunch_d(hcgr_k2_decg<1, TM, 1>, g, dim3(64), lds, st, ev, u);
+      break;
+    case 2:
+      if (wnt) klaunch_d(hcgr_k2_decg<2, TM, 2, true>, g, dim3(128), lds, st, ev, u);
+      else klaunch_d(hcgr_k2_decg<2, TM, 2>, g, dim3(128), lds, st, ev, u);
+      break;
     case 4: klaunch_d(hcgr_k2_decg<4, TM, 4>, g, dim3(256), lds, st, ev, u); break;
     default:
       if (nw == 5) klaunch_d(hcgr_k2_decg<8, TM, 5>, g, dim3(320), lds, st, ev, u);

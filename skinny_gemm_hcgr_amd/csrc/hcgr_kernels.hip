@@ -350,7 +350,7 @@ struct UpArgs {
   uint16_t* x;
 };
 
-template <int TM, int CW>
+template <int TM, int CW, bool WNT>
 __global__ __launch_bounds__((CW + 3) / 4 * 64) void hcgr_k2_dec(UpArgs a) {
   constexpr int NW = (CW + 3) / 4;
   constexpr int NTB = TM / 16;
@@ -391,7 +391,7 @@ __global__ __launch_bounds__((CW + 3) / 4 * 64) void hcgr_k2_dec(UpArgs a) {
     const int c = (sl & ~3) | ((sl ^ row) & 3);  // the chunk this slot holds
     const bool pad = CW % 4 != 0 && (row >> 2) >= CW;  // rows of channels past CW read zeros
     const uint32_t off = pad ? 0x80000000u : (uint32_t)((row & 3) * a.HS + cbase + (row >> 2)) * rowb + (uint32_t)c * 16u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWu, (lds_void_t*)(wl + i * 1024), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWu, (lds_void_t*)(wl + i * 1024), 16, off, 0, 0, WNT ? kNonTemporal : 0);
   }
   for (int i = wave; i * 64 < TM * cpr; i += NW) {
     const int q = i * 64 + lane, row = q / cpr, sl = q % cpr;
@@ -2193,8 +2193,12 @@ static void launch_kf(const FullArgs& f, dim3 grid, hipStream_t st, const hipEve
 int configure_kernels() {
   const int lim = (int)kLdsPerCu;  // make_split keeps k2_dec_lds within it
   hipError_t e;
-  for (const void* k : {(const void*)hcgr_k2_dec<16, 16>, (const void*)hcgr_k2_dec<32, 16>, (const void*)hcgr_k2_dec<64, 16>,
-                        (const void*)hcgr_k2_dec<16, 10>, (const void*)hcgr_k2_dec<32, 10>, (const void*)hcgr_k2_dec<64, 10>})
+  for (const void* k : {(const void*)hcgr_k2_dec<16, 16, false>, (const void*)hcgr_k2_dec<32, 16, false>,
+                        (const void*)hcgr_k2_dec<64, 16, false>, (const void*)hcgr_k2_dec<16, 10, false>,
+                        (const void*)hcgr_k2_dec<32, 10, false>, (const void*)hcgr_k2_dec<64, 10, false>,
+                        (const void*)hcgr_k2_dec<16, 16, true>, (const void*)hcgr_k2_dec<32, 16, true>,
+                        (const void*)hcgr_k2_dec<64, 16, true>, (const void*)hcgr_k2_dec<16, 10, true>,
+                        (const void*)hcgr_k2_dec<32, 10, true>, (const void*)hcgr_k2_dec<64, 10, true>})
     if ((e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lim)) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(2))) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k2_sweep<3>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds_bytes(3))) != hipSuccess) return (int)e;
@@ -2258,17 +2262,24 @@ static int launch_split(const Shape& s, const Plan& p, const ForwardArgs& f, hip
   const size_t lds = k2_dec_lds(tm2, s.r, p.cb);
   const dim3 g2((unsigned)(s.hs / p.cb), (unsigned)cdiv(f.M, (int64_t)tm2));
   const dim3 b2((unsigned)((p.cb + 3) / 4 * 64));
+  // Wu streamed (the non-temporal policy) while the grid has one or two
+  // token tiles (measured per call on MI355X, the two forms interleaved in
+  // two sessions: 0.24 us less at M = 32, 0.39-0.42 at 16, 0.11 at 48,
+  // 0.17-0.40 at 64, level at 1; always streamed, 0.26 more with four tiles
+  // at M = 128, where the tiles read each Wu line again)
+  const bool wnt = g2.y <= 2;
+  auto up = [&](auto k) { klaunch(k, g2, b2, lds, st, tm.stage(2), u); };
   if (p.cb == 10) {
     switch (p.k2) {
-      case K2_T16: klaunch(hcgr_k2_dec<16, 10>, g2, b2, lds, st, tm.stage(2), u); break;
-      case K2_T32: klaunch(hcgr_k2_dec<32, 10>, g2, b2, lds, st, tm.stage(2), u); break;
-      default: klaunch(hcgr_k2_dec<64, 10>, g2, b2, lds, st, tm.stage(2), u); break;
+      case K2_T16: wnt ? up(hcgr_k2_dec<16, 10, true>) : up(hcgr_k2_dec<16, 10, false>); break;
+      case K2_T32: wnt ? up(hcgr_k2_dec<32, 10, true>) : up(hcgr_k2_dec<32, 10, false>); break;
+      default: wnt ? up(hcgr_k2_dec<64, 10, true>) : up(hcgr_k2_dec<64, 10, false>); break;
     }
   } else {
     switch (p.k2) {
-      case K2_T16: klaunch(hcgr_k2_dec<16, 16>, g2, b2, lds, st, tm.stage(2), u); break;
-      case K2_T32: klaunch(hcgr_k2_dec<32, 16>, g2, b2, lds, st, tm.stage(2), u); break;
-      default: klaunch(hcgr_k2_dec<64, 16>, g2, b2, lds, st, tm.stage(2), u); break;
+      case K2_T16: wnt ? up(hcgr_k2_dec<16, 16, true>) : up(hcgr_k2_dec<16, 16, false>); break;
+      case K2_T32: wnt ? up(hcgr_k2_dec<32, 16, true>) : up(hcgr_k2_dec<32, 16, false>); break;
+      default: wnt ? up(hcgr_k2_dec<64, 16, true>) : up(hcgr_k2_dec<64, 16, false>); break;
     }
   }
   return (int)hipGetLastError();
