@@ -141,7 +141,7 @@ struct FuseArgs {
 //     0). Every chunk's sums of squares are recomputed by each block, so the
 //     blocks form bit-identical rrms.
 // ---------------------------------------------------------------------------
-template <int TM, bool PERSIST>
+template <int TM, bool PERSIST, bool WNT = false>
 __device__ __forceinline__ void fuse_down(const FuseArgs& a, int bx, int tile) {
   constexpr int ROWB = kFuseUmax * 128 * 2;  // LDS bytes of one tile row (widest chunk)
   constexpr int NTB = TM / 16;
@@ -180,7 +180,11 @@ __device__ __forceinline__ void fuse_down(const FuseArgs& a, int bx, int tile) {
   const rsrc_t rW = make_rsrc(wbase, (uint32_t)(inject ? a.HC : 16) * rowb);  // rows past HC read as zero
   for (int i = wave; i < cpr / 4; i += 4) {
     const int q = i * 64 + lane, row = q / cpr, sl = q - row * cpr;
-    lds_load16(rW, wl + i * 1024, (uint32_t)row * rowb + kcol + (uint32_t)(sl ^ (row & 7)) * 16u);
+    const uint32_t woff = (uint32_t)row * rowb + kcol + (uint32_t)(sl ^ (row & 7)) * 16u;
+    if constexpr (WNT)  // streamed: one token tile, each weight line read once per call
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void_t*)(wl + i * 1024), 16, woff, 0, 0, kNonTemporal);
+    else
+      lds_load16(rW, wl + i * 1024, woff);
   }
   // R and y: the valid rows only (pieces of rows past M read as zero)
   const rsrc_t rR = make_rsrc(a.R + m0 * a.K, (uint32_t)rows * rowb);
@@ -401,9 +405,9 @@ __device__ __forceinline__ void fuse_down(const FuseArgs& a, int bx, int tile) {
   if (lane == 0) __hip_atomic_store(slot(a.ctr, grp), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int TM>
+template <int TM, bool WNT = false>
 __global__ __launch_bounds__(256) void hcgr_k1_fuse(FuseArgs a) {
-  fuse_down<TM, false>(a, (int)blockIdx.x, (int)blockIdx.y);
+  fuse_down<TM, false, WNT>(a, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -607,11 +611,11 @@ __global__ __launch_bounds__(64 * NW) void hcgr_k2_decg(DecUpArgs a) {
 // workgroup is resident or finished before any up workgroup starts to wait,
 // and each wait is also bounded.
 // ---------------------------------------------------------------------------
-template <int HC, int TM>
+template <int HC, int TM, bool WNT = false>
 __global__ __launch_bounds__(256) void hcgr_dec_persist(FuseArgs a, DecUpArgs u, int ndown_tile, int ntiles, int ncg) {
   const int b = (int)blockIdx.x;
   if (b < ndown_tile * ntiles) {
-    fuse_down<TM, true>(a, b % ndown_tile, b / ndown_tile);
+    fuse_down<TM, true, WNT>(a, b % ndown_tile, b / ndown_tile);
   } else {
     const int j = b - ndown_tile * ntiles;
     decg_up<HC, TM, 4, true>(u, j % ncg, j / ncg, ncg);
@@ -648,6 +652,9 @@ static hipError_t set_decode_lds() {
   if (e == hipSuccess)
     e = hipFuncSetAttribute((const void*)hcgr_dec_persist<HC, TM>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)kLdsPerCu);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)hcgr_dec_persist<HC, TM, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsPerCu);
   return e;
 }
 
@@ -661,6 +668,10 @@ int configure_decode_kernels() {
   if ((e = hipFuncSetAttribute((const void*)hcgr_k1_fuse<16>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)k1_fuse_lds(16))) != hipSuccess) return (int)e;
   if ((e = hipFuncSetAttribute((const void*)hcgr_k1_fuse<32>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)k1_fuse_lds(32))) != hipSuccess) return (int)e;
+  if ((e = hipFuncSetAttribute((const void*)hcgr_k1_fuse<16, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)k1_fuse_lds(16))) != hipSuccess) return (int)e;
+  if ((e = hipFuncSetAttribute((const void*)hcgr_k1_fuse<32, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)k1_fuse_lds(32))) != hipSuccess) return (int)e;
   if ((e = set_decode_lds<1, 16>()) != hipSuccess || (e = set_decode_lds<1, 32>()) != hipSuccess ||
       (e = set_decode_lds<2, 16>()) != hipSuccess || (e = set_decode_lds<2, 32>()) != hipSuccess ||
@@ -724,11 +735,16 @@ template <int TM>
 static void launch_persist(int hc, const FuseArgs& a, const DecUpArgs& u, int ndt, int nt, int ncg, size_t lds,
                            hipStream_t st, const hipEvent_t* ev) {
   const dim3 g((unsigned)((ndt + ncg) * nt)), b(256);
+  // weights streamed with one token tile (see the fused launch below)
+  auto run = [&](auto k, auto k_wnt) {
+    if (nt == 1) klaunch_d(k_wnt, g, b, lds, st, ev, a, u, ndt, nt, ncg);
+    else klaunch_d(k, g, b, lds, st, ev, a, u, ndt, nt, ncg);
+  };
   switch (hc) {
-    case 1: klaunch_d(hcgr_dec_persist<1, TM>, g, b, lds, st, ev, a, u, ndt, nt, ncg); break;
-    case 2: klaunch_d(hcgr_dec_persist<2, TM>, g, b, lds, st, ev, a, u, ndt, nt, ncg); break;
-    case 4: klaunch_d(hcgr_dec_persist<4, TM>, g, b, lds, st, ev, a, u, ndt, nt, ncg); break;
-    default: klaunch_d(hcgr_dec_persist<8, TM>, g, b, lds, st, ev, a, u, ndt, nt, ncg); break;
+    case 1: run(hcgr_dec_persist<1, TM, false>, hcgr_dec_persist<1, TM, true>); break;
+    case 2: run(hcgr_dec_persist<2, TM, false>, hcgr_dec_persist<2, TM, true>); break;
+    case 4: run(hcgr_dec_persist<4, TM, false>, hcgr_dec_persist<4, TM, true>); break;
+    default: run(hcgr_dec_persist<8, TM, false>, hcgr_dec_persist<8, TM, true>); break;
   }
 }
 
@@ -771,9 +787,20 @@ int launch_fused(const Shape& s, const Plan& p, const ForwardArgs& f, void* stre
     }
     return (int)hipSuccess;
   }
+  // weight rows streamed (the non-temporal policy) with one token tile, where
+  // each weight line is read once per call: measured per call on MI355X
+  // against the cached loads (two sessions), fused plan 0.47-0.54 us less at
+  // HC = 4, M = 1, 0.38-0.41 at HC = 2, M = 1 and 8, 0.02-0.32 at HC = 1,
+  // M = 1..16; persistent plan 0.39-0.43, 0.34-0.46 and 0.02-0.23
   const dim3 g1((unsigned)(s.nblk() * p.nkc), (unsigned)p.ntiles);
-  if (p.tm == 16) klaunch_d(hcgr_k1_fuse<16>, g1, dim3(256), k1_fuse_lds(16), st, ev, a);
-  else klaunch_d(hcgr_k1_fuse<32>, g1, dim3(256), k1_fuse_lds(32), st, ev, a);
+  const bool wnt = p.ntiles == 1;
+  if (p.tm == 16) {
+    if (wnt) klaunch_d(hcgr_k1_fuse<16, true>, g1, dim3(256), k1_fuse_lds(16), st, ev, a);
+    else klaunch_d(hcgr_k1_fuse<16>, g1, dim3(256), k1_fuse_lds(16), st, ev, a);
+  } else {
+    if (wnt) klaunch_d(hcgr_k1_fuse<32, true>, g1, dim3(256), k1_fuse_lds(32), st, ev, a);
+    else klaunch_d(hcgr_k1_fuse<32>, g1, dim3(256), k1_fuse_lds(32), st, ev, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   if (ev) {  // no middle kernel: an empty interval right after the down kernel
     if ((e = hipEventRecord(ev[2], st)) != hipSuccess || (e = hipEventRecord(ev[3], st)) != hipSuccess) return (int)e;
