@@ -173,3 +173,24 @@ def test_workspace_keeps_the_counter_bytes(lib):
                     chosen, desc = H.hcgr_plan_lookup(cfg, [c], M)
                     assert chosen["kind"] == kind, (hc, M, desc)
                     assert H.hcgr_workspace_size_table(cfg, [c], M) >= ws_of(desc)
+
+
+# (M, down variant, HS, r) -> up-kernel channels and grid of the HC = 4 split
+# plan: 10 channels where HS is a multiple of 2560 unless they need more
+# rounds of workgroups than 16 (a round: the workgroups that fit the 256 CUs'
+# LDS at once; 64-token tiles fit two per CU with 10 channels, one with 16;
+# 32-token tiles two either way; 16-token tiles three and two)
+@pytest.mark.parametrize("M,kd,hs,r,cw,tiles", [
+    (1, 0, 2560, 320, 10, 1), (48, 0, 2560, 320, 10, 3),              # 16-token tiles: one round either way
+    (64, 4, 2560, 320, 10, 2), (96, 4, 2560, 320, 16, 3),             # 32-token tiles: 768 of 10 need two rounds
+    (128, 4, 2560, 320, 10, 4), (160, 4, 2560, 320, 16, 5),           # four tiles: two rounds either way
+    (128, 8, 2560, 320, 10, 2), (192, 8, 2560, 320, 10, 3), (256, 8, 2560, 320, 10, 4),  # 64-token tiles
+    (9, 1, 5120, 320, 10, 1), (30, 4, 1280, 320, 16, 1), (128, 8, 2560, 512, 10, 2),
+])
+def test_up_kernel_channel_rule(lib, M, kd, hs, r, cw, tiles):
+    cfg = H.Config(hs=hs, r=r)
+    table = [{"tokens": M, "kind": H.HCGR_PLAN_SPLIT, "down_variant": kd, "streams_per_wg": 0, "segments": 0,
+              "up_variant": 0, "ranges": 0}]
+    desc = H.hcgr_plan_lookup(cfg, table, M)[1]
+    tm = (16, 16, 16, 16, 32, 32, 32, 32, 64, 64)[kd]
+    assert f"k2_dec tm={tm} waves={(cw + 3) // 4} channels={cw} grid={hs // cw}x{tiles}" in desc, desc
